@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN state layer on one MI355X.
+
+Headline workload: one multi-slot decode step of a Qwen3-Next-shaped GDN
+layer (h_k=16, h_v=32, d_k=d_v=128, conv_k=4, bf16 io, fp32 state) for 64
+active slots of a 256-slot pool.  Consecutive steps rotate over four
+disjoint 64-slot subsets (512 MiB of state in total, twice the 256 MB
+last-level cache), so every step streams its state from HBM.
+
+Printed: one JSON line.  `value` is decode tokens/s at 64 slots; the line
+also carries the state bandwidth, the roofline of the decode kernel (HIP
+events on the launch stream), the speculative-verify and chunked-prefill
+figures measured in the same run, and the CPU oracle baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+
+# HBM bytes of the plain copy kernel measured with rocprofv3 --pmc
+# (FETCH_SIZE/WRITE_SIZE per dispatch vs. bytes copied); see profiles/.
+COUNTER_SCALE = None
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-verify", action="store_true")
+    p.add_argument("--only", choices=["decode", "verify", "prefill"], default=None,
+                   help="run one workload only (for profiling)")
+    return p.parse_args()
+
+
+def decode_bytes_per_slot(s, io_size=2):
+    state = 2 * s.h_v * s.d_v * s.d_k * 4
+    qkv = (2 * s.h_k * s.d_k + s.h_v * s.d_v) * io_size
+    ab = 2 * s.h_v * 4
+    win = (s.conv_k - 1) * s.c_conv * io_size + s.c_conv * io_size   # read window, write new column
+    out = s.h_v * s.d_v * io_size
+    return state + qkv + ab + win + out + 4
+
+
+def verify_bytes_per_slot(s, n_tok, io_size=2):
+    state = 2 * s.h_v * s.d_v * s.d_k * 4
+    qkv = n_tok * (2 * s.h_k * s.d_k + s.h_v * s.d_v) * io_size
+    ab = n_tok * 2 * s.h_v * 4
+    win = 2 * (s.conv_k - 1) * s.c_conv * io_size
+    out = n_tok * s.h_v * s.d_v * io_size
+    return state + qkv + ab + win + out + 8
+
+
+def time_launches(fn, steps, warmup, torch):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps * 1e-3   # seconds per launch
+
+
+def bench_decode(args, torch, G, syn):
+    s = syn.QWEN3_NEXT
+    n_slots, N, n_sets = 256, 64, 4
+    pool = G.Pool(G.make_desc(n_slots, 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16))
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    pool.state.normal_(generator=gen)
+    pool.window.copy_(torch.randn(pool.window.shape, generator=gen, device="cuda").bfloat16())
+    rng = np.random.default_rng(1001)
+    perm = rng.permutation(n_slots).astype(np.int32)
+    sets = []
+    w = torch.from_numpy(syn.draw_conv_weights(rng, s)).cuda()
+    for j in range(n_sets):
+        tok = syn.draw_tokens(rng, s, (N,), "bf16")
+        d = {n: torch.from_numpy(tok[n]).cuda() for n in "ab"}
+        d.update({n: torch.from_numpy(tok[n]).bfloat16().cuda() for n in "qkv"})
+        d["ids"] = torch.from_numpy(perm[j * N:(j + 1) * N].copy()).cuda()
+        sets.append(d)
+    out = torch.empty((N, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        d = sets[i % n_sets]
+        pool.decode(0, d["ids"], d["q"], d["k"], d["v"], d["a"], d["b"], w, out)
+
+    t = time_launches(step, args.steps, args.warmup, torch)
+    # Hot-cache figure: the same 64 slots every step.
+    t_hot = time_launches(lambda i: step(0), max(20, args.steps // 4), 5, torch)
+    # Small batches (latency-bound at N=1).
+    small = {}
+    for n in (1, 4, 16):
+        d = sets[0]
+        ids = d["ids"][:n].clone()
+        qq, kk, vv, aa, bb = (d[m][:n].contiguous() for m in "qkvab")
+        o = out[:n]
+        small[n] = time_launches(lambda i: pool.decode(0, ids, qq, kk, vv, aa, bb, w, o),
+                                 max(50, args.steps // 4), 10, torch)
+    assert pool.error() == 0
+    per_slot = decode_bytes_per_slot(s)
+    bytes_launch = N * per_slot + s.c_conv * s.conv_k * 4
+    state_bytes = N * 2 * s.h_v * s.d_v * s.d_k * 4
+    return {
+        "sec": t, "sec_hot": t_hot, "n": N, "bytes": bytes_launch,
+        "gbps": bytes_launch / t / 1e9, "state_gbps": state_bytes / t / 1e9,
+        "hot_gbps": bytes_launch / t_hot / 1e9,
+        "small": {str(n): {"us": small[n] * 1e6, "tok_s": n / small[n],
+                           "gbps": (n * per_slot + s.c_conv * s.conv_k * 4) / small[n] / 1e9}
+                  for n in small},
+    }
+
+
+def bench_verify(args, torch, G, syn):
+    s = syn.QWEN3_NEXT
+    n_slots, N, n_tok = 256, 128, 4
+    pool = G.Pool(G.make_desc(n_slots, 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16))
+    gen = torch.Generator(device="cuda").manual_seed(4321)
+    pool.state.normal_(generator=gen)
+    case = syn.verify_case()
+    tok = case["tokens"]
+    d = {n: torch.from_numpy(tok[n]).cuda() for n in "ab"}
+    d.update({n: torch.from_numpy(tok[n]).bfloat16().cuda() for n in "qkv"})
+    w = torch.from_numpy(case["conv_w"]).cuda()
+    # Two disjoint 128-slot halves alternate so each launch streams from HBM.
+    perm = np.random.default_rng(7).permutation(n_slots).astype(np.int32)
+    ids = [torch.from_numpy(perm[:N].copy()).cuda(), torch.from_numpy(perm[N:].copy()).cuda()]
+    acc = torch.from_numpy(case["accept_len"]).cuda()
+    out = torch.empty((N, n_tok, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        pool.verify(0, ids[i % 2], n_tok, d["q"], d["k"], d["v"], d["a"], d["b"], w, acc, out)
+
+    t = time_launches(step, max(50, args.steps // 2), 10, torch)
+    assert pool.error() == 0
+    b = N * verify_bytes_per_slot(s, n_tok) + s.c_conv * s.conv_k * 4
+    return {"sec": t, "n": N, "n_tok": n_tok, "bytes": b, "gbps": b / t / 1e9,
+            "tok_s": N * n_tok / t,
+            "accepted_tok_s": float(case["accept_len"].sum()) / t}
+
+
+def prefill_flops_per_token(s, C):
+    """Algorithmic flops per token of the chunked form (triangular-aware)."""
+    dk, dv, G = s.d_k, s.d_v, s.group
+    per_khead = (C + 1) * dk + (C + 1) * dk          # K K^T and Q K^T lower triangles, per token
+    per_vhead = (C * C / 3.0) / C * 2 / 2            # (I+A)^-1 ~ C^3/3 per chunk -> per token
+    per_vhead += 2 * C * dk + 2 * C * dv             # W = T diag K-side, U_v = T diag(b) V
+    per_vhead += 2 * dk * dv * 3                     # W S0^T, Q S0^T, U^T K (per token)
+    per_vhead += (C + 1) * dv                        # (QK^T * decay) U, lower triangle
+    return s.h_k * per_khead + s.h_v * per_vhead
+
+
+def bench_prefill(args, torch, G, syn):
+    s = syn.QWEN3_NEXT
+    case = syn.prefill_case()
+    T, C = 8192, 64
+    tok = case["tokens"]
+    pool = G.Pool(G.make_desc(4, 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16))
+    d = {n: torch.from_numpy(tok[n]).cuda() for n in "ab"}
+    d.update({n: torch.from_numpy(tok[n]).bfloat16().cuda() for n in "qkv"})
+    w = torch.from_numpy(case["conv_w"]).cuda()
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    out = torch.empty((T, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    try:
+        wsb = pool.prefill_workspace_bytes(1, T, C)
+    except G.GdnError:
+        return None
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    slots = [torch.tensor([j], dtype=torch.int32, device="cuda") for j in range(4)]
+
+    def step(i):
+        sl = slots[i % 4]
+        pool.reset(sl)
+        pool.prefill(0, cu, sl, T, C, d["q"], d["k"], d["v"], d["a"], d["b"], w, out, ws)
+
+    try:
+        step(0)
+    except G.GdnError as e:
+        if e.status == -2:
+            return None
+        raise
+    t = time_launches(step, max(10, args.steps // 10), 3, torch)
+    t_reset = time_launches(lambda i: pool.reset(slots[i % 4]), 20, 3, torch)
+    t -= t_reset
+    io = 2
+    b = T * ((2 * s.h_k * s.d_k + s.h_v * s.d_v) * io + 2 * s.h_v * 4 + s.h_v * s.d_v * io) \
+        + 2 * s.h_v * s.d_v * s.d_k * 4
+    fl = prefill_flops_per_token(s, C) * T
+    return {"sec": t, "T": T, "chunk": C, "tok_s": T / t, "bytes": b, "gbps": b / t / 1e9,
+            "alg_tflops": fl / t / 1e12, "mfma_frac_alg": fl / t / 1e12 / BF16_PEAK_TFLOPS,
+            "workspace_bytes": wsb}
+
+
+def cpu_baseline(syn):
+    """The fp64 oracle, as it stands, on a bounded sample of the decode workload."""
+    from oracle import gdn_oracle as O
+    s = syn.QWEN3_NEXT
+    case = syn.decode_case(64)
+    ids = case["slot_ids"]
+    contents = syn.draw_pool_contents(case["pool_seed"], ids[:16], s, "bf16")
+    op = O.OraclePool(16, 1, s)
+    for j, sl in enumerate(ids[:16]):
+        op.S[j], op.X[j] = contents[int(sl)]
+    tok = case["tokens"]
+    n_done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 10.0:
+        op.decode(0, np.arange(16), *(tok[n][:16] for n in "qkvab"), case["conv_w"])
+        n_done += 16
+    dt = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": n_done / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"{n_done} decode tokens (16-slot decode steps, Qwen3-Next shapes, fp64 "
+                      f"literal matrix form) in {dt:.1f} s on {platform.processor() or 'host'}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import gated_deltanet_state_layer_amd as G
+    import gdn_synth as syn
+    G.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    res = {}
+    if args.only in (None, "decode"):
+        res["decode"] = bench_decode(args, torch, G, syn)
+        print(f"# decode done: {res['decode']['sec'] * 1e6:.1f} us/step", file=sys.stderr, flush=True)
+    if args.only in (None, "verify") and not args.no_verify:
+        res["verify"] = bench_verify(args, torch, G, syn)
+        print(f"# verify done: {res['verify']['sec'] * 1e6:.1f} us", file=sys.stderr, flush=True)
+    if args.only in (None, "prefill") and not args.no_prefill:
+        res["prefill"] = bench_prefill(args, torch, G, syn)
+        print("# prefill done", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu and args.only is None:
+        cpu = cpu_baseline(syn)
+        print("# cpu baseline done", file=sys.stderr, flush=True)
+    if "decode" not in res:
+        print(json.dumps(res))
+        return
+    dec = res["decode"]
+    line = {
+        "metric": "GDN decode tokens/s at 64 slots (state-GB/s, %HBM peak); prefill tok/s (%MFMA)",
+        "value": dec["n"] / dec["sec"],
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": dec["sec"] * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "multi-slot decode step, 64 of 256 slots (rotating 4 disjoint "
+                               "sets), h_k=16 h_v=32 d_k=d_v=128 conv_k=4, bf16 io, fp32 state",
+                   "n_slots": 256, "active_slots": 64},
+        "state_GBps": dec["state_gbps"],
+        "hbm_frac": dec["gbps"] / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": dec["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dec["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "decode_verify_kernel<128,bf16>",
+                     "bytes_per_launch": dec["bytes"], "us_per_launch": dec["sec"] * 1e6},
+        "decode_hot_cache_GBps": dec["hot_gbps"],
+        "decode_small_batches": dec["small"],
+    }
+    if "verify" in res:
+        v = res["verify"]
+        line["verify"] = {"workload": "128 slots x 4 tokens, accept_len U{1..4}",
+                          "us": v["sec"] * 1e6, "tok_s": v["tok_s"],
+                          "accepted_tok_s": v["accepted_tok_s"], "GBps": v["gbps"],
+                          "hbm_frac": v["gbps"] / HBM_PEAK_GBPS}
+    if res.get("prefill"):
+        p = res["prefill"]
+        line["prefill"] = {"workload": "one 8192-token sequence, chunk 64, fresh slot",
+                           "us": p["sec"] * 1e6, "tok_s": p["tok_s"], "GBps": p["gbps"],
+                           "alg_TFLOPs": p["alg_tflops"], "mfma_frac_alg": p["mfma_frac_alg"]}
+    if cpu:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,7 @@
+"""MI355X-native Gated DeltaNet state layer: a slot pool with multi-slot
+decode, speculative verify and chunked prefill, run by the HIP kernels of
+libgdn.so (see include/gdn.h) through a thin ctypes binding."""
+from .binding import (  # noqa: F401
+    GDN_BF16, GDN_F32, GDN_VALIDATE, GdnError, Pool, PoolDesc, load_library, make_desc,
+    pool_bytes, status_string,
+)

@@ -1,0 +1,207 @@
+"""Thin ctypes binding over libgdn (include/gdn.h): argument marshalling only.
+
+Every step of the layer runs in the HIP kernels of libgdn.so.  PyTorch is
+used for device memory (tensors are passed by data_ptr) and for the current
+HIP stream.  There is no fallback: if the library is missing or fails to
+load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARG = -1
+GDN_ERR_UNSUPPORTED = -2
+GDN_ERR_BAD_INDEX = -3
+GDN_ERR_WORKSPACE = -4
+GDN_ERR_HIP = -5
+GDN_F32 = 0
+GDN_BF16 = 1
+GDN_VALIDATE = 1
+
+EXPORTED = (
+    "gdn_pool_bytes", "gdn_pool_create", "gdn_pool_destroy", "gdn_slot_reset",
+    "gdn_decode_step", "gdn_verify_step", "gdn_prefill_workspace_bytes",
+    "gdn_prefill_chunked", "gdn_pool_error", "gdn_status_string",
+)
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_slots", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+        ("h_k", ctypes.c_int32), ("h_v", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("conv_k", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("q_scale", ctypes.c_float), ("norm_eps", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libgdn.so not found at {path}; build it with "
+                           "`python -m gated_deltanet_state_layer_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    PSZ = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "gdn_pool_bytes": [ctypes.POINTER(PoolDesc), PSZ, PSZ],
+        "gdn_pool_create": [ctypes.POINTER(PoolDesc), P, P, P, ctypes.POINTER(P)],
+        "gdn_pool_destroy": [P],
+        "gdn_slot_reset": [P, I32, P, P],
+        "gdn_decode_step": [P, I32, I32, P, P, P, P, P, P, P, P, P],
+        "gdn_verify_step": [P, I32, I32, P, I32, P, P, P, P, P, P, P, P, P],
+        "gdn_prefill_workspace_bytes": [P, I32, I64, I32, PSZ],
+        "gdn_prefill_chunked": [P, I32, I32, P, P, I64, I32, P, P, P, P, P, P, P, P, SZ, P],
+        "gdn_pool_error": [P, P, ctypes.POINTER(I32)],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = I32
+    lib.gdn_status_string.argtypes = [I32]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().gdn_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != GDN_OK:
+        raise GdnError(status, what)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _io_torch(io_dtype: int):
+    return torch.bfloat16 if io_dtype == GDN_BF16 else torch.float32
+
+
+def make_desc(n_slots, n_layers, h_k, h_v, d_k, d_v, conv_k, io_dtype=GDN_BF16,
+              q_scale=0.0, norm_eps=0.0, flags=0) -> PoolDesc:
+    return PoolDesc(n_slots, n_layers, h_k, h_v, d_k, d_v, conv_k, io_dtype,
+                    q_scale, norm_eps, flags)
+
+
+def pool_bytes(desc: PoolDesc):
+    lib = load_library()
+    sb, ab = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.gdn_pool_bytes(ctypes.byref(desc), ctypes.byref(sb), ctypes.byref(ab)),
+           "gdn_pool_bytes")
+    return sb.value, ab.value
+
+
+class Pool:
+    """A slot pool over torch-owned device buffers.
+
+    Attributes `state` ([n_slots, n_layers, h_v, d_v, d_k] fp32) and `window`
+    ([n_slots, n_layers, conv_k-1, C_conv] io dtype) are views of the pool's
+    device memory in the library's documented layout.
+    """
+
+    def __init__(self, desc: PoolDesc, device="cuda", stream=None):
+        lib = load_library()
+        self.desc = desc
+        self.device = torch.device(device)
+        sb, ab = pool_bytes(desc)
+        self._state_buf = torch.empty(sb // 4, dtype=torch.float32, device=self.device)
+        self._aux_buf = torch.empty(ab, dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        _check(lib.gdn_pool_create(ctypes.byref(desc), _ptr(self._state_buf), _ptr(self._aux_buf),
+                                   _stream(stream), ctypes.byref(h)), "gdn_pool_create")
+        self._h = h
+        self.c_conv = 2 * desc.h_k * desc.d_k + desc.h_v * desc.d_v
+        self.io_torch = _io_torch(desc.io_dtype)
+        self.state = self._state_buf.view(desc.n_slots, desc.n_layers, desc.h_v, desc.d_v, desc.d_k)
+        io_size = 2 if desc.io_dtype == GDN_BF16 else 4
+        nwin = desc.n_slots * desc.n_layers * (desc.conv_k - 1) * self.c_conv
+        self.window = self._aux_buf[: nwin * io_size].view(self.io_torch).view(
+            desc.n_slots, desc.n_layers, desc.conv_k - 1, self.c_conv)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load_library().gdn_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- calls -------------------------------------------------------------
+    def reset(self, slot_ids, stream=None):
+        lib = load_library()
+        _check(lib.gdn_slot_reset(self._h, int(slot_ids.numel()), _ptr(slot_ids), _stream(stream)),
+               "gdn_slot_reset")
+
+    def decode(self, layer, slot_ids, q, k, v, a, b, conv_w, out, stream=None):
+        lib = load_library()
+        _check(lib.gdn_decode_step(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), _ptr(q),
+                                   _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(out),
+                                   _stream(stream)), "gdn_decode_step")
+        return out
+
+    def verify(self, layer, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len, out, stream=None):
+        lib = load_library()
+        _check(lib.gdn_verify_step(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), n_tok,
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
+                                   _ptr(accept_len), _ptr(out), _stream(stream)),
+               "gdn_verify_step")
+        return out
+
+    def prefill_workspace_bytes(self, n_seq, total_tokens, chunk):
+        lib = load_library()
+        n = ctypes.c_size_t()
+        _check(lib.gdn_prefill_workspace_bytes(self._h, n_seq, total_tokens, chunk,
+                                               ctypes.byref(n)), "gdn_prefill_workspace_bytes")
+        return n.value
+
+    def prefill(self, layer, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v, a, b, conv_w,
+                out, workspace=None, stream=None):
+        lib = load_library()
+        n_seq = int(slot_ids.numel())
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib.gdn_prefill_chunked(self._h, layer, n_seq, _ptr(cu_seqlens), _ptr(slot_ids),
+                                       total_tokens, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                       _ptr(b), _ptr(conv_w), _ptr(out), _ptr(workspace), ws_bytes,
+                                       _stream(stream)), "gdn_prefill_chunked")
+        return out
+
+    def error(self, stream=None) -> int:
+        lib = load_library()
+        e = ctypes.c_int32()
+        _check(lib.gdn_pool_error(self._h, _stream(stream), ctypes.byref(e)), "gdn_pool_error")
+        return e.value

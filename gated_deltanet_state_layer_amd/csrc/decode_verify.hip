@@ -1,0 +1,244 @@
+// Multi-slot decode and speculative verify for the gated delta rule.
+//
+// One workgroup owns one (entry, q/k head group): the conv channels of that
+// group (its q head, its k head and the G = h_v/h_k value heads that share
+// them) and the G fp32 [d_v][d_k] state tiles of those value heads in the
+// entry's slot.  No other workgroup touches these channels or tiles, so the
+// in-place conv-window roll and the state write-back need no cross-workgroup
+// ordering (baseRT issue #31, "Why this looks tractable": a slot index in the
+// recurrence and conv kernels).
+//
+// The state update is bound by HBM: each tile is read once and written once
+// (bytes per slot: 2 * h_v * d_v * d_k * 4).  Each row of a tile is split over
+// D/8 lanes holding 8 fp32 columns (two 16-byte loads), so a wave instruction
+// moves contiguous 256/128/64-byte row segments.  A row's two dot products
+// (S.k and S.q) are summed across its lanes with DPP, then
+//     delta = b (v - a S.k),  S <- a S + delta k^T,  o = a S.q + delta k.q
+// which is S <- a S (I - b k k^T) + b v k^T and o = S_new q written as one
+// pass over the row ("Plan (research-based): Qwen3.6-35B-A3B", "What the
+// research found": delta rule over a [V,K] state).
+//
+// Verify keeps each thread's rows in registers across the n_tok tokens, writes
+// every position's output and stores the rows once, after accept_len tokens
+// ("Plan (research-based)", "What the research found" and "Why >150 is still
+// reachable": no per-position state snapshots).  Decode is the same kernel
+// with one token, so verify positions are bitwise equal to decode steps.
+#include "gdn_common.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D, typename T>
+__global__ __launch_bounds__(kThreads) void decode_verify_kernel(
+    PoolView P, int layer, const int32_t* __restrict__ slot_ids, int n_tok,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ conv_w,
+    const int32_t* __restrict__ accept_len, T* __restrict__ out) {
+    extern __shared__ float smem[];
+    const int tid = threadIdx.x;
+    const int g = blockIdx.x;   // q/k head group
+    const int i = blockIdx.y;   // entry
+    const int slot = slot_ids[i];
+    if (slot < 0) return;  // padding entry
+    if (slot >= P.n_slots) {
+        if (tid == 0) atomicOr(P.err, kErrSlotRange);
+        return;
+    }
+    const int G = P.h_v / P.h_k;
+    const int K = P.conv_k;
+    const int C = P.c_conv;
+    const int nch = (2 + G) * D;  // channels owned by this group
+    int commit = n_tok;
+    if (accept_len) commit = min(max(accept_len[i], 0), n_tok);
+
+    // LDS: line [K-1+n_tok][nch] raw inputs (window rows, then tokens),
+    //      act  [n_tok][nch]     conv+SiLU outputs,
+    //      nrm  [n_tok][3]       q scale, k scale, k.q
+    const int L = K - 1 + n_tok;
+    float* line = smem;
+    float* act = line + L * nch;
+    float* nrm = act + n_tok * nch;
+
+    // ---- front end: depthwise causal conv + SiLU over the group's channels.
+    T* win = reinterpret_cast<T*>(P.window) +
+             ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
+    for (int c = tid; c < nch; c += kThreads) {
+        int gc;             // global channel
+        const T* src;       // token 0 of this channel
+        int64_t tstride;    // element stride between tokens
+        if (c < D) {
+            gc = g * D + c;
+            src = q + ((int64_t)i * n_tok * P.h_k + g) * D + c;
+            tstride = (int64_t)P.h_k * D;
+        } else if (c < 2 * D) {
+            gc = P.h_k * D + g * D + (c - D);
+            src = k + ((int64_t)i * n_tok * P.h_k + g) * D + (c - D);
+            tstride = (int64_t)P.h_k * D;
+        } else {
+            gc = 2 * P.h_k * D + g * G * D + (c - 2 * D);
+            src = v + ((int64_t)i * n_tok * P.h_v + g * G) * D + (c - 2 * D);
+            tstride = (int64_t)P.h_v * D;
+        }
+        for (int r = 0; r < K - 1; ++r) line[r * nch + c] = Io<T>::load(win, (int64_t)r * C + gc);
+        for (int t = 0; t < n_tok; ++t) line[(K - 1 + t) * nch + c] = Io<T>::load(src, t * tstride);
+        const float* wc = conv_w + (int64_t)gc * K;
+        for (int t = 0; t < n_tok; ++t) {
+            float z = 0.f;
+            for (int j = 0; j < K; ++j) z = fmaf(wc[j], line[(t + j) * nch + c], z);
+            act[t * nch + c] = silu(z);
+        }
+        // Roll the window by `commit` tokens (same thread, after all reads).
+        if (commit > 0)
+            for (int r = 0; r < K - 1; ++r)
+                Io<T>::store(win, (int64_t)r * C + gc, line[(commit + r) * nch + c]);
+    }
+    __syncthreads();
+
+    // ---- q/k normalisation factors and k.q per token (one wave per token).
+    {
+        const int wave = tid >> 6, lane = tid & 63;
+        for (int t = wave; t < n_tok; t += kThreads / 64) {
+            float sq = 0.f, sk = 0.f, sqk = 0.f;
+            for (int c = lane; c < D; c += 64) {
+                const float xq = act[t * nch + c], xk = act[t * nch + D + c];
+                sq = fmaf(xq, xq, sq);
+                sk = fmaf(xk, xk, sk);
+                sqk = fmaf(xq, xk, sqk);
+            }
+            sq = wave_sum(sq);
+            sk = wave_sum(sk);
+            sqk = wave_sum(sqk);
+            if (lane == 0) {
+                const float rq = P.q_scale / sqrtf(sq + P.eps);
+                const float rk = 1.0f / sqrtf(sk + P.eps);
+                nrm[t * 3 + 0] = rq;
+                nrm[t * 3 + 1] = rk;
+                nrm[t * 3 + 2] = sqk * rq * rk;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- state tiles: rows split over LPR lanes, 8 columns per lane.
+    constexpr int LPR = D / 8;              // lanes per row
+    constexpr int RPP = kThreads / LPR;     // rows per pass
+    constexpr int NP = (D + RPP - 1) / RPP; // passes per tile
+    const int lr = tid % LPR;
+    const int row0 = tid / LPR;
+    const int c0 = 4 * lr, c1 = D / 2 + 4 * lr;
+
+    for (int hl = 0; hl < G; ++hl) {
+        const int hv = g * G + hl;
+        float* tile = P.state + (((int64_t)slot * P.n_layers + layer) * P.h_v + hv) * (int64_t)D * D;
+        float s[NP][8];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int row = row0 + p * RPP;
+            if (row < D) {
+                const float4 x0 = *reinterpret_cast<const float4*>(tile + row * D + c0);
+                const float4 x1 = *reinterpret_cast<const float4*>(tile + row * D + c1);
+                s[p][0] = x0.x; s[p][1] = x0.y; s[p][2] = x0.z; s[p][3] = x0.w;
+                s[p][4] = x1.x; s[p][5] = x1.y; s[p][6] = x1.z; s[p][7] = x1.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[p][e] = 0.f;
+            }
+        }
+        for (int t = 0; t < n_tok; ++t) {
+            const float* y = act + t * nch;
+            const float rq = nrm[t * 3 + 0], rk = nrm[t * 3 + 1], kq = nrm[t * 3 + 2];
+            float kc[8], qc[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qc[e] = y[c0 + e] * rq;
+                qc[4 + e] = y[c1 + e] * rq;
+                kc[e] = y[D + c0 + e] * rk;
+                kc[4 + e] = y[D + c1 + e] * rk;
+            }
+            const int64_t tok = (int64_t)i * n_tok + t;
+            const float at = a[tok * P.h_v + hv];
+            const float bt = b[tok * P.h_v + hv];
+            T* o_row = out + (tok * P.h_v + hv) * D;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                float u = 0.f, pq = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    u = fmaf(s[p][e], kc[e], u);
+                    pq = fmaf(s[p][e], qc[e], pq);
+                }
+                u = group_sum<LPR>(u);
+                pq = group_sum<LPR>(pq);
+                const int row = row0 + p * RPP;
+                const float vi = (row < D) ? y[2 * D + hl * D + row] : 0.f;
+                const float delta = bt * (vi - at * u);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[p][e] = fmaf(at, s[p][e], delta * kc[e]);
+                if (lr == 0 && row < D) Io<T>::store(o_row, row, fmaf(at, pq, delta * kq));
+            }
+            if (t + 1 == commit) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    const int row = row0 + p * RPP;
+                    if (row < D) {
+                        *reinterpret_cast<float4*>(tile + row * D + c0) =
+                            make_float4(s[p][0], s[p][1], s[p][2], s[p][3]);
+                        *reinterpret_cast<float4*>(tile + row * D + c1) =
+                            make_float4(s[p][4], s[p][5], s[p][6], s[p][7]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int D, typename T>
+hipError_t launch_dv(const gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                     int32_t n_tok, const void* q, const void* k, const void* v, const float* a,
+                     const float* b, const float* conv_w, const int32_t* accept_len, void* out,
+                     hipStream_t stream) {
+    const PoolView& P = pool->view;
+    const int G = P.h_v / P.h_k;
+    const size_t lds = (size_t)(P.conv_k - 1 + 2 * n_tok) * (2 + G) * D * sizeof(float) +
+                       (size_t)n_tok * 3 * sizeof(float);
+    dim3 grid(P.h_k, n);
+    hipLaunchKernelGGL((decode_verify_kernel<D, T>), grid, dim3(kThreads), lds, stream, P, layer,
+                       slot_ids, n_tok, static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), a, b, conv_w, accept_len, static_cast<T*>(out));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_verify_lds_bytes(const gdn_pool* pool, int32_t n_tok) {
+    const PoolView& P = pool->view;
+    const int G = P.h_v / P.h_k;
+    return (size_t)(P.conv_k - 1 + 2 * n_tok) * (2 + G) * P.d * sizeof(float) +
+           (size_t)n_tok * 3 * sizeof(float);
+}
+
+hipError_t launch_decode_verify(const gdn_pool* pool, int32_t layer, int32_t n,
+                                const int32_t* slot_ids, int32_t n_tok, const void* q,
+                                const void* k, const void* v, const float* a, const float* b,
+                                const float* conv_w, const int32_t* accept_len, void* out,
+                                hipStream_t stream) {
+    const bool bf = pool->desc.io_dtype == GDN_BF16;
+    switch (pool->view.d) {
+#define GDN_CASE(DD)                                                                             \
+    case DD:                                                                                     \
+        return bf ? launch_dv<DD, uint16_t>(pool, layer, n, slot_ids, n_tok, q, k, v, a, b,      \
+                                            conv_w, accept_len, out, stream)                     \
+                  : launch_dv<DD, float>(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, \
+                                         accept_len, out, stream);
+        GDN_CASE(32)
+        GDN_CASE(64)
+        GDN_CASE(128)
+#undef GDN_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn

@@ -1,0 +1,264 @@
+// libgdn host API: descriptor checks, the slot pool, argument validation and
+// dispatch to the kernels.  Every check runs before anything is enqueued, so
+// a negative status leaves device memory untouched.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <new>
+#include <vector>
+
+#include "gdn_common.h"
+
+namespace gdn {
+size_t decode_verify_lds_bytes(const gdn_pool* pool, int32_t n_tok);
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kMaxLds = 64 * 1024;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+gdn_status check_desc(const gdn_pool_desc* d) {
+    if (!d) return GDN_ERR_INVALID_ARG;
+    if (d->n_slots < 1 || d->n_layers < 1 || d->h_k < 1 || d->h_v < 1 || d->d_k < 1 ||
+        d->d_v < 1 || d->conv_k < 1)
+        return GDN_ERR_INVALID_ARG;
+    if (d->h_v % d->h_k != 0) return GDN_ERR_INVALID_ARG;
+    if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+    if (!(d->q_scale >= 0.f) || !(d->norm_eps >= 0.f) || std::isinf(d->q_scale) ||
+        std::isinf(d->norm_eps))
+        return GDN_ERR_INVALID_ARG;
+    if (d->flags & ~GDN_VALIDATE) return GDN_ERR_INVALID_ARG;
+    if (d->d_k != d->d_v) return GDN_ERR_UNSUPPORTED;
+    if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return GDN_ERR_UNSUPPORTED;
+    if (d->conv_k < 2 || d->conv_k > kMaxConvK) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+void layout(const gdn_pool_desc* d, size_t* state_bytes, size_t* window_bytes, size_t* aux_bytes) {
+    const size_t io = d->io_dtype == GDN_BF16 ? 2 : 4;
+    const size_t c_conv = 2 * (size_t)d->h_k * d->d_k + (size_t)d->h_v * d->d_v;
+    *state_bytes = (size_t)d->n_slots * d->n_layers * d->h_v * d->d_v * d->d_k * sizeof(float);
+    *window_bytes = (size_t)d->n_slots * d->n_layers * (d->conv_k - 1) * c_conv * io;
+    *aux_bytes = align_up(*window_bytes, kAlign) + kAlign;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// GDN_VALIDATE: copy a device index array to the host and check it.
+gdn_status host_check_ids(const int32_t* ids, int32_t n, int32_t n_slots, hipStream_t s) {
+    std::vector<int32_t> h(n);
+    if (n == 0) return GDN_OK;
+    if (hipMemcpyAsync(h.data(), ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
+    std::vector<int32_t> seen;
+    for (int32_t x : h) {
+        if (x >= n_slots) return GDN_ERR_BAD_INDEX;
+        if (x >= 0) seen.push_back(x);
+    }
+    std::sort(seen.begin(), seen.end());
+    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return GDN_ERR_BAD_INDEX;
+    return GDN_OK;
+}
+
+gdn_status host_check_seqlens(const int32_t* cu, int32_t n_seq, int64_t total, hipStream_t s) {
+    std::vector<int32_t> h(n_seq + 1);
+    if (hipMemcpyAsync(h.data(), cu, (n_seq + 1) * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+        hipSuccess)
+        return GDN_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
+    if (h[0] != 0 || h[n_seq] != total) return GDN_ERR_BAD_INDEX;
+    for (int j = 0; j < n_seq; ++j)
+        if (h[j + 1] < h[j]) return GDN_ERR_BAD_INDEX;
+    return GDN_OK;
+}
+
+}  // namespace
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+gdn_status gdn_pool_bytes(const gdn_pool_desc* desc, size_t* state_bytes, size_t* aux_bytes) {
+    gdn_status st = check_desc(desc);
+    if (st != GDN_OK) return st;
+    if (!state_bytes || !aux_bytes) return GDN_ERR_INVALID_ARG;
+    size_t wb;
+    layout(desc, state_bytes, &wb, aux_bytes);
+    return GDN_OK;
+}
+
+gdn_status gdn_pool_create(const gdn_pool_desc* desc, void* state_buf, void* aux_buf, void* stream,
+                           gdn_pool** out) {
+    gdn_status st = check_desc(desc);
+    if (st != GDN_OK) return st;
+    if (!state_buf || !aux_buf || !out) return GDN_ERR_INVALID_ARG;
+    if (!aligned(state_buf, kAlign) || !aligned(aux_buf, kAlign)) return GDN_ERR_INVALID_ARG;
+    gdn_pool* p = new (std::nothrow) gdn_pool();
+    if (!p) return GDN_ERR_INVALID_ARG;
+    p->desc = *desc;
+    if (p->desc.q_scale == 0.f) p->desc.q_scale = 1.0f / std::sqrt((float)desc->d_k);
+    if (p->desc.norm_eps == 0.f) p->desc.norm_eps = 1e-6f;
+    layout(desc, &p->state_bytes, &p->window_bytes, &p->aux_bytes);
+    p->io_size = desc->io_dtype == GDN_BF16 ? 2 : 4;
+    PoolView& v = p->view;
+    v.state = static_cast<float*>(state_buf);
+    v.window = aux_buf;
+    v.err = reinterpret_cast<int32_t*>(static_cast<char*>(aux_buf) + align_up(p->window_bytes, kAlign));
+    v.n_slots = desc->n_slots;
+    v.n_layers = desc->n_layers;
+    v.h_k = desc->h_k;
+    v.h_v = desc->h_v;
+    v.d = desc->d_k;
+    v.conv_k = desc->conv_k;
+    v.c_conv = 2 * desc->h_k * desc->d_k + desc->h_v * desc->d_v;
+    v.q_scale = p->desc.q_scale;
+    v.eps = p->desc.norm_eps;
+    hipStream_t s = as_stream(stream);
+    if (launch_fill_zero(state_buf, p->state_bytes, s) != hipSuccess ||
+        launch_fill_zero(aux_buf, p->aux_bytes, s) != hipSuccess) {
+        delete p;
+        return GDN_ERR_HIP;
+    }
+    *out = p;
+    return GDN_OK;
+}
+
+gdn_status gdn_pool_destroy(gdn_pool* pool) {
+    if (!pool) return GDN_ERR_INVALID_ARG;
+    delete pool;
+    return GDN_OK;
+}
+
+gdn_status gdn_slot_reset(gdn_pool* pool, int32_t n, const int32_t* slot_ids, void* stream) {
+    if (!pool || n < 0 || (n > 0 && !slot_ids)) return GDN_ERR_INVALID_ARG;
+    if (n == 0) return GDN_OK;
+    if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
+    hipStream_t s = as_stream(stream);
+    if (pool->desc.flags & GDN_VALIDATE) {
+        gdn_status st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+        if (st != GDN_OK) return st;
+    }
+    return launch_slot_reset(pool, n, slot_ids, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+static gdn_status check_step_args(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                                  int32_t n_tok, const void* q, const void* k, const void* v,
+                                  const float* a, const float* b, const float* conv_w,
+                                  const void* out) {
+    if (!pool) return GDN_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= pool->desc.n_layers || n < 0) return GDN_ERR_INVALID_ARG;
+    if (n_tok < 1 || n_tok > kMaxVerifyTokens) return GDN_ERR_INVALID_ARG;
+    if (n > 0 && (!slot_ids || !q || !k || !v || !a || !b || !conv_w || !out))
+        return GDN_ERR_INVALID_ARG;
+    if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
+    if (decode_verify_lds_bytes(pool, n_tok) > kMaxLds) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                           const void* q, const void* k, const void* v, const float* a,
+                           const float* b, const float* conv_w, void* out, void* stream) {
+    gdn_status st = check_step_args(pool, layer, n, slot_ids, 1, q, k, v, a, b, conv_w, out);
+    if (st != GDN_OK || n == 0) return st;
+    hipStream_t s = as_stream(stream);
+    if (pool->desc.flags & GDN_VALIDATE) {
+        st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+        if (st != GDN_OK) return st;
+    }
+    return launch_decode_verify(pool, layer, n, slot_ids, 1, q, k, v, a, b, conv_w, nullptr, out,
+                                s) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                           int32_t n_tok, const void* q, const void* k, const void* v,
+                           const float* a, const float* b, const float* conv_w,
+                           const int32_t* accept_len, void* out, void* stream) {
+    gdn_status st = check_step_args(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, out);
+    if (st != GDN_OK) return st;
+    if (n > 0 && !accept_len) return GDN_ERR_INVALID_ARG;
+    if (n == 0) return GDN_OK;
+    hipStream_t s = as_stream(stream);
+    if (pool->desc.flags & GDN_VALIDATE) {
+        st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+        if (st != GDN_OK) return st;
+    }
+    return launch_decode_verify(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len,
+                                out, s) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+gdn_status gdn_prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
+                                       int32_t chunk, size_t* bytes) {
+    if (!pool || !bytes || n_seq < 0 || total_tokens < 0) return GDN_ERR_INVALID_ARG;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
+    *bytes = prefill_workspace_bytes(pool, n_seq, total_tokens, chunk);
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
+                               const int32_t* cu_seqlens, const int32_t* slot_ids,
+                               int64_t total_tokens, int32_t chunk, const void* q, const void* k,
+                               const void* v, const float* a, const float* b, const float* conv_w,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!pool || layer < 0 || layer >= pool->desc.n_layers || n_seq < 0 || total_tokens < 0)
+        return GDN_ERR_INVALID_ARG;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (total_tokens > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (n_seq == 0) return GDN_OK;
+    if (!cu_seqlens || !slot_ids || !conv_w) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !k || !v || !a || !b || !out)) return GDN_ERR_INVALID_ARG;
+    const size_t need = prefill_workspace_bytes(pool, n_seq, total_tokens, chunk);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, kAlign)) return GDN_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    if (pool->desc.flags & GDN_VALIDATE) {
+        gdn_status st = host_check_ids(slot_ids, n_seq, pool->desc.n_slots, s);
+        if (st != GDN_OK) return st;
+        st = host_check_seqlens(cu_seqlens, n_seq, total_tokens, s);
+        if (st != GDN_OK) return st;
+    }
+    hipError_t e = launch_prefill(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q,
+                                  k, v, a, b, conv_w, out, workspace, s);
+    if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_pool_error(gdn_pool* pool, void* stream, int32_t* device_error) {
+    if (!pool || !device_error) return GDN_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    int32_t h = 0;
+    if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
+    if (hipMemcpy(&h, pool->view.err, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (h != 0) {
+        if (launch_fill_zero(pool->view.err, kAlign, s) != hipSuccess) return GDN_ERR_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return GDN_ERR_HIP;
+    }
+    *device_error = h;
+    return GDN_OK;
+}
+
+const char* gdn_status_string(gdn_status status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARG: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported shape or option";
+        case GDN_ERR_BAD_INDEX: return "slot id out of range or repeated, or malformed cu_seqlens";
+        case GDN_ERR_WORKSPACE: return "prefill workspace too small";
+        case GDN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Shared device helpers and the internal launcher interface of libgdn.
+// gfx950 (CDNA4) only: wave64, DPP cross-lane moves, bf16 storage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+constexpr int kMaxConvK = 8;
+constexpr int kMaxVerifyTokens = 8;
+
+// Sticky error bits written to the pool's meta word.
+constexpr int kErrSlotRange = 1;
+constexpr int kErrSeqlens = 2;
+
+// ----------------------------------------------------------------- bf16 / io
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Activation element access for the two io dtypes.
+template <typename T> struct Io;
+template <> struct Io<float> {
+    __device__ static __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+    __device__ static __forceinline__ void store(float* p, int64_t i, float x) { p[i] = x; }
+};
+template <> struct Io<uint16_t> {
+    __device__ static __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+    __device__ static __forceinline__ void store(uint16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+// ----------------------------------------------------------- cross-lane sums
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W = 2, 4, 8 or 16); every lane of the
+// group receives the sum.  Uses DPP inside 16-lane rows: quad swaps, then the
+// half-row and row mirrors (after the quad steps every quad holds its own sum,
+// so any pairing of quads completes the reduction).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(W == 2 || W == 4 || W == 8 || W == 16, "group width");
+    x += dpp_mov<0xB1>(x);                      // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) x += dpp_mov<0x4E>(x); // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) x += dpp_mov<0x141>(x); // row_half_mirror
+    if constexpr (W >= 16) x += dpp_mov<0x140>(x); // row_mirror
+    return x;
+}
+
+// Full 64-lane sum, result in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+    x = group_sum<16>(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------ pool (device)
+
+struct PoolView {
+    float* state;         // [n_slots][n_layers][h_v][d_v][d_k]
+    void* window;         // [n_slots][n_layers][conv_k-1][C_conv] io dtype
+    int32_t* err;         // sticky error word
+    int32_t n_slots, n_layers, h_k, h_v, d, conv_k, c_conv;
+    float q_scale, eps;
+};
+
+}  // namespace gdn
+
+// Host-side pool object (opaque to callers).
+struct gdn_pool {
+    gdn_pool_desc desc;
+    gdn::PoolView view;
+    size_t state_bytes, aux_bytes, window_bytes;
+    int io_size;
+};
+
+namespace gdn {
+
+// Kernel launchers (defined next to their kernels).  All return hipError_t
+// from the launch; arguments were validated by the caller.
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+hipError_t launch_slot_reset(const gdn_pool* pool, int32_t n, const int32_t* slot_ids,
+                             hipStream_t stream);
+hipError_t launch_decode_verify(const gdn_pool* pool, int32_t layer, int32_t n,
+                                const int32_t* slot_ids, int32_t n_tok, const void* q,
+                                const void* k, const void* v, const float* a, const float* b,
+                                const float* conv_w, const int32_t* accept_len, void* out,
+                                hipStream_t stream);
+size_t prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
+                               int32_t chunk);
+hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,
+                          const int32_t* cu_seqlens, const int32_t* slot_ids,
+                          int64_t total_tokens, int32_t chunk, const void* q, const void* k,
+                          const void* v, const float* a, const float* b, const float* conv_w,
+                          void* out, void* workspace, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,193 @@
+/*
+ * gdn.h -- C ABI of libgdn, a Gated DeltaNet (GDN) state layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer core is the gated delta rule over a depthwise causal
+ * conv1d + SiLU front end:
+ *     y      = silu(depthwise causal conv of the raw q|k|v channels)
+ *     q^, k^ = per-head L2 normalisation of q, k (q^ also times q_scale)
+ *     S_t    = a_t * S_{t-1} (I - b_t k^_t k^_t^T) + b_t v_t k^_t^T
+ *     o_t    = S_t q^_t
+ * with one fp32 [d_v, d_k] state per value head and request ("Plan
+ * (research-based): Qwen3.6-35B-A3B", section "What the research found":
+ * delta rule, full [V,K] state, chunked (I+A)^-1 UT-transform prefill).
+ *
+ * It runs over a pool of independent fixed-size request slots: an outer slot
+ * dimension on the state cache and a slot index in every kernel (baseRT issue
+ * #31, sections "Why this looks tractable" and "Scope note"); each slot holds
+ * one conv window and one recurrent state per layer, a new request starts
+ * from zero and chunked prefill carries the state from chunk to chunk
+ * ("Project: adding the hybrid model Qwen3.5", table "What to do", row
+ * "State").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Memory: the caller owns every device buffer (pool, inputs, outputs,
+ *    workspace); the library never allocates device memory.  All pointers
+ *    marked "device" are device pointers; index arrays (slot_ids, cu_seqlens,
+ *    accept_len) are device arrays too, so calls never read them on the host
+ *    (except in GDN_VALIDATE mode, below).
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Every call only enqueues work on it and returns; nothing
+ *    synchronises except gdn_pool_error and GDN_VALIDATE mode.  Calls are
+ *    therefore safe to record into a HIP graph (no memset nodes are used).
+ *  - Errors: a negative gdn_status means the call enqueued nothing and
+ *    touched no memory.  Out-of-range slot ids found by a kernel (id >=
+ *    n_slots) skip that entry and set a sticky device error word, read with
+ *    gdn_pool_error.  A negative slot id marks a padding entry: skipped
+ *    silently, its output rows are left unwritten.
+ *  - Threads: a pool may be used from several host threads, but calls that
+ *    touch the same slot must be ordered by the caller (same stream or
+ *    events).  Slot ids within one call must be distinct; a duplicate is a
+ *    data race (GDN_VALIDATE rejects it).
+ *
+ * Pool memory layout (part of the ABI: tests and checkpointing may read or
+ * write a slot directly):
+ *   state buffer, fp32, row-major
+ *       [n_slots][n_layers][h_v][d_v][d_k]        (d_k contiguous)
+ *   aux buffer:
+ *       conv windows, io dtype, [n_slots][n_layers][conv_k-1][C_conv]
+ *       (row 0 = oldest raw input; C_conv = 2*h_k*d_k + h_v*d_v channels in
+ *       the order q heads | k heads | v heads, each head's d contiguous),
+ *       then, at the next 256-byte boundary, a 256-byte meta block whose
+ *       first int32 is the sticky device error word.
+ *
+ * Activations: per token, raw q, k are [h_k][d_k] and v is [h_v][d_v] in the
+ * io dtype; a and b are [h_v] fp32, already activated (a in (0,1], b in
+ * [0,1]).  Value head h reads q/k head h / (h_v/h_k).  Conv weights are fp32
+ * [C_conv][conv_k]; tap conv_k-1 multiplies the current token.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gdn_pool gdn_pool; /* opaque: host metadata + borrowed device pointers */
+
+typedef int32_t gdn_status;
+#define GDN_OK 0
+#define GDN_ERR_INVALID_ARG (-1) /* null pointer, bad size or range */
+#define GDN_ERR_UNSUPPORTED (-2) /* shape outside the compiled kernels */
+#define GDN_ERR_BAD_INDEX (-3)   /* GDN_VALIDATE: slot id out of range or repeated */
+#define GDN_ERR_WORKSPACE (-4)   /* prefill workspace too small */
+#define GDN_ERR_HIP (-5)         /* a HIP runtime call failed */
+
+typedef int32_t gdn_dtype;
+#define GDN_F32 0
+#define GDN_BF16 1
+
+/* flags */
+#define GDN_VALIDATE 1u /* check device index arrays on the host (synchronises) */
+
+typedef struct {
+    int32_t n_slots;   /* >= 1 */
+    int32_t n_layers;  /* >= 1 */
+    int32_t h_k;       /* q/k heads, >= 1 */
+    int32_t h_v;       /* value heads, a multiple of h_k */
+    int32_t d_k;       /* head widths: d_k == d_v, one of 32, 64, 128 */
+    int32_t d_v;
+    int32_t conv_k;    /* conv taps, 2..8 */
+    gdn_dtype io_dtype; /* GDN_F32 or GDN_BF16: q, k, v, outputs and windows */
+    float q_scale;     /* multiplies the normalised q; 0 -> 1/sqrt(d_k) */
+    float norm_eps;    /* eps in x/sqrt(|x|^2+eps); 0 -> 1e-6 */
+    uint32_t flags;    /* GDN_VALIDATE or 0 */
+} gdn_pool_desc;
+
+/* Bytes the caller must allocate for a pool with this descriptor: the fp32
+ * state buffer and the aux buffer (conv windows + meta).  Both buffers must be
+ * 256-byte aligned.  Returns INVALID_ARG / UNSUPPORTED for a bad descriptor. */
+gdn_status gdn_pool_bytes(const gdn_pool_desc* desc, size_t* state_bytes, size_t* aux_bytes);
+
+/* Create a pool over caller-owned device buffers sized by gdn_pool_bytes and
+ * zero them on `stream` (every slot starts from zero state and window).  The
+ * buffers must outlive the pool.  *out receives a host handle. */
+gdn_status gdn_pool_create(const gdn_pool_desc* desc, void* state_buf, void* aux_buf,
+                           void* stream, gdn_pool** out);
+
+/* Free the host handle (device buffers are the caller's). */
+gdn_status gdn_pool_destroy(gdn_pool* pool);
+
+/* Zero the state and conv window of every layer of the n listed slots
+ * (slot_ids: device int32[n]); a reused slot starts from zero ("Project:
+ * adding the hybrid model Qwen3.5", table "What to do", row "State"). */
+gdn_status gdn_slot_reset(gdn_pool* pool, int32_t n, const int32_t* slot_ids, void* stream);
+
+/* One decode token for each of n entries; entry i reads and writes slot
+ * slot_ids[i] of layer `layer` (baseRT issue #31, "Why this looks tractable":
+ * a slot index in the recurrence kernels).
+ *   q, k    device io dtype [n][h_k][d_k]      raw (pre-conv) inputs
+ *   v       device io dtype [n][h_v][d_v]
+ *   a, b    device fp32 [n][h_v]
+ *   conv_w  device fp32 [C_conv][conv_k]        this layer's conv weights
+ *   out     device io dtype [n][h_v][d_v]       o = S q^ with the updated S
+ * The state and window of each listed slot advance by one token; every other
+ * slot is left bitwise unchanged. */
+gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                           const void* q, const void* k, const void* v, const float* a,
+                           const float* b, const float* conv_w, void* out, void* stream);
+
+/* Speculative verify: n_tok tokens (1..8) per entry run through the
+ * recurrence in order, every position's output is written, and the slot keeps
+ * the state and window reached after accept_len[i] tokens (0..n_tok; 0 leaves
+ * the slot untouched).  No per-position state copies are stored ("Plan
+ * (research-based)", sections "What the research found" and "Why >150 is
+ * still reachable": the per-position state is the costly part of verify).
+ *   q, k       device io dtype [n][n_tok][h_k][d_k]
+ *   v          device io dtype [n][n_tok][h_v][d_v]
+ *   a, b       device fp32 [n][n_tok][h_v]
+ *   accept_len device int32 [n]; values outside 0..n_tok are clamped
+ *   out        device io dtype [n][n_tok][h_v][d_v]
+ * Each position's output is bitwise the output of the same number of
+ * gdn_decode_step calls. */
+gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                           int32_t n_tok, const void* q, const void* k, const void* v,
+                           const float* a, const float* b, const float* conv_w,
+                           const int32_t* accept_len, void* out, void* stream);
+
+/* Workspace bytes for gdn_prefill_chunked with these sizes (an upper bound
+ * that depends only on n_seq, total_tokens and chunk). */
+gdn_status gdn_prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
+                                       int32_t chunk, size_t* bytes);
+
+/* Chunked prefill of n_seq packed sequences, sequence j = tokens
+ * [cu_seqlens[j], cu_seqlens[j+1]) into slot slot_ids[j], starting from what
+ * the slot holds (zero after reset, or an earlier chunk's state and window:
+ * scheduler chunks carry over).  Inside a call each sequence is cut into
+ * chunks of `chunk` tokens (16, 32 or 64) aligned to its start; each chunk is
+ * solved in the (I+A)^-1 UT-transform form and the state is carried chunk to
+ * chunk ("Plan (research-based)", "What the research found"; "Project: adding
+ * the hybrid model Qwen3.5", "What to do", row "State").
+ *   cu_seqlens device int32 [n_seq+1]: 0, non-decreasing, last = total_tokens
+ *   slot_ids   device int32 [n_seq]
+ *   q, k       device io dtype [total_tokens][h_k][d_k]
+ *   v          device io dtype [total_tokens][h_v][d_v]
+ *   a, b       device fp32 [total_tokens][h_v]
+ *   out        device io dtype [total_tokens][h_v][d_v]
+ *   workspace  device, >= gdn_prefill_workspace_bytes, 256-byte aligned;
+ *              scratch only, contents undefined afterwards
+ * Zero-length sequences are no-ops. */
+gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
+                               const int32_t* cu_seqlens, const int32_t* slot_ids,
+                               int64_t total_tokens, int32_t chunk, const void* q, const void* k,
+                               const void* v, const float* a, const float* b,
+                               const float* conv_w, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Synchronise `stream`, then read and clear the sticky device error word
+ * (0 = none; bit 0 = a slot id >= n_slots was skipped; bit 1 = a malformed
+ * cu_seqlens was seen). */
+gdn_status gdn_pool_error(gdn_pool* pool, void* stream, int32_t* device_error);
+
+/* Static text for a status code. */
+const char* gdn_status_string(gdn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,103 @@
+"""Helpers for the GPU parity tests: device upload, pools filled from the
+seeded generators, oracle pools holding the same slot contents, and the
+comparison metrics."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import gdn_synth as syn
+from oracle import gdn_oracle as O
+
+TOL_F32 = 1e-3       # fp32 outputs and all final states: max|x-ref| / RMS(ref)
+TOL_BF16 = 2e-2      # bf16 outputs, on top of half a bf16 ulp of each reference value
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev(x, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dtype).to("cuda")
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def io_torch(io):
+    return torch.bfloat16 if io == "bf16" else torch.float32
+
+
+def make_pool(s: syn.Shapes, n_slots, io, n_layers=1, flags=0):
+    import gated_deltanet_state_layer_amd as G
+    d = G.make_desc(n_slots, n_layers, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k,
+                    G.GDN_BF16 if io == "bf16" else G.GDN_F32, 0.0, 0.0, flags)
+    return G.Pool(d)
+
+
+def scramble_pool(pool, seed):
+    """Fill every slot with seeded noise (for bitwise untouched-slot checks)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    pool.state.normal_(generator=g)
+    w = torch.randn(pool.window.shape, generator=g, device="cuda")
+    pool.window.copy_(w.to(pool.window.dtype))
+    torch.cuda.synchronize()
+
+
+def load_slots(pool, contents: dict):
+    for slot, (st, wn) in contents.items():
+        pool.state[slot].copy_(dev(st))
+        pool.window[slot].copy_(dev(wn, pool.window.dtype))
+    torch.cuda.synchronize()
+
+
+def oracle_pool(s, contents: dict, slot_order, n_layers=1, form="matrix"):
+    """An oracle pool whose slot j holds contents[slot_order[j]]."""
+    op = O.OraclePool(len(slot_order), n_layers, s, form=form)
+    for j, slot in enumerate(slot_order):
+        if contents is not None and int(slot) in contents:
+            st, wn = contents[int(slot)]
+            op.S[j] = st
+            op.X[j] = wn
+    return op
+
+
+def tokens_to_dev(tok, io):
+    t = io_torch(io)
+    return {n: dev(tok[n], t if n in "qkv" else torch.float32) for n in ("q", "k", "v", "a", "b")}
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    return float(np.max(np.abs(x - ref)) / rms) if ref.size else 0.0
+
+
+def check_f32(name, x, ref, tol=TOL_F32):
+    e = rel_err(x, ref)
+    say(f"  {name}: max|err|/rms = {e:.3e} (tol {tol:g})")
+    assert np.isfinite(np.asarray(x)).all(), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: {e:.3e} > {tol:g}"
+
+
+def check_bf16(name, x, ref, tol=TOL_BF16):
+    """bf16 outputs: every element within half a bf16 ulp of its reference
+    value (the rounding of the output itself) plus tol * RMS(ref)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    excess = np.abs(x - ref) - 2.0 ** -8 * np.abs(ref)
+    e = float(np.max(excess) / rms)
+    say(f"  {name}: literal max|err|/rms = {rel_err(x, ref):.3e}; beyond half-ulp = {e:.3e} "
+        f"(tol {tol:g})")
+    assert np.isfinite(x).all(), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: {e:.3e} > {tol:g}"
+
+
+def check_out(name, x, ref, io):
+    if io == "bf16":
+        check_bf16(name, x, ref)
+    else:
+        check_f32(name, x, ref)

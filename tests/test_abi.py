@@ -1,0 +1,94 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every call include/gdn.h declares, sizes pools as documented and rejects bad
+arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_deltanet_state_layer_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libgdn.so is not built (run __graft_entry__.build())")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_calls():
+    names = declared_functions()
+    for want in ("gdn_pool_create", "gdn_slot_reset", "gdn_decode_step", "gdn_prefill_chunked",
+                 "gdn_verify_step"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from gated_deltanet_state_layer_amd import binding
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(binding.EXPORTED)
+
+
+def test_pool_bytes_layout(lib):
+    from gated_deltanet_state_layer_amd import binding as B
+    d = B.make_desc(256, 1, 16, 32, 128, 128, 4, B.GDN_BF16)
+    sb, ab = B.pool_bytes(d)
+    assert sb == 256 * 32 * 128 * 128 * 4
+    win = 256 * 3 * (2 * 16 * 128 + 32 * 128) * 2
+    assert ab == (win + 255) // 256 * 256 + 256
+    d = B.make_desc(3, 2, 2, 2, 32, 32, 4, B.GDN_F32)
+    sb, ab = B.pool_bytes(d)
+    assert sb == 3 * 2 * 2 * 32 * 32 * 4
+    assert ab == (3 * 2 * 3 * 192 * 4 + 255) // 256 * 256 + 256
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_slots", 0, -1), ("h_v", 3, -1), ("d_k", 96, -2), ("d_v", 32, -2), ("conv_k", 0, -1), ("conv_k", 1, -2),
+    ("conv_k", 9, -2), ("io_dtype", 7, -1), ("flags", 8, -1), ("q_scale", -1.0, -1),
+])
+def test_bad_descriptor_is_rejected(lib, field, value, status):
+    from gated_deltanet_state_layer_amd import binding as B
+    d = B.make_desc(4, 1, 2, 4, 64, 64, 4)
+    setattr(d, field, value)
+    sb, ab = ctypes.c_size_t(7), ctypes.c_size_t(7)
+    assert lib.gdn_pool_bytes(ctypes.byref(d), ctypes.byref(sb), ctypes.byref(ab)) == status
+    assert sb.value == 7 and ab.value == 7
+
+
+def test_null_arguments_are_rejected_before_any_device_work(lib):
+    from gated_deltanet_state_layer_amd import binding as B
+    d = B.make_desc(4, 1, 2, 4, 64, 64, 4)
+    h = ctypes.c_void_p()
+    assert lib.gdn_pool_create(ctypes.byref(d), None, None, None, ctypes.byref(h)) == -1
+    assert lib.gdn_pool_create(None, None, None, None, ctypes.byref(h)) == -1
+    # Misaligned buffers are refused without a launch.
+    assert lib.gdn_pool_create(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(256), None,
+                               ctypes.byref(h)) == -1
+    nul = None
+    assert lib.gdn_slot_reset(nul, 1, nul, nul) == -1
+    assert lib.gdn_decode_step(nul, 0, 1, *([nul] * 9)) == -1
+    assert lib.gdn_verify_step(nul, 0, 1, nul, 2, *([nul] * 9)) == -1
+    assert lib.gdn_prefill_chunked(nul, 0, 1, nul, nul, 8, 64, *([nul] * 8), 0, nul) == -1
+    n = ctypes.c_size_t()
+    assert lib.gdn_prefill_workspace_bytes(nul, 1, 8, 64, ctypes.byref(n)) == -1
+    e = ctypes.c_int32()
+    assert lib.gdn_pool_error(nul, nul, ctypes.byref(e)) == -1
+    assert lib.gdn_pool_destroy(nul) == -1
+
+
+def test_status_strings(lib):
+    from gated_deltanet_state_layer_amd import binding as B
+    assert B.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert B.status_string(s) != "unknown status"
+    assert B.status_string(42) == "unknown status"
