@@ -28,15 +28,39 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kHeadThreads = 256;       // threads per value-head tile
+constexpr int kMaxHeadsPerBlock = 2;    // value heads streamed concurrently per workgroup
+constexpr bool kNontemporal = true;     // state is streamed once: bypass cache retention
 
-template <int D, typename T>
-__global__ __launch_bounds__(kThreads) void decode_verify_kernel(
-    PoolView P, int layer, const int32_t* __restrict__ slot_ids, int n_tok,
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The state tiles are streamed with buffer instructions: one descriptor per
+// tile (base in scalar registers), one 32-bit lane offset, and the per-pass
+// row offset in a scalar register, so a lane needs no per-row addresses.
+// Cache policy: non-temporal (each tile is read once and written once).
+constexpr int kStatePolicy = kNontemporal ? 2 : 0;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(float* tile, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(tile, 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ f32x4 ld_state(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStatePolicy);
+}
+__device__ __forceinline__ void st_state(__amdgpu_buffer_rsrc_t r, int voff, int soff, f32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, kStatePolicy);
+}
+
+// NTOK > 0: token count fixed at compile time (decode: 1); 0: runtime (verify).
+template <int D, typename T, int NTOK>
+__global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verify_kernel(
+    PoolView P, int layer, const int32_t* __restrict__ slot_ids, int n_tok_rt,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ conv_w,
     const int32_t* __restrict__ accept_len, T* __restrict__ out) {
     extern __shared__ float smem[];
+    const int n_tok = NTOK > 0 ? NTOK : n_tok_rt;
+    const int nthr = blockDim.x;
     const int tid = threadIdx.x;
     const int g = blockIdx.x;   // q/k head group
     const int i = blockIdx.y;   // entry
@@ -47,11 +71,44 @@ __global__ __launch_bounds__(kThreads) void decode_verify_kernel(
         return;
     }
     const int G = P.h_v / P.h_k;
+    const int HB = nthr / kHeadThreads;   // heads per round
     const int K = P.conv_k;
     const int C = P.c_conv;
     const int nch = (2 + G) * D;  // channels owned by this group
     int commit = n_tok;
     if (accept_len) commit = min(max(accept_len[i], 0), n_tok);
+
+    // ---- state tile mapping: each row split over LPR lanes, 8 columns per
+    // lane (two 16-byte segments, D/2 apart); RPP rows per pass.
+    constexpr int LPR = D / 8;
+    constexpr int RPP = kHeadThreads / LPR;
+    constexpr int NP = (D + RPP - 1) / RPP;
+    const int sub = tid / kHeadThreads;
+    const int ht = tid % kHeadThreads;
+    const int lr = ht % LPR;
+    const int row0 = ht / LPR;
+    const int c0 = 4 * lr, c1 = D / 2 + 4 * lr;
+    const int voff = (row0 * D + c0) * (int)sizeof(float);   // byte offset of pass 0, segment 0
+    constexpr int kSeg1 = D / 2 * (int)sizeof(float);         // segment 1, immediate offset
+    constexpr int kPass = RPP * D * (int)sizeof(float);       // bytes between passes
+    constexpr int kTileBytes = D * D * (int)sizeof(float);
+    float* slot_state = P.state + ((int64_t)slot * P.n_layers + layer) * (int64_t)P.h_v * D * D;
+
+    float s[NP][8];
+    // Rows past D (only when D < RPP) read as zero through the descriptor's
+    // range check and are never stored.
+    auto load_tile = [&](__amdgpu_buffer_rsrc_t rs) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const f32x4 x0 = ld_state(rs, voff, p * kPass);
+            const f32x4 x1 = ld_state(rs, voff + kSeg1, p * kPass);
+            s[p][0] = x0.x; s[p][1] = x0.y; s[p][2] = x0.z; s[p][3] = x0.w;
+            s[p][4] = x1.x; s[p][5] = x1.y; s[p][6] = x1.z; s[p][7] = x1.w;
+        }
+    };
+    // Issue the first round's state loads before the conv front end so the
+    // HBM stream overlaps it.
+    if (sub < G) load_tile(tile_rsrc(slot_state + (int64_t)(g * G + sub) * D * D, kTileBytes));
 
     // LDS: line [K-1+n_tok][nch] raw inputs (window rows, then tokens),
     //      act  [n_tok][nch]     conv+SiLU outputs,
@@ -64,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void decode_verify_kernel(
     // ---- front end: depthwise causal conv + SiLU over the group's channels.
     T* win = reinterpret_cast<T*>(P.window) +
              ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
-    for (int c = tid; c < nch; c += kThreads) {
+    for (int c = tid; c < nch; c += nthr) {
         int gc;             // global channel
         const T* src;       // token 0 of this channel
         int64_t tstride;    // element stride between tokens
@@ -99,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void decode_verify_kernel(
     // ---- q/k normalisation factors and k.q per token (one wave per token).
     {
         const int wave = tid >> 6, lane = tid & 63;
-        for (int t = wave; t < n_tok; t += kThreads / 64) {
+        for (int t = wave; t < n_tok; t += nthr / 64) {
             float sq = 0.f, sk = 0.f, sqk = 0.f;
             for (int c = lane; c < D; c += 64) {
                 const float xq = act[t * nch + c], xk = act[t * nch + D + c];
@@ -121,31 +178,13 @@ __global__ __launch_bounds__(kThreads) void decode_verify_kernel(
     }
     __syncthreads();
 
-    // ---- state tiles: rows split over LPR lanes, 8 columns per lane.
-    constexpr int LPR = D / 8;              // lanes per row
-    constexpr int RPP = kThreads / LPR;     // rows per pass
-    constexpr int NP = (D + RPP - 1) / RPP; // passes per tile
-    const int lr = tid % LPR;
-    const int row0 = tid / LPR;
-    const int c0 = 4 * lr, c1 = D / 2 + 4 * lr;
-
-    for (int hl = 0; hl < G; ++hl) {
+    // ---- state tiles, HB value heads at a time.
+    for (int r = 0;; ++r) {
+        const int hl = r * HB + sub;
+        if (hl >= G) break;
         const int hv = g * G + hl;
-        float* tile = P.state + (((int64_t)slot * P.n_layers + layer) * P.h_v + hv) * (int64_t)D * D;
-        float s[NP][8];
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int row = row0 + p * RPP;
-            if (row < D) {
-                const float4 x0 = *reinterpret_cast<const float4*>(tile + row * D + c0);
-                const float4 x1 = *reinterpret_cast<const float4*>(tile + row * D + c1);
-                s[p][0] = x0.x; s[p][1] = x0.y; s[p][2] = x0.z; s[p][3] = x0.w;
-                s[p][4] = x1.x; s[p][5] = x1.y; s[p][6] = x1.z; s[p][7] = x1.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s[p][e] = 0.f;
-            }
-        }
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(slot_state + (int64_t)hv * D * D, kTileBytes);
+        if (r > 0) load_tile(rs);
         for (int t = 0; t < n_tok; ++t) {
             const float* y = act + t * nch;
             const float rq = nrm[t * 3 + 0], rk = nrm[t * 3 + 1], kq = nrm[t * 3 + 2];
@@ -177,21 +216,19 @@ __global__ __launch_bounds__(kThreads) void decode_verify_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s[p][e] = fmaf(at, s[p][e], delta * kc[e]);
                 if (lr == 0 && row < D) Io<T>::store(o_row, row, fmaf(at, pq, delta * kq));
-            }
-            if (t + 1 == commit) {
-#pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    const int row = row0 + p * RPP;
-                    if (row < D) {
-                        *reinterpret_cast<float4*>(tile + row * D + c0) =
-                            make_float4(s[p][0], s[p][1], s[p][2], s[p][3]);
-                        *reinterpret_cast<float4*>(tile + row * D + c1) =
-                            make_float4(s[p][4], s[p][5], s[p][6], s[p][7]);
-                    }
+                if (t + 1 == commit && row < D) {
+                    st_state(rs, voff, p * kPass, f32x4{s[p][0], s[p][1], s[p][2], s[p][3]});
+                    st_state(rs, voff + kSeg1, p * kPass, f32x4{s[p][4], s[p][5], s[p][6], s[p][7]});
                 }
             }
         }
     }
+}
+
+size_t lds_bytes(const PoolView& P, int n_tok) {
+    const int G = P.h_v / P.h_k;
+    return (size_t)(P.conv_k - 1 + 2 * n_tok) * (2 + G) * P.d * sizeof(float) +
+           (size_t)n_tok * 3 * sizeof(float);
 }
 
 template <int D, typename T>
@@ -201,22 +238,26 @@ hipError_t launch_dv(const gdn_pool* pool, int32_t layer, int32_t n, const int32
                      hipStream_t stream) {
     const PoolView& P = pool->view;
     const int G = P.h_v / P.h_k;
-    const size_t lds = (size_t)(P.conv_k - 1 + 2 * n_tok) * (2 + G) * D * sizeof(float) +
-                       (size_t)n_tok * 3 * sizeof(float);
+    const int threads = kHeadThreads * (G < kMaxHeadsPerBlock ? G : kMaxHeadsPerBlock);
+    const size_t lds = lds_bytes(P, n_tok);
     dim3 grid(P.h_k, n);
-    hipLaunchKernelGGL((decode_verify_kernel<D, T>), grid, dim3(kThreads), lds, stream, P, layer,
-                       slot_ids, n_tok, static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), a, b, conv_w, accept_len, static_cast<T*>(out));
+    const T* qq = static_cast<const T*>(q);
+    const T* kk = static_cast<const T*>(k);
+    const T* vv = static_cast<const T*>(v);
+    T* oo = static_cast<T*>(out);
+    if (n_tok == 1)
+        hipLaunchKernelGGL((decode_verify_kernel<D, T, 1>), grid, dim3(threads), lds, stream, P,
+                           layer, slot_ids, 1, qq, kk, vv, a, b, conv_w, accept_len, oo);
+    else
+        hipLaunchKernelGGL((decode_verify_kernel<D, T, 0>), grid, dim3(threads), lds, stream, P,
+                           layer, slot_ids, n_tok, qq, kk, vv, a, b, conv_w, accept_len, oo);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t decode_verify_lds_bytes(const gdn_pool* pool, int32_t n_tok) {
-    const PoolView& P = pool->view;
-    const int G = P.h_v / P.h_k;
-    return (size_t)(P.conv_k - 1 + 2 * n_tok) * (2 + G) * P.d * sizeof(float) +
-           (size_t)n_tok * 3 * sizeof(float);
+    return lds_bytes(pool->view, n_tok);
 }
 
 hipError_t launch_decode_verify(const gdn_pool* pool, int32_t layer, int32_t n,

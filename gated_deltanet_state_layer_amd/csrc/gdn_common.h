@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/gdn.h"
+#include "gdn.h"
 
 namespace gdn {
 
