@@ -101,3 +101,22 @@ def check_out(name, x, ref, io):
         check_bf16(name, x, ref)
     else:
         check_f32(name, x, ref)
+
+
+def group_slice(s: syn.Shapes, g: int):
+    """Channel indices and head ranges of q/k head group g (its q head, k head
+    and the value heads that share them): the sub-layer the oracle can run on
+    its own, since groups do not interact."""
+    D, G = s.d_k, s.group
+    ch = np.concatenate([np.arange(g * D, (g + 1) * D),
+                         s.h_k * D + np.arange(g * D, (g + 1) * D),
+                         2 * s.h_k * D + np.arange(g * G * D, (g + 1) * G * D)])
+    sub = syn.Shapes(1, G, s.d_k, s.d_v, s.conv_k)
+    return ch, slice(g * G, (g + 1) * G), sub
+
+
+def slice_tokens(tok, s, g):
+    G = s.group
+    return {"q": tok["q"][..., g:g + 1, :], "k": tok["k"][..., g:g + 1, :],
+            "v": tok["v"][..., g * G:(g + 1) * G, :], "a": tok["a"][..., g * G:(g + 1) * G],
+            "b": tok["b"][..., g * G:(g + 1) * G]}

@@ -1,0 +1,265 @@
+"""GPU parity: chunked prefill through the C ABI against the fp64 token-by-
+token oracle, plus the chunk/scheduler-split invariants and the bookkeeping
+guarantees (untouched slots, windows, zero-length and padding sequences,
+malformed cu_seqlens)."""
+import numpy as np
+import pytest
+
+import gdn_synth as syn
+from oracle import gdn_oracle as O
+from gpu_util import (check_f32, check_out, dev, group_slice, host, load_slots, make_pool,
+                      oracle_pool, say, scramble_pool, slice_tokens, tokens_to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_deltanet_state_layer_amd import binding
+    binding.load_library()
+
+
+def run_prefill(pool, layer, cu_np, ids_np, tok, w, chunk, io):
+    s = pool.desc
+    T = int(cu_np[-1])
+    td = tokens_to_dev(tok, io)
+    out = torch.full((T, s.h_v, s.d_v), float("nan"), dtype=pool.io_torch, device="cuda")
+    nbytes = pool.prefill_workspace_bytes(len(ids_np), T, chunk)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    pool.prefill(layer, dev(cu_np, torch.int32), dev(ids_np, torch.int32), T, chunk, td["q"],
+                 td["k"], td["v"], td["a"], td["b"], w, out, ws)
+    return out
+
+
+def test_tiny_layer_prefill_then_decode():
+    """64-token prefill (chunk 16) then 16 decode steps on the tiny fp32 layer."""
+    case = syn.tiny_layer_case()
+    s = case["shapes"]
+    say("tiny layer: prefill 64 (chunk 16) + 16 decode")
+    pool = make_pool(s, 3, "f32")
+    w = dev(case["conv_w"])
+    pre, dec = case["prefill"], case["decode"]
+    out = run_prefill(pool, 0, np.array([0, 64], np.int32), np.array([1], np.int32), pre, w, 16, "f32")
+    op = O.OraclePool(1, 1, s)
+    ref = op.prefill(0, [0, 64], [0], pre["q"], pre["k"], pre["v"], pre["a"], pre["b"], case["conv_w"])
+    check_f32("prefill outputs", host(out), ref)
+    check_f32("state after prefill", host(pool.state[1]), op.S[0])
+    assert np.array_equal(host(pool.window[1]), op.X[0])
+    ids = dev(np.array([1], np.int32), torch.int32)
+    outs, refs = [], []
+    for t in range(16):
+        tt = {n: dec[n][t:t + 1] for n in dec}
+        td = tokens_to_dev(tt, "f32")
+        o = torch.empty((1, s.h_v, s.d_v), device="cuda")
+        pool.decode(0, ids, td["q"], td["k"], td["v"], td["a"], td["b"], w, o)
+        outs.append(host(o))
+        refs.append(op.decode(0, [0], tt["q"], tt["k"], tt["v"], tt["a"], tt["b"], case["conv_w"]))
+    check_f32("decode outputs", np.array(outs), np.array(refs))
+    check_f32("final state", host(pool.state[1]), op.S[0])
+    assert not host(pool.state[[0, 2]]).any()
+
+
+def _oracle_groups(s, groups, tok, w, cu, ids_order, contents=None, form="rank1"):
+    """Run the oracle on q/k head groups `groups` only; returns per group
+    (outputs [T, G, d], oracle pool)."""
+    res = {}
+    for g in groups:
+        ch, hs, sub = group_slice(s, g)
+        sub_contents = None
+        if contents is not None:
+            sub_contents = {sl: (st[:, hs], wn[..., ch]) for sl, (st, wn) in contents.items()}
+        op = oracle_pool(sub, sub_contents, ids_order, form=form)
+        tk = slice_tokens(tok, s, g)
+        out = op.prefill(0, cu, np.arange(len(ids_order)), tk["q"], tk["k"], tk["v"], tk["a"],
+                         tk["b"], w[ch])
+        res[g] = (out, op, hs, ch)
+    return res
+
+
+def _check_groups(pool, res, out, ids_np, io, cu=None):
+    idx = torch.from_numpy(ids_np.astype(np.int64)).cuda()
+    for g, (ref, op, hs, ch) in res.items():
+        o = host(out[:, hs])
+        if cu is not None:   # skip rows of padding sequences
+            keep = np.zeros(o.shape[0], bool)
+            for j in range(len(cu) - 1):
+                if ids_np[j] >= 0:
+                    keep[cu[j]:cu[j + 1]] = True
+            o, ref = o[keep], ref[keep]
+        check_out(f"group {g} outputs", o, ref, io)
+        check_f32(f"group {g} final states", host(pool.state[idx][:, :, hs]), op.S)
+        assert np.array_equal(host(pool.window[idx][..., ch]), op.X), f"group {g} windows"
+
+
+def test_prefill_8192_tokens_sampled_groups():
+    """One 8192-token sequence, chunk 64, Qwen3-Next shapes (the benchmark's
+    launch), checked on q/k head groups 0 and 11 against the oracle."""
+    case = syn.prefill_case()
+    s, io, tok = case["shapes"], case["io"], case["tokens"]
+    T = tok["q"].shape[0]
+    say(f"prefill T={T} chunk 64")
+    pool = make_pool(s, 4, io)
+    scramble_pool(pool, 21)
+    pool.reset(dev(np.array([2], np.int32), torch.int32))
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    out = run_prefill(pool, 0, np.array([0, T], np.int32), np.array([2], np.int32), tok,
+                      dev(case["conv_w"]), 64, io)
+    torch.cuda.synchronize()
+    assert pool.error() == 0
+    res = _oracle_groups(s, [0, 11], tok, case["conv_w"], [0, T], np.array([2]))
+    _check_groups(pool, res, out, np.array([2], np.int32), io)
+    keep = [0, 1, 3]
+    assert torch.equal(pool.state[keep], st0[keep]) and torch.equal(pool.window[keep], wn0[keep])
+    assert torch.isfinite(out.float()).all()
+
+
+def test_prefill_scheduler_split_matches_unsplit():
+    """The same 8192 tokens as 16 calls of 512 tokens carrying state and
+    window match the single call (within tolerance) and the oracle."""
+    case = syn.prefill_case()
+    s, io, tok = case["shapes"], case["io"], case["tokens"]
+    T = tok["q"].shape[0]
+    say("prefill split 16 x 512")
+    w = dev(case["conv_w"])
+    p1 = make_pool(s, 2, io)
+    o1 = run_prefill(p1, 0, np.array([0, T], np.int32), np.array([1], np.int32), tok, w, 64, io)
+    p2 = make_pool(s, 2, io)
+    parts = []
+    for c0 in range(0, T, 512):
+        sl = {n: tok[n][c0:c0 + 512] for n in tok}
+        parts.append(run_prefill(p2, 0, np.array([0, 512], np.int32), np.array([1], np.int32), sl,
+                                 w, 64, io))
+    o2 = torch.cat(parts)
+    torch.cuda.synchronize()
+    check_out("split vs unsplit outputs", host(o2), host(o1), io)
+    check_f32("split vs unsplit state", host(p2.state[1]), host(p1.state[1]))
+    assert torch.equal(p2.window[1], p1.window[1])
+    res = _oracle_groups(s, [5], tok, case["conv_w"], [0, T], np.array([1]))
+    _check_groups(p2, res, o2, np.array([1], np.int32), io)
+
+
+def test_varlen_batched_prefill_into_slots():
+    """16 packed sequences of 128..4096 tokens; 12 into reset slots, 4
+    continuing from pre-filled states and windows."""
+    case = syn.varlen_case()
+    s, io, tok = case["shapes"], case["io"], case["tokens"]
+    cu, ids_np, cont = case["cu_seqlens"], case["slot_ids"], case["continuing"]
+    say(f"varlen: {len(ids_np)} seqs, {int(cu[-1])} tokens")
+    pool = make_pool(s, case["n_slots"], io)
+    scramble_pool(pool, 31)
+    contents = syn.draw_pool_contents(case["pool_seed"], ids_np[cont], s, io)
+    load_slots(pool, contents)
+    fresh = ids_np[~cont]
+    pool.reset(dev(fresh, torch.int32))
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    out = run_prefill(pool, 0, cu, ids_np, tok, dev(case["conv_w"]), 64, io)
+    torch.cuda.synchronize()
+    assert pool.error() == 0
+    res = _oracle_groups(s, [3], tok, case["conv_w"], cu, ids_np,
+                         contents={int(k): v for k, v in contents.items()})
+    _check_groups(pool, res, out, ids_np, io)
+    mask = torch.ones(case["n_slots"], dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(ids_np.astype(np.int64)).cuda()] = False
+    assert torch.equal(pool.state[mask], st0[mask]) and torch.equal(pool.window[mask], wn0[mask])
+
+
+@pytest.mark.parametrize("h_k,h_v,d,chunk,io", [
+    (2, 2, 32, 16, "f32"), (1, 4, 64, 32, "bf16"), (2, 4, 128, 64, "bf16"), (1, 2, 128, 32, "f32"),
+    (2, 2, 64, 64, "f32")])
+def test_ragged_edges_vs_oracle(h_k, h_v, d, chunk, io):
+    """Ragged chunk tails, sequences shorter than the conv window (lengths
+    1, 2), a zero-length sequence, a padding entry, continuing slots, on the
+    full layer (every head) against the oracle."""
+    s = syn.Shapes(h_k, h_v, d, d, 4)
+    say(f"ragged edges: {s} chunk={chunk} io={io}")
+    rng = np.random.default_rng(d + chunk + h_v)
+    lens = np.array([1, chunk + 3, 0, 2, 3 * chunk - 1, 5, chunk])
+    ids_np = np.array([4, 0, 2, 7, -1, 3, 6], np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    w_np = syn.draw_conv_weights(rng, s)
+    tok = syn.draw_tokens(rng, s, (T,), io)
+    n_slots = 8
+    pool = make_pool(s, n_slots, io)
+    contents = syn.draw_pool_contents(3, [0, 3, 7, 2], s, io)
+    load_slots(pool, contents)
+    pool.reset(dev(np.array([4, 6], np.int32), torch.int32))
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    out = run_prefill(pool, 0, cu, ids_np, tok, dev(w_np), chunk, io)
+    torch.cuda.synchronize()
+    assert pool.error() == 0
+    valid = ids_np >= 0
+    op = oracle_pool(s, contents, np.where(valid, ids_np, 0), form="rank1")
+    op.S[~valid] = 0.0
+    ref = op.prefill(0, cu, np.where(valid, np.arange(len(ids_np)), -1), tok["q"], tok["k"],
+                     tok["v"], tok["a"], tok["b"], w_np)
+    rows = np.concatenate([np.arange(cu[j], cu[j + 1]) for j in range(len(lens)) if valid[j]])
+    check_out("outputs", host(out)[rows], ref[rows], io)
+    assert torch.isnan(out[cu[4]:cu[5]].float()).all(), "padding sequence rows were written"
+    for jj, sl in enumerate(ids_np):
+        if sl < 0:
+            continue
+        check_f32(f"state of slot {sl}", host(pool.state[int(sl)]), op.S[jj])
+        assert np.array_equal(host(pool.window[int(sl)]), op.X[jj]), f"window of slot {sl}"
+    for sl in (1, 5):
+        assert torch.equal(pool.state[sl], st0[sl]) and torch.equal(pool.window[sl], wn0[sl])
+    # zero-length sequence into slot 2 left it bitwise unchanged
+    assert torch.equal(pool.state[2], st0[2]) and torch.equal(pool.window[2], wn0[2])
+
+
+def test_malformed_cu_seqlens_is_flagged_and_touches_nothing():
+    s, io = syn.Shapes(2, 4, 64, 64, 4), "bf16"
+    say("malformed cu_seqlens")
+    rng = np.random.default_rng(12)
+    w = dev(syn.draw_conv_weights(rng, s))
+    pool = make_pool(s, 4, io)
+    scramble_pool(pool, 13)
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    tok = syn.draw_tokens(rng, s, (40,), io)
+    for cu in ([0, 30, 20, 40], [0, 10, 41, 40], [1, 20, 30, 40]):
+        out = run_prefill(pool, 0, np.array(cu, np.int32), np.array([0, 1, 2], np.int32), tok, w,
+                          32, io)
+        assert pool.error() == 2
+        assert torch.isnan(out.float()).all()
+    assert torch.equal(pool.state, st0) and torch.equal(pool.window, wn0)
+
+
+def test_prefill_then_verify_and_decode_continue_the_sequence():
+    """Prefill a prompt, then decode and verify steps continue from the
+    prefilled state and window (Qwen3-Next shapes, one group checked)."""
+    s, io = syn.QWEN3_NEXT, "bf16"
+    say("prefill -> decode -> verify continuity")
+    rng = np.random.default_rng(50)
+    w_np = syn.draw_conv_weights(rng, s)
+    w = dev(w_np)
+    T = 300
+    tok = syn.draw_tokens(rng, s, (T,), io)
+    pool = make_pool(s, 3, io)
+    ids = np.array([2], np.int32)
+    out = run_prefill(pool, 0, np.array([0, T], np.int32), ids, tok, w, 64, io)
+    g = 7
+    ch, hs, sub = group_slice(s, g)
+    op = O.OraclePool(1, 1, sub, form="rank1")
+    tk = slice_tokens(tok, s, g)
+    ref = op.prefill(0, [0, T], [0], tk["q"], tk["k"], tk["v"], tk["a"], tk["b"], w_np[ch])
+    check_out("prefill outputs", host(out[:, hs]), ref, io)
+    d1 = syn.draw_tokens(rng, s, (1,), io)
+    o = torch.empty((1, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    td = tokens_to_dev(d1, io)
+    pool.decode(0, dev(ids, torch.int32), td["q"], td["k"], td["v"], td["a"], td["b"], w, o)
+    t1 = slice_tokens(d1, s, g)
+    r1 = op.decode(0, [0], t1["q"], t1["k"], t1["v"], t1["a"], t1["b"], w_np[ch])
+    check_out("decode after prefill", host(o[:, hs]), r1, io)
+    v4 = syn.draw_tokens(rng, s, (1, 4), io)
+    ov = torch.empty((1, 4, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    tv = tokens_to_dev(v4, io)
+    pool.verify(0, dev(ids, torch.int32), 4, tv["q"], tv["k"], tv["v"], tv["a"], tv["b"], w,
+                dev(np.array([3], np.int32), torch.int32), ov)
+    t4 = slice_tokens(v4, s, g)
+    r4 = op.verify(0, [0], 4, t4["q"], t4["k"], t4["v"], t4["a"], t4["b"], w_np[ch], np.array([3]))
+    check_out("verify after prefill", host(ov[:, :, hs]), r4, io)
+    check_f32("state", host(pool.state[2][:, hs]), op.S[0])
+    assert np.array_equal(host(pool.window[2][..., ch]), op.X[0])
