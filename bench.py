@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-verify", action="store_true")
-    p.add_argument("--only", choices=["decode", "verify", "prefill"], default=None,
+    p.add_argument("--only", choices=["decode", "verify", "prefill", "copy"], default=None,
                    help="run one workload only (for profiling)")
     return p.parse_args()
 
@@ -158,55 +158,99 @@ def bench_verify(args, torch, G, syn):
 
 
 def prefill_flops_per_token(s, C):
-    """Algorithmic flops per token of the chunked form (triangular-aware)."""
-    dk, dv, G = s.d_k, s.d_v, s.group
-    per_khead = (C + 1) * dk + (C + 1) * dk          # K K^T and Q K^T lower triangles, per token
-    per_vhead = (C * C / 3.0) / C * 2 / 2            # (I+A)^-1 ~ C^3/3 per chunk -> per token
-    per_vhead += 2 * C * dk + 2 * C * dv             # W = T diag K-side, U_v = T diag(b) V
-    per_vhead += 2 * dk * dv * 3                     # W S0^T, Q S0^T, U^T K (per token)
-    per_vhead += (C + 1) * dv                        # (QK^T * decay) U, lower triangle
-    return s.h_k * per_khead + s.h_v * per_vhead
+    """Algorithmic flops per token of the chunked form (2 per multiply-add,
+    triangular products counted as triangles), per chunk divided by C:
+      per q/k head: K K^T and Q K^T lower triangles      2 * C * d_k
+      per value head: (I+A)^-1 by substitution            C^2 / 3
+                      K S0^T, Q S0^T, U^T K               3 * 2 * d_k * d_v
+                      T' R and P U (lower triangles)      2 * C * d_v
+    """
+    dk, dv = s.d_k, s.d_v
+    per_k = 2 * C * dk
+    per_v = C * C / 3.0 + 6 * dk * dv + 2 * C * dv
+    return s.h_k * per_k + s.h_v * per_v
+
+
+def _prefill_inputs(torch, tok):
+    d = {n: torch.from_numpy(tok[n]).cuda() for n in "ab"}
+    d.update({n: torch.from_numpy(tok[n]).bfloat16().cuda() for n in "qkv"})
+    return d
+
+
+def _time_prefill(args, torch, pool, cu_list, ids, d, w, out, C, reps):
+    """Time one prefill pass made of the given calls (each (t0, t1, cu) over
+    the packed token range [t0, t1)).  The slots keep their state between
+    repetitions: the kernels do the same work for zero and non-zero states."""
+    calls = []
+    for (t0, t1, cu) in cu_list:
+        wsb = pool.prefill_workspace_bytes(int(ids.numel()), t1 - t0, C)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+        cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        calls.append((t0, t1, cu_d, ws))
+
+    def step(i):
+        for (t0, t1, cu_d, ws) in calls:
+            pool.prefill(0, cu_d, ids, t1 - t0, C, d["q"][t0:t1], d["k"][t0:t1], d["v"][t0:t1],
+                         d["a"][t0:t1], d["b"][t0:t1], w, out[t0:t1], ws)
+
+    return time_launches(step, reps, 3, torch)
 
 
 def bench_prefill(args, torch, G, syn):
     s = syn.QWEN3_NEXT
-    case = syn.prefill_case()
-    T, C = 8192, 64
-    tok = case["tokens"]
-    pool = G.Pool(G.make_desc(4, 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16))
-    d = {n: torch.from_numpy(tok[n]).cuda() for n in "ab"}
-    d.update({n: torch.from_numpy(tok[n]).bfloat16().cuda() for n in "qkv"})
-    w = torch.from_numpy(case["conv_w"]).cuda()
-    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
-    out = torch.empty((T, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
-    try:
-        wsb = pool.prefill_workspace_bytes(1, T, C)
-    except G.GdnError:
-        return None
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
-    slots = [torch.tensor([j], dtype=torch.int32, device="cuda") for j in range(4)]
-
-    def step(i):
-        sl = slots[i % 4]
-        pool.reset(sl)
-        pool.prefill(0, cu, sl, T, C, d["q"], d["k"], d["v"], d["a"], d["b"], w, out, ws)
-
-    try:
-        step(0)
-    except G.GdnError as e:
-        if e.status == -2:
-            return None
-        raise
-    t = time_launches(step, max(10, args.steps // 10), 3, torch)
-    t_reset = time_launches(lambda i: pool.reset(slots[i % 4]), 20, 3, torch)
-    t -= t_reset
+    C = 64
+    res = {}
     io = 2
-    b = T * ((2 * s.h_k * s.d_k + s.h_v * s.d_v) * io + 2 * s.h_v * 4 + s.h_v * s.d_v * io) \
-        + 2 * s.h_v * s.d_v * s.d_k * 4
-    fl = prefill_flops_per_token(s, C) * T
-    return {"sec": t, "T": T, "chunk": C, "tok_s": T / t, "bytes": b, "gbps": b / t / 1e9,
-            "alg_tflops": fl / t / 1e12, "mfma_frac_alg": fl / t / 1e12 / BF16_PEAK_TFLOPS,
-            "workspace_bytes": wsb}
+    tok_bytes = (2 * s.h_k * s.d_k + s.h_v * s.d_v) * io + 2 * s.h_v * 4 + s.h_v * s.d_v * io
+    state_rw = 2 * s.h_v * s.d_v * s.d_k * 4
+    fl_tok = prefill_flops_per_token(s, C)
+    # One 8192-token sequence: one call, and 16 scheduler chunks of 512.
+    case = syn.prefill_case()
+    T = case["tokens"]["q"].shape[0]
+    pool = G.Pool(G.make_desc(4, 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16))
+    d = _prefill_inputs(torch, case["tokens"])
+    w = torch.from_numpy(case["conv_w"]).cuda()
+    out = torch.empty((T, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    ids = torch.tensor([1], dtype=torch.int32, device="cuda")
+    reps = max(10, args.steps // 10)
+    t1 = _time_prefill(args, torch, pool, [(0, T, [0, T])], ids, d, w, out, C, reps)
+    t16 = _time_prefill(args, torch, pool, [(c0, c0 + 512, [0, 512]) for c0 in range(0, T, 512)],
+                        ids, d, w, out, C, reps)
+    b = T * tok_bytes + state_rw
+    res["single"] = {"workload": "one 8192-token sequence, chunk 64", "us": t1 * 1e6,
+                     "tok_s": T / t1, "GBps": b / t1 / 1e9, "alg_TFLOPs": fl_tok * T / t1 / 1e12,
+                     "mfma_frac_alg": fl_tok * T / t1 / 1e12 / BF16_PEAK_TFLOPS}
+    res["split512"] = {"workload": "the same sequence as 16 calls of 512 tokens", "us": t16 * 1e6,
+                       "tok_s": T / t16}
+    assert pool.error() == 0
+    del pool, d, out
+    # Varlen: 16 sequences, lengths uniform in [128, 4096].
+    case = syn.varlen_case()
+    cu = case["cu_seqlens"]
+    Tv = int(cu[-1])
+    pool = G.Pool(G.make_desc(case["n_slots"], 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16))
+    d = _prefill_inputs(torch, case["tokens"])
+    w = torch.from_numpy(case["conv_w"]).cuda()
+    out = torch.empty((Tv, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    ids = torch.from_numpy(case["slot_ids"]).cuda()
+    tv = _time_prefill(args, torch, pool, [(0, Tv, [int(x) for x in cu])], ids, d, w, out, C, reps)
+    bv = Tv * tok_bytes + len(cu) * state_rw
+    res["varlen"] = {"workload": f"16 packed sequences, {Tv} tokens (lengths U[128,4096])",
+                     "us": tv * 1e6, "tok_s": Tv / tv, "GBps": bv / tv / 1e9,
+                     "alg_TFLOPs": fl_tok * Tv / tv / 1e12,
+                     "mfma_frac_alg": fl_tok * Tv / tv / 1e12 / BF16_PEAK_TFLOPS}
+    assert pool.error() == 0
+    return res
+
+
+def bench_copy(args, torch):
+    """torch's plain copy kernel over 512 MiB: the achievable-bandwidth
+    reference and the byte count used to scale the HBM counters."""
+    n = 128 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    t = time_launches(lambda i: dst.copy_(src), max(20, args.steps // 10), 5, torch)
+    return {"bytes": 2 * n * 4, "us": t * 1e6, "GBps": 2 * n * 4 / t / 1e9}
 
 
 def cpu_baseline(syn):
@@ -255,6 +299,9 @@ def main():
     if args.only in (None, "prefill") and not args.no_prefill:
         res["prefill"] = bench_prefill(args, torch, G, syn)
         print("# prefill done", file=sys.stderr, flush=True)
+    if args.only in (None, "copy"):
+        res["copy"] = bench_copy(args, torch)
+        print("# copy done", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu and args.only is None:
         cpu = cpu_baseline(syn)
@@ -290,10 +337,9 @@ def main():
                           "accepted_tok_s": v["accepted_tok_s"], "GBps": v["gbps"],
                           "hbm_frac": v["gbps"] / HBM_PEAK_GBPS}
     if res.get("prefill"):
-        p = res["prefill"]
-        line["prefill"] = {"workload": "one 8192-token sequence, chunk 64, fresh slot",
-                           "us": p["sec"] * 1e6, "tok_s": p["tok_s"], "GBps": p["gbps"],
-                           "alg_TFLOPs": p["alg_tflops"], "mfma_frac_alg": p["mfma_frac_alg"]}
+        line["prefill"] = res["prefill"]
+    if res.get("copy"):
+        line["copy_reference"] = res["copy"]
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

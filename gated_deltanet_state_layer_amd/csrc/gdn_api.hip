@@ -218,6 +218,8 @@ gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
     if (n_seq == 0) return GDN_OK;
     if (!cu_seqlens || !slot_ids || !conv_w) return GDN_ERR_INVALID_ARG;
     if (total_tokens > 0 && (!q || !k || !v || !a || !b || !out)) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)))
+        return GDN_ERR_INVALID_ARG;
     const size_t need = prefill_workspace_bytes(pool, n_seq, total_tokens, chunk);
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, kAlign)) return GDN_ERR_INVALID_ARG;

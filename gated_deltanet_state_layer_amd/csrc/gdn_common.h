@@ -70,7 +70,7 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------ pool (device)
 

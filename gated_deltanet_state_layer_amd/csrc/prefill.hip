@@ -14,21 +14,23 @@
 //     S       = exp(g_last) S0 + U^T diag(exp(g_last - g)) K
 //
 // Three kernels, stream-ordered, no host synchronisation:
-//   prep   (1 workgroup)            chunk map from the device cu_seqlens;
+//   prep   (1 workgroup)             chunk map from the device cu_seqlens;
 //   factor (chunk x q/k head)        conv+SiLU, q/k normalisation, KK^T and QK^T
 //                                    on bf16 MFMA, T' and P per value head;
-//   scan   (row block x v head x seq) the serial chunk carry: X = [Q;K] S0^T,
-//                                    U, O and the state update on bf16 MFMA,
-//                                    the state block kept in registers.
-// Every MFMA operand that is not an exact bf16 value is split as hi + lo
-// bf16 and multiplied as hi*hi + hi*lo + lo*hi (fp32 accumulate), which keeps
-// the chunked result within fp32-recurrence accuracy.
+//   scan   (seq x v head x 16 rows)  the serial chunk carry on bf16 MFMA, the
+//                                    state block kept in registers.
+// Every MFMA operand that is not an exact bf16 value is split as hi + lo bf16
+// and multiplied as hi*hi + hi*lo + lo*hi (fp32 accumulate), which keeps the
+// chunked result within fp32-recurrence accuracy.  The factor kernel writes
+// every chunk operand of the scan already split and in MFMA fragment order,
+// so the scan's serial loop only splits what it produces itself.
 #include "gdn_common.h"
 
 namespace gdn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -37,12 +39,15 @@ constexpr float kLogDecayMin = -87.f;
 
 // ------------------------------------------------------------ MFMA helpers
 
-struct Split8 {
+// One lane's share of a 16x16x32 bf16 MFMA operand, split as hi + lo.
+// Lane l = 16 q + m of an A operand holds row m, k = 8q..8q+7; of a B operand
+// column m, k = 8q..8q+7; the fp32 result holds rows 4q..4q+3 of column m.
+struct Frag {
     bf16x8 hi, lo;
 };
 
-__device__ __forceinline__ Split8 split8(const float* x) {
-    Split8 r;
+__device__ __forceinline__ Frag split8(const float* x) {
+    Frag r;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const __bf16 h = (__bf16)x[j];
@@ -52,31 +57,69 @@ __device__ __forceinline__ Split8 split8(const float* x) {
     return r;
 }
 
-// acc += A * B for one 16x16x32 tile, operands split in hi/lo bf16.
-__device__ __forceinline__ f32x4 mma3(f32x4 acc, const Split8& a, const Split8& b) {
+// acc += A * B for one 16x16x32 tile.
+__device__ __forceinline__ f32x4 mma3(f32x4 acc, const Frag& a, const Frag& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
     return acc;
 }
 
-__device__ __forceinline__ void ld8(float* dst, const float* src) {
-    const float4 x0 = *reinterpret_cast<const float4*>(src);
-    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+// Fragment buffers: [fragment][hi | lo][64 lanes] of 16-byte vectors, 2 KiB
+// per fragment, so a wave reads or writes one half in one coalesced 1 KiB.
+constexpr int kFragVecs = 128;   // bf16x8 per fragment
+
+__device__ __forceinline__ void store_frag(bf16x8* base, int f, int lane, const Frag& x) {
+    base[f * kFragVecs + lane] = x.hi;
+    base[f * kFragVecs + 64 + lane] = x.lo;
+}
+__device__ __forceinline__ Frag load_frag(const bf16x8* base, int f, int lane) {
+    Frag x;
+    x.hi = base[f * kFragVecs + lane];
+    x.lo = base[f * kFragVecs + 64 + lane];
+    return x;
+}
+// Scatter four consecutive k values (hi and lo) into lane `dl`, elements
+// e0..e0+3, of B fragment f.
+__device__ __forceinline__ void store_frag4(bf16x8* base, int f, int dl, int e0, const float* x) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const __bf16 hh = (__bf16)x[i];
+        h[i] = hh;
+        l[i] = (__bf16)(x[i] - (float)hh);
+    }
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base + f * kFragVecs + dl) + e0) = h;
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base + f * kFragVecs + 64 + dl) + e0) = l;
+}
+
+__device__ __forceinline__ void ld4x2(float* dst, const float* lo, const float* hi) {
+    const float4 x0 = *reinterpret_cast<const float4*>(lo);
+    const float4 x1 = *reinterpret_cast<const float4*>(hi);
     dst[0] = x0.x; dst[1] = x0.y; dst[2] = x0.z; dst[3] = x0.w;
     dst[4] = x1.x; dst[5] = x1.y; dst[6] = x1.z; dst[7] = x1.w;
 }
 
+__device__ __forceinline__ void ld8(float* dst, const float* src) { ld4x2(dst, src, src + 4); }
+
 // --------------------------------------------------------------- workspace
+
+// Fragment counts per (chunk, head): CP tokens per chunk (padded), NT = CP/16
+// token tiles, NKS = D/32 k-steps over d_k, NKC = CP/32 k-steps over tokens.
+struct Geom {
+    int D, CP, NT, NKS, NKC;
+    int nqk() const { return 2 * NT * NKS; }       // Q^ and K^ rows (A of [Q;K] S0^T)
+    int nkt() const { return (D / 16) * NKC; }     // K^T (A of the state update)
+    int ntp() const { return 2 * NT * NKC; }       // T' and P
+};
 
 struct Ws {
     int32_t* hdr;        // [0]: number of chunks, or -1 if cu_seqlens is malformed
     int32_t* seq_coff;   // [n_seq+1] first global chunk of each sequence
     int32_t* chunk_seq;  // [max_chunks] sequence owning each chunk
-    float* qh;           // [max_chunks][h_k][CP][D] normalised, scaled q
-    float* kh;           // [max_chunks][h_k][CP][D] normalised k
-    float* tq;           // [max_chunks][h_v][CP][CP] T' = (I+A)^-1 diag(b)
-    float* pm;           // [max_chunks][h_v][CP][CP] P (lower triangle incl. diagonal)
+    bf16x8* qkf;         // [max_chunks][h_k][nqk fragments]
+    bf16x8* ktf;         // [max_chunks][h_k][nkt fragments]
+    bf16x8* tpf;         // [max_chunks][h_v][ntp fragments]
     float* gl;           // [max_chunks][h_v][CP] cumulative log-decay in the chunk
 };
 
@@ -88,10 +131,16 @@ int64_t max_chunks(int32_t n_seq, int64_t total, int32_t chunk) {
 
 int padded_chunk(int32_t chunk) { return chunk < 32 ? 32 : chunk; }
 
+Geom geom(int D, int chunk) {
+    const int CP = padded_chunk(chunk);
+    return Geom{D, CP, CP / 16, D / 32, CP / 32};
+}
+
 Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t chunk,
          size_t* bytes) {
     const int64_t mc = max_chunks(n_seq, total, chunk);
-    const int64_t CP = padded_chunk(chunk);
+    const Geom gm = geom(P.d, chunk);
+    const size_t fb = (size_t)kFragVecs * 16;  // bytes per fragment
     size_t off = 0;
     auto take = [&](size_t n) {
         const size_t o = off;
@@ -101,21 +150,19 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
     const size_t o_hdr = take(256);
     const size_t o_coff = take((size_t)(n_seq + 1) * 4);
     const size_t o_cseq = take((size_t)mc * 4);
-    const size_t o_q = take((size_t)mc * P.h_k * CP * P.d * 4);
-    const size_t o_k = take((size_t)mc * P.h_k * CP * P.d * 4);
-    const size_t o_t = take((size_t)mc * P.h_v * CP * CP * 4);
-    const size_t o_p = take((size_t)mc * P.h_v * CP * CP * 4);
-    const size_t o_g = take((size_t)mc * P.h_v * CP * 4);
+    const size_t o_qk = take((size_t)mc * P.h_k * gm.nqk() * fb);
+    const size_t o_kt = take((size_t)mc * P.h_k * gm.nkt() * fb);
+    const size_t o_tp = take((size_t)mc * P.h_v * gm.ntp() * fb);
+    const size_t o_g = take((size_t)mc * P.h_v * gm.CP * 4);
     *bytes = off;
     char* b = static_cast<char*>(base);
     Ws w;
     w.hdr = reinterpret_cast<int32_t*>(b + o_hdr);
     w.seq_coff = reinterpret_cast<int32_t*>(b + o_coff);
     w.chunk_seq = reinterpret_cast<int32_t*>(b + o_cseq);
-    w.qh = reinterpret_cast<float*>(b + o_q);
-    w.kh = reinterpret_cast<float*>(b + o_k);
-    w.tq = reinterpret_cast<float*>(b + o_t);
-    w.pm = reinterpret_cast<float*>(b + o_p);
+    w.qkf = reinterpret_cast<bf16x8*>(b + o_qk);
+    w.ktf = reinterpret_cast<bf16x8*>(b + o_kt);
+    w.tpf = reinterpret_cast<bf16x8*>(b + o_tp);
     w.gl = reinterpret_cast<float*>(b + o_g);
     return w;
 }
@@ -176,40 +223,63 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     }
 }
 
-// ------------------------------------------------------------- conv helper
+// ------------------------------------------------------------- raw loads
 
-// Raw input of channel `gc` at token position p of a sequence starting at
-// `s0`: from the input tensor for p >= s0, else from the slot's window
-// (window row conv_k-1 + (p - s0)).
-template <typename T>
-__device__ __forceinline__ float raw_at(const T* src, int64_t stride, const T* win, int C, int K,
-                                        int gc, int64_t p, int64_t s0) {
-    if (p >= s0) return Io<T>::load(src, p * stride);
-    return Io<T>::load(win, (int64_t)(K - 1 + (p - s0)) * C + gc);
-}
+// 16 bytes of raw activations (8 bf16 or 4 fp32) converted to fp32.
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> {
+    static constexpr int N = 8;
+    __device__ static __forceinline__ float at(const uint4& u, int i) {
+        const uint32_t w = (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
+        return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    __device__ static __forceinline__ void load(float* dst, const uint16_t* src) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int i = 0; i < N; ++i) dst[i] = at(u, i);
+    }
+};
+template <> struct Vec<float> {
+    static constexpr int N = 4;
+    __device__ static __forceinline__ float at(const uint4& u, int i) {
+        return __uint_as_float(i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w);
+    }
+    __device__ static __forceinline__ void load(float* dst, const float* src) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int i = 0; i < N; ++i) dst[i] = at(u, i);
+    }
+};
 
 // ------------------------------------------------------------------ factor
 
-// grid (max_chunks, h_k), 256 threads.  LDS: q^ and k^ [CP][D+4] fp32, then
-// reused for A [CP][CP+1] and T [CP][CP+1]; small per-token arrays.
+// grid (max_chunks, h_k), 256 threads.  Dynamic LDS: the chunk's raw q|k rows
+// (conv_k-1 rows of left context, then CP tokens), overwritten in place by
+// the conv+SiLU outputs and normalised; later reused for A, T and P.
 template <int D, int CP, typename T>
 __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ q,
     const T* __restrict__ k, const float* __restrict__ a, const float* __restrict__ b,
     const float* __restrict__ conv_w) {
-    constexpr int LD = D + 4;          // padded row (floats)
+    constexpr int LD = 2 * D + 4;      // row of the staged q|k lines (floats)
     constexpr int LT = CP + 1;
     constexpr int NT = CP / 16;        // token tiles
-    constexpr int NKD = D / 32;        // k-steps over d_k
+    constexpr int NKS = D / 32;        // k-steps over d_k
+    constexpr int NKC = CP / 32;       // k-steps over tokens
+    constexpr int NQK = 2 * NT * NKS, NKT = (D / 16) * NKC, NTP = 2 * NT * NKC;
+    constexpr int VN = Vec<T>::N;
     extern __shared__ __align__(16) float smem[];
-    float* xq = smem;                  // [CP][LD]
-    float* xk = xq + CP * LD;          // [CP][LD]
+    float* xr = smem;                  // [K-1+CP][LD]; row r <-> position t0-(K-1)+r
+    float* xq = xr;                    // after the conv: q of token t at xq[t*LD + c]
+    float* xk = xr + D;                //                 k of token t at xk[t*LD + c]
     float* sA = smem;                  // [CP][LT]  (after q^, k^ are consumed)
     float* sT = sA + CP * LT;          // [CP][LT]
+    float* sP = sT + CP * LT;          // [CP][LT]
     __shared__ float s_rq[CP], s_rk[CP], s_g[CP], s_b[CP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m16 = lane & 15, q4 = lane >> 4;
     const int ci = blockIdx.x, g = blockIdx.y;
     const int n_chunks = W.hdr[0];
     if (ci >= n_chunks) return;        // also when the workspace is invalid (-1)
@@ -224,46 +294,65 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     const int K = P.conv_k, C = P.c_conv, G = P.h_v / P.h_k;
     T* win = reinterpret_cast<T*>(P.window) + ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
 
-    // ---- conv + SiLU of the q and k channels of head g (one channel per thread).
+    // ---- stage the raw q|k rows with 16-byte loads: window rows before the
+    // sequence start, zeros past the chunk's valid tokens.
+    {
+        const int nrow = K - 1 + CP;
+        constexpr int vpr = 2 * D / VN;
+        for (int e = tid; e < nrow * vpr; e += kThreads) {
+            const int r = e / vpr, cv = (e % vpr) * VN;
+            const bool isk = cv >= D;
+            const int cc = isk ? cv - D : cv;
+            const int64_t p = t0 - (K - 1) + r;
+            float x[VN];
+            if (p >= t0 + L) {
+#pragma unroll
+                for (int i = 0; i < VN; ++i) x[i] = 0.f;
+            } else if (p >= s0) {
+                Vec<T>::load(x, (isk ? k : q) + (p * P.h_k + g) * D + cc);
+            } else {
+                Vec<T>::load(x, win + (int64_t)(K - 1 + (p - s0)) * C + (isk ? P.h_k * D : 0) + g * D + cc);
+            }
+#pragma unroll
+            for (int i = 0; i < VN; ++i) xr[r * LD + cv + i] = x[i];
+        }
+    }
+    __syncthreads();
+    // The sequence's first chunk owns the window of these channels: store the
+    // last conv_k-1 raw inputs of the sequence (old window rows come from LDS).
+    if (cpos == 0) {
+        for (int e = tid; e < (K - 1) * 2 * D; e += kThreads) {
+            const int m = e / (2 * D), c = e % (2 * D);
+            const bool isk = c >= D;
+            const int cc = isk ? c - D : c;
+            const int64_t p = s0 + len - (K - 1) + m;
+            const float x = p >= s0 ? Io<T>::load(isk ? k : q, (p * P.h_k + g) * D + cc)
+                                    : xr[(int)(K - 1 + (p - s0)) * LD + c];
+            Io<T>::store(win, (int64_t)m * C + (isk ? P.h_k * D : 0) + g * D + cc, x);
+        }
+        __syncthreads();
+    }
+    // ---- conv + SiLU in place, one channel per thread: y_t lands in row t,
+    // which no later token of the channel reads.
     for (int c = tid; c < 2 * D; c += kThreads) {
-        const bool isk = c >= D;
-        const int cc = isk ? c - D : c;
-        const int gc = (isk ? P.h_k * D : 0) + g * D + cc;
-        const T* src = (isk ? k : q) + (int64_t)g * D + cc;
-        const int64_t stride = (int64_t)P.h_k * D;
-        float w[kMaxConvK], prev[kMaxConvK - 1];
+        const int gc = (c >= D ? P.h_k * D + g * D + (c - D) : g * D + c);
+        float w[kMaxConvK], line[kMaxConvK - 1];
 #pragma unroll
         for (int m = 0; m < kMaxConvK; ++m) w[m] = m < K ? conv_w[(int64_t)gc * K + m] : 0.f;
 #pragma unroll
-        for (int m = 0; m < kMaxConvK - 1; ++m)
-            prev[m] = m < K - 1 ? raw_at(src, stride, win, C, K, gc, t0 - (K - 1) + m, s0) : 0.f;
-        float* dst = isk ? xk : xq;
+        for (int m = 0; m < kMaxConvK - 1; ++m) line[m] = m < K - 1 ? xr[m * LD + c] : 0.f;
+#pragma unroll 4
         for (int t = 0; t < CP; ++t) {
-            float y = 0.f;
-            if (t < L) {
-                const float x = Io<T>::load(src, (t0 + t) * stride);
-                float z = 0.f;
-#pragma unroll
-                for (int m = 0; m < kMaxConvK - 1; ++m)
-                    if (m < K - 1) z = fmaf(w[m], prev[m], z);
-                z = fmaf(w[K - 1], x, z);
-                y = silu(z);
-#pragma unroll
-                for (int m = 0; m < kMaxConvK - 1; ++m)
-                    prev[m] = (m == K - 2) ? x : (m < K - 2 ? prev[m + 1] : prev[m]);
-            }
-            dst[t * LD + cc] = y;
-        }
-        // The sequence's first chunk owns the window of these channels: after
-        // its own reads, store the last conv_k-1 raw inputs of the sequence.
-        if (cpos == 0) {
-            float nw[kMaxConvK - 1];
+            const float x = xr[(t + K - 1) * LD + c];
+            float z = 0.f;
 #pragma unroll
             for (int m = 0; m < kMaxConvK - 1; ++m)
-                nw[m] = m < K - 1 ? raw_at(src, stride, win, C, K, gc, s0 + len - (K - 1) + m, s0) : 0.f;
+                if (m < K - 1) z = fmaf(w[m], line[m], z);
+            z = fmaf(w[K - 1], x, z);
+            xr[t * LD + c] = t < L ? silu(z) : 0.f;
 #pragma unroll
             for (int m = 0; m < kMaxConvK - 1; ++m)
-                if (m < K - 1) Io<T>::store(win, (int64_t)m * C + gc, nw[m]);
+                line[m] = (m == K - 2) ? x : (m < K - 2 ? line[m + 1] : line[m]);
         }
     }
     __syncthreads();
@@ -284,28 +373,42 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         }
     }
     __syncthreads();
-    // Scale in place and store q^, k^ to the workspace.
-    {
-        float* gq = W.qh + ((int64_t)ci * P.h_k + g) * CP * D;
-        float* gk = W.kh + ((int64_t)ci * P.h_k + g) * CP * D;
-        for (int e = tid; e < CP * D / 4; e += kThreads) {
-            const int t = e / (D / 4), c = (e % (D / 4)) * 4;
-            float4 x = *reinterpret_cast<float4*>(xq + t * LD + c);
-            float4 y = *reinterpret_cast<float4*>(xk + t * LD + c);
-            const float rq = s_rq[t], rk = s_rk[t];
-            x.x *= rq; x.y *= rq; x.z *= rq; x.w *= rq;
-            y.x *= rk; y.y *= rk; y.z *= rk; y.w *= rk;
-            *reinterpret_cast<float4*>(xq + t * LD + c) = x;
-            *reinterpret_cast<float4*>(xk + t * LD + c) = y;
-            *reinterpret_cast<float4*>(gq + t * D + c) = x;
-            *reinterpret_cast<float4*>(gk + t * D + c) = y;
-        }
+    for (int e = tid; e < CP * D / 4; e += kThreads) {
+        const int t = e / (D / 4), c = (e % (D / 4)) * 4;
+        float4 x = *reinterpret_cast<float4*>(xq + t * LD + c);
+        float4 y = *reinterpret_cast<float4*>(xk + t * LD + c);
+        const float rq = s_rq[t], rk = s_rk[t];
+        x.x *= rq; x.y *= rq; x.z *= rq; x.w *= rq;
+        y.x *= rk; y.y *= rk; y.z *= rk; y.w *= rk;
+        *reinterpret_cast<float4*>(xq + t * LD + c) = x;
+        *reinterpret_cast<float4*>(xk + t * LD + c) = y;
     }
     __syncthreads();
 
-    // ---- KK^T and QK^T lower-triangular tiles: wave w takes tile row w (and
-    // w+4 when CP/16 > 4 is not possible here: NT <= 4).  Tile (i, jt), jt <= i.
-    const int m16 = lane & 15, q4 = lane >> 4;
+    // ---- q^/k^ fragments for the scan.  [Q;K] S0^T operands: fragment
+    // (qk, tile, ks), lane (m, q): token tile*16+m, d_k {32ks+4q+i, 32ks+16+4q+i}
+    // (the d_k order in which the scan holds its state).  State-update
+    // operands K^T: fragment (jt, kc), lane (m, q): d_k 16jt+m, tokens 32kc+8q+e.
+    {
+        bf16x8* gqk = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
+        for (int f = wave; f < NQK; f += kThreads / 64) {
+            const int qk = f / (NT * NKS), tile = (f / NKS) % NT, ks = f % NKS;
+            const float* row = (qk ? xk : xq) + (tile * 16 + m16) * LD + ks * 32 + q4 * 4;
+            float x[8];
+            ld4x2(x, row, row + 16);
+            store_frag(gqk, f, lane, split8(x));
+        }
+        bf16x8* gkt = W.ktf + ((int64_t)ci * P.h_k + g) * NKT * kFragVecs;
+        for (int f = wave; f < NKT; f += kThreads / 64) {
+            const int jt = f / NKC, kc = f % NKC;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = xk[(kc * 32 + q4 * 8 + e) * LD + jt * 16 + m16];
+            store_frag(gkt, f, lane, split8(x));
+        }
+    }
+
+    // ---- KK^T and QK^T lower-triangular tiles: wave w takes tile row w.
     f32x4 kk[NT], qk[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
@@ -315,17 +418,17 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     const int ti = wave;  // tile row
     if (ti < NT) {
 #pragma unroll
-        for (int ks = 0; ks < NKD; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             float x[8];
             ld8(x, xk + (ti * 16 + m16) * LD + ks * 32 + q4 * 8);
-            const Split8 ak = split8(x);
+            const Frag ak = split8(x);
             ld8(x, xq + (ti * 16 + m16) * LD + ks * 32 + q4 * 8);
-            const Split8 aq = split8(x);
+            const Frag aq = split8(x);
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) {
                 if (jt <= ti) {
                     ld8(x, xk + (jt * 16 + m16) * LD + ks * 32 + q4 * 8);
-                    const Split8 bk = split8(x);
+                    const Frag bk = split8(x);
                     kk[jt] = mma3(kk[jt], ak, bk);
                     qk[jt] = mma3(qk[jt], aq, bk);
                 }
@@ -345,9 +448,8 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
                 la = fmaxf(__logf(a[tok * P.h_v + hv]), kLogDecayMin);
                 bt = b[tok * P.h_v + hv];
             }
-            // inclusive prefix sum over the wave (CP <= 64)
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
+            for (int o = 1; o < 64; o <<= 1) {   // inclusive prefix sum (CP <= 64)
                 const float y = __shfl_up(la, o);
                 if (lane >= o) la += y;
             }
@@ -357,14 +459,13 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             }
         }
         __syncthreads();
-        // A (strictly lower) into LDS, P to the workspace.
-        float* gp = W.pm + ((int64_t)ci * P.h_v + hv) * CP * CP;
+        // A (strictly lower) and P (lower incl. diagonal) into LDS.
         if (ti < NT) {
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = ti * 16 + q4 * 4 + r;   // row (query / later token)
+                    const int t = ti * 16 + q4 * 4 + r;   // row (later token)
                     const int s = jt * 16 + m16;          // column
                     float av = 0.f, pv = 0.f;
                     if (jt <= ti && s <= t) {
@@ -373,16 +474,8 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
                         if (s < t) av = s_b[t] * dec * kk[jt][r];
                     }
                     sA[t * LT + s] = av;
-                    gp[t * CP + s] = pv;
+                    sP[t * LT + s] = pv;
                 }
-            }
-        }
-        // Tiles of A above the diagonal band are zero.
-        for (int e = tid; e < CP * CP; e += kThreads) {
-            const int t = e / CP, s = e % CP;
-            if (s / 16 > t / 16) {
-                sA[t * LT + s] = 0.f;
-                gp[t * CP + s] = 0.f;
             }
         }
         __syncthreads();
@@ -408,17 +501,16 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         }
         __syncthreads();
         for (int dist = 1; dist < NT; ++dist) {
-            // blocks (i, i-dist); 256 threads cover (NT-dist) blocks of 256 entries
             for (int e = tid; e < (NT - dist) * 256; e += kThreads) {
                 const int bi = e / 256 + dist, bj = bi - dist;
                 const int r = (e % 256) / 16, c = e % 16;
-                // M = sum_{m=bj}^{bi-1} A[bi][m] T[m][bj]  (row r, col c), then -T_ii M
+                // M = sum_{m=bj}^{bi-1} A[bi][m] T[m][bj], kept in the zero
+                // upper block (bj, bi) of A
                 float acc = 0.f;
                 for (int mb = bj; mb < bi; ++mb)
                     for (int x = 0; x < 16; ++x)
                         acc = fmaf(sA[(bi * 16 + r) * LT + mb * 16 + x],
                                    sT[(mb * 16 + x) * LT + bj * 16 + c], acc);
-                // stash M in the (still zero) upper block (bj, bi) of A
                 sA[(bj * 16 + r) * LT + bi * 16 + c] = acc;
             }
             __syncthreads();
@@ -432,11 +524,20 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             }
             __syncthreads();
         }
-        // T' = T diag(b), upper part zero; write to the workspace.
-        float* gt = W.tq + ((int64_t)ci * P.h_v + hv) * CP * CP;
+        // T' = T diag(b) (lower triangle incl. diagonal).
         for (int e = tid; e < CP * CP; e += kThreads) {
             const int t = e / CP, s = e % CP;
-            gt[e] = (s <= t) ? sT[t * LT + s] * s_b[s] : 0.f;
+            sT[t * LT + s] = (s <= t) ? sT[t * LT + s] * s_b[s] : 0.f;
+        }
+        __syncthreads();
+        // T' and P fragments: (tp, tile, kc), lane (m, q): row tile*16+m, cols 32kc+8q+e.
+        bf16x8* gtp = W.tpf + ((int64_t)ci * P.h_v + hv) * NTP * kFragVecs;
+        for (int f = wave; f < NTP; f += kThreads / 64) {
+            const int tp = f / (NT * NKC), tile = (f / NKC) % NT, kc = f % NKC;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (tp ? sP : sT)[(tile * 16 + m16) * LT + kc * 32 + q4 * 8 + e];
+            store_frag(gtp, f, lane, split8(x));
         }
         if (tid < CP) W.gl[((int64_t)ci * P.h_v + hv) * CP + tid] = s_g[tid];
         __syncthreads();
@@ -445,29 +546,59 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
 
 // -------------------------------------------------------------------- scan
 
-// grid: one workgroup per (sequence, value head, block of 16 state rows), 256 threads.  Wave w < D/32 owns the
-// state tiles 2w, 2w+1 of S^T (d_k x rows) for rows rb*16.. of value head h,
-// in MFMA accumulator layout: lane l holds S[row l%16][16 tile + 4 (l/16) + i].
-// The same registers, read as k-slots {32w+4q+i, 32w+16+4q+i} (q = l/16), are
-// the B operand of [Q;K] S^T for k-step w; Q and K fragments are loaded with
-// that d_k order.
+// One workgroup per (sequence, value head, block of 16 state rows), 256
+// threads, serial over the sequence's chunks.  Per chunk (three phases):
+//   1. wave w < CP/16 takes token tile w: X_Q = Q S0^T and X_K = K S0^T for
+//      its 16 tokens (B operand: the state block, published split in LDS),
+//      XQ = diag(gamma) X_Q stays in registers, R = V - diag(gamma) X_K goes
+//      to LDS as B fragments;
+//   2. U = T' R for the tile, published as B fragments with its decayed copy
+//      diag(exp(g_last - g)) U;
+//   3. O = XQ + P U for the tile is written out; wave w < D/32 updates state
+//      tiles 2w, 2w+1 of S^T (d_k x rows), S^T <- exp(g_last) S^T + K^T (decayed
+//      U), and republishes them.
+// The next chunk's fragments (registers) are fetched while the current chunk
+// computes; raw v rows and g run one chunk further ahead (registers, then a
+// second LDS buffer).
+template <int D, int CP>
+struct ScanLds {
+    static constexpr int NKS = D / 32, NKC = CP / 32;
+    static constexpr int NRAW = kMaxConvK - 1 + CP;
+    // 16-byte vectors
+    static constexpr int stf = 0;                              // [NKS] state fragments
+    static constexpr int rf = stf + NKS * kFragVecs;           // [NKC] R fragments
+    static constexpr int uf = rf + NKC * kFragVecs;            // [NKC] U fragments
+    static constexpr int uuf = uf + NKC * kFragVecs;           // [NKC] decayed U fragments
+    static constexpr int vec_end = uuf + NKC * kFragVecs;
+    // floats, after the fragments
+    static constexpr int vv = vec_end * 4;                     // [2][CP][16] conv+SiLU of v
+    static constexpr int raw = vv + 2 * CP * kRows;            // [2][NRAW][16] raw v rows
+    static constexpr int gg = raw + 2 * NRAW * kRows;          // [2][CP] cumulative log-decay
+    static constexpr int win = gg + 2 * CP;                    // [kMaxConvK-1][16] old window
+    static constexpr int total = win + (kMaxConvK - 1) * kRows;
+    static constexpr size_t bytes = (size_t)total * sizeof(float);
+};
+
 template <int D, int CP, typename T>
 __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ v,
     const float* __restrict__ conv_w, T* __restrict__ out) {
-    constexpr int NKS = D / 32;       // d_k slices = waves owning state
+    using S = ScanLds<D, CP>;
+    constexpr int NKS = D / 32;       // 32-wide k-steps over d_k
     constexpr int NT = CP / 16;       // token tiles
-    constexpr int NM = 2 * NT;        // M tiles of [Q;K]
-    constexpr int LR = CP + 4;        // padded row of transposed [rows][tokens] tiles
-    __shared__ __align__(16) float s_v[CP][kRows];            // conv+SiLU of v for the block
-    __shared__ __align__(16) float s_xp[NKS][NM][256];        // partial [Q;K] S^T per d_k slice
-    __shared__ __align__(16) float s_rt[kRows][LR];           // R^T
-    __shared__ __align__(16) float s_ut[kRows][LR];           // U^T
-    __shared__ __align__(16) float s_uu[kRows][LR];           // (diag(exp(g_last - g)) U)^T
-    __shared__ __align__(16) float s_xq[CP][kRows];           // diag(gamma) Q S0^T
-    __shared__ float s_win[kMaxConvK - 1][kRows];
-    __shared__ float s_g[CP];
+    constexpr int NKC = CP / 32;      // 32-wide k-steps over tokens
+    constexpr int NQK = 2 * NT * NKS, NKT = (D / 16) * NKC, NTP = 2 * NT * NKC;
+    constexpr int NRAW = S::NRAW;
+    extern __shared__ __align__(16) float smem[];
+    bf16x8* s_stf = reinterpret_cast<bf16x8*>(smem) + S::stf;
+    bf16x8* s_rf = reinterpret_cast<bf16x8*>(smem) + S::rf;
+    bf16x8* s_uf = reinterpret_cast<bf16x8*>(smem) + S::uf;
+    bf16x8* s_uuf = reinterpret_cast<bf16x8*>(smem) + S::uuf;
+    float* s_v = smem + S::vv;
+    float* s_raw = smem + S::raw;
+    float* s_g = smem + S::gg;
+    float* s_win = smem + S::win;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
@@ -477,8 +608,8 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
     // (which read the same chunk operands) share that XCD's L2.
     constexpr int NRB = D / kRows;
     const int n_units = gridDim.x;
-    const int b = blockIdx.x;
-    const int u = (n_units % 8 == 0) ? (b % 8) * (n_units / 8) + b / 8 : b;
+    const int bid = blockIdx.x;
+    const int u = (n_units % 8 == 0) ? (bid % 8) * (n_units / 8) + bid / 8 : bid;
     const int rb = u % NRB, h = (u / NRB) % P.h_v, j = u / (NRB * P.h_v);
     if (W.hdr[0] < 0) return;
     const int slot = slot_ids[j];
@@ -500,179 +631,266 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
     const int64_t vstride = (int64_t)P.h_v * D;
     float* tile_base = P.state + (((int64_t)slot * P.n_layers + layer) * P.h_v + h) * (int64_t)D * D;
 
-    // ---- load the state block (waves owning a d_k slice).
-    f32x4 st[2];
-    if (wave < NKS) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float4 x = *reinterpret_cast<const float4*>(
-                tile_base + (int64_t)(row0 + m16) * D + (2 * wave + u) * 16 + q4 * 4);
-            st[u] = f32x4{x.x, x.y, x.z, x.w};
-        }
-    }
-    // ---- old v window of the block, then the new window (last conv_k-1 raw
-    // inputs of the sequence); this workgroup is the only owner of these
-    // channels.
-    if (tid < (K - 1) * kRows) {
-        const int r = tid / kRows, c = tid % kRows;
-        s_win[r][c] = Io<T>::load(win, (int64_t)r * C + gc0 + c);
-    }
-    __syncthreads();
-    if (tid < (K - 1) * kRows) {
-        const int r = tid / kRows, c = tid % kRows;
-        const int64_t p = s0 + len - (K - 1) + r;
-        const float x = p >= s0 ? Io<T>::load(vsrc, p * vstride + c) : s_win[K - 1 + (int)(p - s0)][c];
-        Io<T>::store(win, (int64_t)r * C + gc0 + c, x);
-    }
-    const float* wv = conv_w;   // taps of channel gc0 + c at wv[(gc0 + c) * K + m]
+    // Every global access in the chunk loop is unconditional (chunk indices
+    // clamped, waves without a tile of their own redo tile NT-1 / NKS-1 and
+    // write identical values), so the compiler can count outstanding loads
+    // exactly and each prefetch is waited for only where it is used.
+    const int tw = wave < NT ? wave : NT - 1;       // token tile of this wave
+    const int sw = wave < NKS ? wave : NKS - 1;     // d_k k-step / state tiles of this wave
 
-    for (int cc = 0; cc < n_ch; ++cc) {
-        const int ci = ci0 + cc;
+    // ---- operand fetchers -------------------------------------------------
+    Frag fqk[2][NKS];      // Q and K fragments of token tile tw
+    Frag ftt[NKC];         // T' fragments of token tile tw
+    Frag fpp[NKC];         // P fragments of token tile tw
+    Frag fkt[2][NKC];      // K^T fragments of state tiles 2sw, 2sw+1
+    auto load_qk = [&](int ci) {
+        const bf16x8* base = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            fqk[0][ks] = load_frag(base, (0 * NT + tw) * NKS + ks, lane);
+            fqk[1][ks] = load_frag(base, (1 * NT + tw) * NKS + ks, lane);
+        }
+    };
+    auto load_t = [&](int ci) {
+        const bf16x8* base = W.tpf + ((int64_t)ci * P.h_v + h) * NTP * kFragVecs;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) ftt[kc] = load_frag(base, (0 * NT + tw) * NKC + kc, lane);
+    };
+    auto load_p = [&](int ci) {
+        const bf16x8* base = W.tpf + ((int64_t)ci * P.h_v + h) * NTP * kFragVecs;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) fpp[kc] = load_frag(base, (1 * NT + tw) * NKC + kc, lane);
+    };
+    auto load_kt = [&](int ci) {
+        const bf16x8* base = W.ktf + ((int64_t)ci * P.h_k + g) * NKT * kFragVecs;
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) fkt[uu][kc] = load_frag(base, (2 * sw + uu) * NKC + kc, lane);
+    };
+    // Raw v rows of chunk cc (left context first) and its g, fetched into
+    // registers: one 16-byte vector per (row, part) and one g per token.  The
+    // address is clamped into the sequence, out-of-chunk rows are zeroed after
+    // the load.
+    constexpr int VN = Vec<T>::N;
+    constexpr int kRawVec = kRows / VN;             // vectors per raw row
+    constexpr int kRawIt = (NRAW * kRawVec + kThreads - 1) / kThreads;
+    uint4 rv[kRawIt];
+    float rg = 0.f;
+    auto fetch_raw = [&](int cc) {
         const int64_t t0 = s0 + (int64_t)cc * chunk;
         const int L = min(chunk, len - cc * chunk);
-        const float* gq = W.qh + ((int64_t)ci * P.h_k + g) * CP * D;
-        const float* gk = W.kh + ((int64_t)ci * P.h_k + g) * CP * D;
-        const float* gt = W.tq + ((int64_t)ci * P.h_v + h) * CP * CP;
-        const float* gp = W.pm + ((int64_t)ci * P.h_v + h) * CP * CP;
-        if (tid < CP) s_g[tid] = W.gl[((int64_t)ci * P.h_v + h) * CP + tid];
-
-        // (a) v conv + SiLU for the block's 16 channels.
-        for (int e = tid; e < CP * kRows; e += kThreads) {
-            const int t = e / kRows, c = e % kRows;
-            float y = 0.f;
-            if (t < L) {
-                float z = 0.f;
-                for (int m = 0; m < K; ++m) {
-                    const int64_t p = t0 + t - (K - 1) + m;
-                    const float x = p >= s0 ? Io<T>::load(vsrc, p * vstride + c)
-                                            : s_win[K - 1 + (int)(p - s0)][c];
-                    z = fmaf(wv[(int64_t)(gc0 + c) * K + m], x, z);
-                }
-                y = silu(z);
-            }
-            s_v[t][c] = y;
+#pragma unroll
+        for (int it = 0; it < kRawIt; ++it) {
+            const int e = tid + it * kThreads;
+            const int r = e / kRawVec, cv = (e % kRawVec) * VN;
+            const int64_t p = t0 - (K - 1) + r;
+            const int64_t pc = p < s0 ? s0 : (p >= s0 + len ? s0 + len - 1 : p);
+            const uint4 x = *reinterpret_cast<const uint4*>(vsrc + pc * vstride + cv);
+            const bool ok = r < K - 1 + CP && p >= s0 && p < t0 + L;
+            rv[it] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
         }
+        rg = W.gl[((int64_t)(ci0 + cc) * P.h_v + h) * CP + (tid % CP)];
+    };
+    auto store_raw = [&](int cc, int buf) {
+        const int64_t t0 = s0 + (int64_t)cc * chunk;
+        float* dst = s_raw + buf * NRAW * kRows;
+#pragma unroll
+        for (int it = 0; it < kRawIt; ++it) {
+            const int e = tid + it * kThreads;
+            const int r = e / kRawVec, cv = (e % kRawVec) * VN;
+            if (r < K - 1 + CP) {
+                const int64_t p = t0 - (K - 1) + r;
+#pragma unroll
+                for (int i = 0; i < VN; ++i)
+                    dst[r * kRows + cv + i] = p < s0 ? s_win[(K - 1 + (int)(p - s0)) * kRows + cv + i]
+                                                     : Vec<T>::at(rv[it], i);
+            }
+        }
+        if (tid < CP) s_g[buf * CP + tid] = rg;
+    };
+    // conv+SiLU of the block's v channels for chunk cc from s_raw[buf].
+    const int cch = tid % kRows;
+    float wv[kMaxConvK];
+#pragma unroll
+    for (int m = 0; m < kMaxConvK; ++m) wv[m] = m < K ? conv_w[(int64_t)(gc0 + cch) * K + m] : 0.f;
+    auto conv_v = [&](int cc, int buf) {
+        const int L = min(chunk, len - cc * chunk);
+        const float* src = s_raw + buf * NRAW * kRows;
+        float* dst = s_v + buf * CP * kRows;
+        for (int t = tid / kRows; t < CP; t += kThreads / kRows) {
+            float z = 0.f;
+#pragma unroll
+            for (int m = 0; m < kMaxConvK; ++m)
+                if (m < K) z = fmaf(wv[m], src[(t + m) * kRows + cch], z);
+            dst[t * kRows + cch] = t < L ? silu(z) : 0.f;
+        }
+    };
+    // Publish this wave's state tiles as the B fragment of k-step sw.
+    f32x4 st[2];
+    auto publish_state = [&]() {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = st[0][i];
+            x[4 + i] = st[1][i];
+        }
+        store_frag(s_stf, sw, lane, split8(x));
+    };
+    // Lane and element that receive value i of token tile tw, row m16, in the
+    // B fragments over tokens (k-step kc = tw/2).
+    const int dst_lane = (2 * (tw & 1) + (q4 >> 1)) * 16 + m16;
+    const int dst_e0 = 4 * (q4 & 1);
+    // Outputs go through a buffer descriptor bounded at the sequence's last
+    // token, so rows past it are dropped without a branch.
+    T* out_base = out + (s0 * P.h_v + h) * D + row0;
+    const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
+        out_base, 0, (int)(((int64_t)(len - 1) * P.h_v * D + kRows) * sizeof(T)), 0x00020000);
 
-        // (b) partial [Q;K] S^T over this wave's d_k slice.
-        if (wave < NKS) {
-            float sv[8];
+    // ---- prologue: state block, old v window, new v window, chunk 0 operands.
+    {
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            const float4 x = *reinterpret_cast<const float4*>(
+                tile_base + (int64_t)(row0 + m16) * D + (2 * sw + uu) * 16 + q4 * 4);
+            st[uu] = f32x4{x.x, x.y, x.z, x.w};
+        }
+        publish_state();
+    }
+    if (tid < (K - 1) * kRows) {
+        const int r = tid / kRows, c = tid % kRows;
+        s_win[r * kRows + c] = Io<T>::load(win, (int64_t)r * C + gc0 + c);
+    }
+    load_kt(ci0);
+    load_qk(ci0);
+    load_t(ci0);
+    load_p(ci0);
+    fetch_raw(0);
+    __syncthreads();
+    if (tid < (K - 1) * kRows) {   // this workgroup alone owns these channels
+        const int r = tid / kRows, c = tid % kRows;
+        const int64_t p = s0 + len - (K - 1) + r;
+        const float x = p >= s0 ? Io<T>::load(vsrc, p * vstride + c) : s_win[(K - 1 + (int)(p - s0)) * kRows + c];
+        Io<T>::store(win, (int64_t)r * C + gc0 + c, x);
+    }
+    store_raw(0, 0);
+    __syncthreads();
+    conv_v(0, 0);
+    // Raw rows are fetched one chunk ahead of their LDS store, which is one
+    // phase ahead of their conv.
+    fetch_raw(min(1, n_ch - 1));
+    __syncthreads();
+
+    for (int cc = 0; cc < n_ch; ++cc) {
+        const int buf = cc & 1;
+        const bool nxt = cc + 1 < n_ch;
+        const int cn = ci0 + min(cc + 1, n_ch - 1);   // next chunk (clamped)
+        const int64_t trel = (int64_t)cc * chunk;      // chunk start relative to s0
+        const float* gb = s_g + buf * CP;
+        const float glast = gb[CP - 1];
+
+        // (1) X_Q, X_K for token tile tw; XQ in registers; R to LDS.
+        f32x4 xq;
+        {
+            f32x4 aq[2], ak[2];
+            aq[0] = aq[1] = ak[0] = ak[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const Frag bs = load_frag(s_stf, ks, lane);
+                aq[ks & 1] = mma3(aq[ks & 1], fqk[0][ks], bs);
+                ak[ks & 1] = mma3(ak[ks & 1], fqk[1][ks], bs);
+            }
+            const float* vb = s_v + buf * CP * kRows;
+            float r4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sv[i] = st[0][i];
-                sv[4 + i] = st[1][i];
+                const int t = tw * 16 + q4 * 4 + i;
+                const float gam = __expf(gb[t]);
+                xq[i] = gam * (aq[0][i] + aq[1][i]);
+                r4[i] = vb[t * kRows + m16] - gam * (ak[0][i] + ak[1][i]);
             }
-            const Split8 bs = split8(sv);
-#pragma unroll
-            for (int mt = 0; mt < NM; ++mt) {
-                const float* src = (mt < NT ? gq : gk) + (int64_t)((mt % NT) * 16 + m16) * D + wave * 32 + q4 * 4;
-                float x[8];
-                const float4 x0 = *reinterpret_cast<const float4*>(src);
-                const float4 x1 = *reinterpret_cast<const float4*>(src + 16);
-                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-                x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-                const f32x4 acc = mma3(f32x4{0.f, 0.f, 0.f, 0.f}, split8(x), bs);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s_xp[wave][mt][(q4 * 4 + i) * 16 + m16] = acc[i];
-            }
+            store_frag4(s_rf, tw >> 1, dst_lane, dst_e0, r4);
+            load_qk(cn);
         }
         __syncthreads();
 
-        // (c) reduce the slices: R = V - gamma * (K S0^T), XQ = gamma * (Q S0^T).
-        for (int e = tid; e < CP * kRows; e += kThreads) {
-            const int t = e / kRows, r = e % kRows;
-            const int tl = t % 16, tt = t / 16;
-            float xq = 0.f, xk = 0.f;
-#pragma unroll
-            for (int w = 0; w < NKS; ++w) {
-                xq += s_xp[w][tt][tl * 16 + r];
-                xk += s_xp[w][NT + tt][tl * 16 + r];
-            }
-            const float gam = __expf(s_g[t]);
-            s_xq[t][r] = gam * xq;
-            s_rt[r][t] = s_v[t][r] - gam * xk;
-        }
-        __syncthreads();
-
-        // (d) U = T' R, token tile per wave; store U^T and the decayed U^T.
-        if (wave < NT) {
+        // (2) U = T' R for token tile tw; U and the decayed U to LDS.
+        {
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < CP / 32; ++ks) {
-                if (ks * 32 <= wave * 16 + 15) {
-                    float x[8];
-                    ld8(x, gt + (int64_t)(wave * 16 + m16) * CP + ks * 32 + q4 * 8);
-                    const Split8 at = split8(x);
-                    ld8(x, &s_rt[m16][ks * 32 + q4 * 8]);
-                    acc = mma3(acc, at, split8(x));
-                }
-            }
-            const float glast = s_g[CP - 1];
+            for (int kc = 0; kc < NKC; ++kc) acc = mma3(acc, ftt[kc], load_frag(s_rf, kc, lane));
+            float u4[4], uu4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = wave * 16 + q4 * 4 + i;
-                s_ut[m16][t] = acc[i];
-                s_uu[m16][t] = acc[i] * __expf(glast - s_g[t]);
+                const int t = tw * 16 + q4 * 4 + i;
+                u4[i] = acc[i];
+                uu4[i] = acc[i] * __expf(glast - gb[t]);
             }
+            store_frag4(s_uf, tw >> 1, dst_lane, dst_e0, u4);
+            store_frag4(s_uuf, tw >> 1, dst_lane, dst_e0, uu4);
+            load_t(cn);
         }
+        if (nxt) store_raw(cc + 1, buf ^ 1);
         __syncthreads();
 
-        // (e) O = XQ + P U for the wave's token tile; state update for the
-        // wave's d_k tiles: S^T <- exp(g_last) S^T + K^T (decayed U).
-        if (wave < NT) {
-            f32x4 acc;
+        // (3) O = XQ + P U for token tile tw; state update; next v conv.
+        {
+            f32x4 acc = xq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = s_xq[wave * 16 + q4 * 4 + i][m16];
-#pragma unroll
-            for (int ks = 0; ks < CP / 32; ++ks) {
-                if (ks * 32 <= wave * 16 + 15) {
-                    float x[8];
-                    ld8(x, gp + (int64_t)(wave * 16 + m16) * CP + ks * 32 + q4 * 8);
-                    const Split8 ap = split8(x);
-                    ld8(x, &s_ut[m16][ks * 32 + q4 * 8]);
-                    acc = mma3(acc, ap, split8(x));
-                }
-            }
+            for (int kc = 0; kc < NKC; ++kc) acc = mma3(acc, fpp[kc], load_frag(s_uf, kc, lane));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = wave * 16 + q4 * 4 + i;
-                if (t < L) Io<T>::store(out, ((t0 + t) * P.h_v + h) * D + row0 + m16, acc[i]);
+                const int t = tw * 16 + q4 * 4 + i;
+                const int off = (int)(((trel + t) * P.h_v * D + m16) * (int64_t)sizeof(T));
+                if constexpr (sizeof(T) == 2)
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i]), out_rs, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), out_rs, off, 0, 0);
             }
+            load_p(cn);
         }
-        if (wave < NKS) {
-            const float dlast = __expf(s_g[CP - 1]);
+        {
+            const float dlast = __expf(glast);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int dk0 = (2 * wave + u) * 16;
-                f32x4 acc = st[u] * dlast;
+            for (int uu = 0; uu < 2; ++uu) {
+                f32x4 acc = st[uu] * dlast;
 #pragma unroll
-                for (int ks = 0; ks < CP / 32; ++ks) {
-                    float x[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = gk[(int64_t)(ks * 32 + q4 * 8 + e) * D + dk0 + m16];
-                    const Split8 ak = split8(x);
-                    ld8(x, &s_uu[m16][ks * 32 + q4 * 8]);
-                    acc = mma3(acc, ak, split8(x));
-                }
-                st[u] = acc;
+                for (int kc = 0; kc < NKC; ++kc) acc = mma3(acc, fkt[uu][kc], load_frag(s_uuf, kc, lane));
+                st[uu] = acc;
             }
+            publish_state();
+            load_kt(cn);
         }
+        if (nxt) conv_v(cc + 1, buf ^ 1);
+        fetch_raw(min(cc + 2, n_ch - 1));
         __syncthreads();
     }
 
     // ---- store the state block back to the slot.
-    if (wave < NKS) {
+    if (wave < NKS) {   // waves >= NKS hold copies of tile set NKS-1
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            *reinterpret_cast<float4*>(tile_base + (int64_t)(row0 + m16) * D + (2 * wave + u) * 16 + q4 * 4) =
-                make_float4(st[u][0], st[u][1], st[u][2], st[u][3]);
+        for (int uu = 0; uu < 2; ++uu)
+            *reinterpret_cast<float4*>(tile_base + (int64_t)(row0 + m16) * D + (2 * wave + uu) * 16 + q4 * 4) =
+                make_float4(st[uu][0], st[uu][1], st[uu][2], st[uu][3]);
     }
 }
 
 template <int D, int CP>
 size_t factor_lds_bytes() {
-    const size_t a = (size_t)2 * CP * (D + 4) * sizeof(float);
-    const size_t b = (size_t)2 * CP * (CP + 1) * sizeof(float);
+    const size_t a = (size_t)(kMaxConvK - 1 + CP) * (2 * D + 4) * sizeof(float);
+    const size_t b = (size_t)3 * CP * (CP + 1) * sizeof(float);
     return a > b ? a : b;
+}
+
+// More than 64 KiB of dynamic LDS has to be enabled per kernel (gfx950 has
+// 160 KiB per CU); done once per kernel instance.
+template <typename KFn>
+hipError_t allow_lds(KFn* kernel, size_t bytes, bool* done) {
+    if (*done) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) *done = true;
+    return e;
 }
 
 template <int D, int CP, typename T>
@@ -681,27 +899,24 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
                       const void* q, const void* k, const void* v, const float* a, const float* b,
                       const float* conv_w, void* out, hipStream_t stream) {
     const PoolView& P = pool->view;
+    static bool factor_lds = false, scan_lds = false;
+    const size_t lf = factor_lds_bytes<D, CP>();
+    const size_t ls = ScanLds<D, CP>::bytes;
+    hipError_t e = allow_lds(&prefill_factor_kernel<D, CP, T>, lf, &factor_lds);
+    if (e != hipSuccess) return e;
+    e = allow_lds(&prefill_scan_kernel<D, CP, T>, ls, &scan_lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, P, W, cu,
                        n_seq, total, chunk, mc);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = factor_lds_bytes<D, CP>();
-    // More than 64 KiB of dynamic LDS must be enabled per kernel (gfx950 has
-    // 160 KiB per CU).
-    static bool lds_set = false;
-    if (!lds_set) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_factor_kernel<D, CP, T>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_set = true;
-    }
-    hipLaunchKernelGGL((prefill_factor_kernel<D, CP, T>), dim3(mc, P.h_k), dim3(kThreads), lds,
+    hipLaunchKernelGGL((prefill_factor_kernel<D, CP, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
                        stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
                        static_cast<const T*>(k), a, b, conv_w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<D, CP, T>), dim3((D / kRows) * P.h_v * n_seq),
-                       dim3(kThreads), 0, stream, P, W, layer, cu, slot_ids, chunk,
+                       dim3(kThreads), ls, stream, P, W, layer, cu, slot_ids, chunk,
                        static_cast<const T*>(v), conv_w, static_cast<T*>(out));
     return hipGetLastError();
 }

@@ -168,6 +168,8 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int6
  *   v          device io dtype [total_tokens][h_v][d_v]
  *   a, b       device fp32 [total_tokens][h_v]
  *   out        device io dtype [total_tokens][h_v][d_v]
+ *              (q, k, v and out must be 16-byte aligned: rows are read and
+ *              written in 16-byte vectors)
  *   workspace  device, >= gdn_prefill_workspace_bytes, 256-byte aligned;
  *              scratch only, contents undefined afterwards
  * Zero-length sequences are no-ops. */
