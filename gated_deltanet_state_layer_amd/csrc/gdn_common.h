@@ -22,12 +22,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest, ties to even; NaN stays NaN (quiet).
+// Round to nearest, ties to even (the hardware conversion on gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Activation element access for the two io dtypes.

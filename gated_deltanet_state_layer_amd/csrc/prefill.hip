@@ -65,6 +65,19 @@ __device__ __forceinline__ f32x4 mma3(f32x4 acc, const Frag& a, const Frag& b) {
     return acc;
 }
 
+// acc[j] += a[j] * b[j] for N independent tiles, with the three hi/lo products
+// of all tiles interleaved so that consecutive MFMAs never depend on each
+// other (a dependent MFMA would wait for the previous one to drain).
+template <int N>
+__device__ __forceinline__ void mma3_n(f32x4* acc, const Frag* a, const Frag* b) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j].lo, b[j].hi, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j].hi, b[j].lo, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j].hi, b[j].hi, acc[j], 0, 0, 0);
+}
+
 // Fragment buffers: [fragment][hi | lo][64 lanes] of 16-byte vectors, 2 KiB
 // per fragment, so a wave reads or writes one half in one coalesced 1 KiB.
 constexpr int kFragVecs = 128;   // bf16x8 per fragment
@@ -580,7 +593,7 @@ struct ScanLds {
 };
 
 template <int D, int CP, typename T>
-__global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
+__global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ v,
     const float* __restrict__ conv_w, T* __restrict__ out) {
@@ -679,21 +692,21 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
     float rg = 0.f;
     auto fetch_raw = [&](int cc) {
         const int64_t t0 = s0 + (int64_t)cc * chunk;
-        const int L = min(chunk, len - cc * chunk);
 #pragma unroll
         for (int it = 0; it < kRawIt; ++it) {
             const int e = tid + it * kThreads;
             const int r = e / kRawVec, cv = (e % kRawVec) * VN;
             const int64_t p = t0 - (K - 1) + r;
             const int64_t pc = p < s0 ? s0 : (p >= s0 + len ? s0 + len - 1 : p);
-            const uint4 x = *reinterpret_cast<const uint4*>(vsrc + pc * vstride + cv);
-            const bool ok = r < K - 1 + CP && p >= s0 && p < t0 + L;
-            rv[it] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+            rv[it] = *reinterpret_cast<const uint4*>(vsrc + pc * vstride + cv);
         }
         rg = W.gl[((int64_t)(ci0 + cc) * P.h_v + h) * CP + (tid % CP)];
     };
-    auto store_raw = [&](int cc, int buf) {
+    // Store chunk cc's raw rows: zero past its valid tokens, window rows
+    // before the sequence start (only the first chunk reaches back there).
+    auto store_raw = [&](int cc, int buf, bool first) {
         const int64_t t0 = s0 + (int64_t)cc * chunk;
+        const int L = min(chunk, len - cc * chunk);
         float* dst = s_raw + buf * NRAW * kRows;
 #pragma unroll
         for (int it = 0; it < kRawIt; ++it) {
@@ -701,15 +714,21 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
             const int r = e / kRawVec, cv = (e % kRawVec) * VN;
             if (r < K - 1 + CP) {
                 const int64_t p = t0 - (K - 1) + r;
+                const bool valid = p < t0 + L;
+                const bool from_win = first && p < s0;
 #pragma unroll
-                for (int i = 0; i < VN; ++i)
-                    dst[r * kRows + cv + i] = p < s0 ? s_win[(K - 1 + (int)(p - s0)) * kRows + cv + i]
-                                                     : Vec<T>::at(rv[it], i);
+                for (int i = 0; i < VN; ++i) {
+                    float x = valid ? Vec<T>::at(rv[it], i) : 0.f;
+                    if (from_win) x = s_win[(K - 1 + (int)(p - s0)) * kRows + cv + i];
+                    dst[r * kRows + cv + i] = x;
+                }
             }
         }
         if (tid < CP) s_g[buf * CP + tid] = rg;
     };
-    // conv+SiLU of the block's v channels for chunk cc from s_raw[buf].
+    // conv+SiLU of the block's v channels for chunk cc from s_raw[buf].  All
+    // kMaxConvK taps are applied (weights past conv_k are zero, and raw rows
+    // past the chunk are zero), so there is no branch between the LDS reads.
     const int cch = tid % kRows;
     float wv[kMaxConvK];
 #pragma unroll
@@ -718,11 +737,11 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
         const int L = min(chunk, len - cc * chunk);
         const float* src = s_raw + buf * NRAW * kRows;
         float* dst = s_v + buf * CP * kRows;
+#pragma unroll
         for (int t = tid / kRows; t < CP; t += kThreads / kRows) {
             float z = 0.f;
 #pragma unroll
-            for (int m = 0; m < kMaxConvK; ++m)
-                if (m < K) z = fmaf(wv[m], src[(t + m) * kRows + cch], z);
+            for (int m = 0; m < kMaxConvK; ++m) z = fmaf(wv[m], src[(t + m) * kRows + cch], z);
             dst[t * kRows + cch] = t < L ? silu(z) : 0.f;
         }
     };
@@ -761,6 +780,7 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
         const int r = tid / kRows, c = tid % kRows;
         s_win[r * kRows + c] = Io<T>::load(win, (int64_t)r * C + gc0 + c);
     }
+    for (int e = tid; e < 2 * NRAW * kRows; e += kThreads) s_raw[e] = 0.f;
     load_kt(ci0);
     load_qk(ci0);
     load_t(ci0);
@@ -773,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
         const float x = p >= s0 ? Io<T>::load(vsrc, p * vstride + c) : s_win[(K - 1 + (int)(p - s0)) * kRows + c];
         Io<T>::store(win, (int64_t)r * C + gc0 + c, x);
     }
-    store_raw(0, 0);
+    store_raw(0, 0, true);
     __syncthreads();
     conv_v(0, 0);
     // Raw rows are fetched one chunk ahead of their LDS store, which is one
@@ -792,13 +812,22 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
         // (1) X_Q, X_K for token tile tw; XQ in registers; R to LDS.
         f32x4 xq;
         {
-            f32x4 aq[2], ak[2];
-            aq[0] = aq[1] = ak[0] = ak[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Frag fa[2 * NKS], fb[2 * NKS];
+            f32x4 acc[2 * NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const Frag bs = load_frag(s_stf, ks, lane);
-                aq[ks & 1] = mma3(aq[ks & 1], fqk[0][ks], bs);
-                ak[ks & 1] = mma3(ak[ks & 1], fqk[1][ks], bs);
+                fa[ks] = fqk[0][ks];
+                fa[NKS + ks] = fqk[1][ks];
+                fb[ks] = fb[NKS + ks] = bs;
+                acc[ks] = acc[NKS + ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            mma3_n<2 * NKS>(acc, fa, fb);
+            f32x4 aq = acc[0], ak = acc[NKS];
+#pragma unroll
+            for (int ks = 1; ks < NKS; ++ks) {
+                aq += acc[ks];
+                ak += acc[NKS + ks];
             }
             const float* vb = s_v + buf * CP * kRows;
             float r4[4];
@@ -806,8 +835,8 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
             for (int i = 0; i < 4; ++i) {
                 const int t = tw * 16 + q4 * 4 + i;
                 const float gam = __expf(gb[t]);
-                xq[i] = gam * (aq[0][i] + aq[1][i]);
-                r4[i] = vb[t * kRows + m16] - gam * (ak[0][i] + ak[1][i]);
+                xq[i] = gam * aq[i];
+                r4[i] = vb[t * kRows + m16] - gam * ak[i];
             }
             store_frag4(s_rf, tw >> 1, dst_lane, dst_e0, r4);
             load_qk(cn);
@@ -816,49 +845,73 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(
 
         // (2) U = T' R for token tile tw; U and the decayed U to LDS.
         {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            Frag fr[NKC];
+            f32x4 acc[NKC];
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) acc = mma3(acc, ftt[kc], load_frag(s_rf, kc, lane));
+            for (int kc = 0; kc < NKC; ++kc) {
+                fr[kc] = load_frag(s_rf, kc, lane);
+                acc[kc] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            mma3_n<NKC>(acc, ftt, fr);
+            f32x4 uv = acc[0];
+#pragma unroll
+            for (int kc = 1; kc < NKC; ++kc) uv += acc[kc];
             float u4[4], uu4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = tw * 16 + q4 * 4 + i;
-                u4[i] = acc[i];
-                uu4[i] = acc[i] * __expf(glast - gb[t]);
+                u4[i] = uv[i];
+                uu4[i] = uv[i] * __expf(glast - gb[t]);
             }
             store_frag4(s_uf, tw >> 1, dst_lane, dst_e0, u4);
             store_frag4(s_uuf, tw >> 1, dst_lane, dst_e0, uu4);
             load_t(cn);
         }
-        if (nxt) store_raw(cc + 1, buf ^ 1);
+        if (nxt) store_raw(cc + 1, buf ^ 1, false);
         __syncthreads();
 
-        // (3) O = XQ + P U for token tile tw; state update; next v conv.
+        // (3) O = XQ + P U for token tile tw, and the state update
+        //     S^T <- exp(g_last) S^T + K^T U'' for tiles 2sw, 2sw+1, interleaved.
         {
-            f32x4 acc = xq;
+            constexpr int NJ = 3 * NKC;
+            Frag fa[NJ], fb[NJ];
+            f32x4 acc[NJ];
+            const float dlast = __expf(glast);
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) acc = mma3(acc, fpp[kc], load_frag(s_uf, kc, lane));
+            for (int kc = 0; kc < NKC; ++kc) {
+                const Frag ub = load_frag(s_uf, kc, lane);
+                const Frag uub = load_frag(s_uuf, kc, lane);
+                fa[kc] = fpp[kc];
+                fb[kc] = ub;
+                acc[kc] = kc == 0 ? xq : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    fa[NKC + uu * NKC + kc] = fkt[uu][kc];
+                    fb[NKC + uu * NKC + kc] = uub;
+                    acc[NKC + uu * NKC + kc] = kc == 0 ? st[uu] * dlast : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            mma3_n<NJ>(acc, fa, fb);
+            f32x4 o = acc[0];
+#pragma unroll
+            for (int kc = 1; kc < NKC; ++kc) o += acc[kc];
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+                st[uu] = acc[NKC + uu * NKC];
+#pragma unroll
+                for (int kc = 1; kc < NKC; ++kc) st[uu] += acc[NKC + uu * NKC + kc];
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = tw * 16 + q4 * 4 + i;
                 const int off = (int)(((trel + t) * P.h_v * D + m16) * (int64_t)sizeof(T));
                 if constexpr (sizeof(T) == 2)
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[i]), out_rs, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(o[i]), out_rs, off, 0, 0);
                 else
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), out_rs, off, 0, 0);
-            }
-            load_p(cn);
-        }
-        {
-            const float dlast = __expf(glast);
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-                f32x4 acc = st[uu] * dlast;
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) acc = mma3(acc, fkt[uu][kc], load_frag(s_uuf, kc, lane));
-                st[uu] = acc;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[i]), out_rs, off, 0, 0);
             }
             publish_state();
+            load_p(cn);
             load_kt(cn);
         }
         if (nxt) conv_v(cc + 1, buf ^ 1);
