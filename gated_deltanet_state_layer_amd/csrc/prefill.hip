@@ -269,14 +269,15 @@ template <> struct Vec<float> {
 // grid (max_chunks, h_k), 256 threads.  Dynamic LDS: the chunk's raw q|k rows
 // (conv_k-1 rows of left context, then CP tokens), overwritten in place by
 // the conv+SiLU outputs and normalised; later reused for A, T and P.
-template <int D, int CP, typename T>
+// KC > 0: conv taps fixed at compile time (must equal conv_k); 0: runtime.
+template <int D, int CP, int KC, typename T>
 __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ q,
     const T* __restrict__ k, const float* __restrict__ a, const float* __restrict__ b,
     const float* __restrict__ conv_w) {
     constexpr int LD = 2 * D + 4;      // row of the staged q|k lines (floats)
-    constexpr int LT = CP + 1;
+    constexpr int LT = CP + 4;         // padded row of A, T, P (16-byte aligned)
     constexpr int NT = CP / 16;        // token tiles
     constexpr int NKS = D / 32;        // k-steps over d_k
     constexpr int NKC = CP / 32;       // k-steps over tokens
@@ -289,7 +290,10 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     float* sA = smem;                  // [CP][LT]  (after q^, k^ are consumed)
     float* sT = sA + CP * LT;          // [CP][LT]
     float* sP = sT + CP * LT;          // [CP][LT]
+    constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
+    constexpr int kMaxGroup = 4;                   // value heads per group kept in LDS
     __shared__ float s_rq[CP], s_rk[CP], s_g[CP], s_b[CP];
+    __shared__ float s_la[kMaxGroup][CP], s_bb[kMaxGroup][CP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
@@ -304,8 +308,22 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     const int cpos = ci - W.seq_coff[j];          // chunk index inside the sequence
     const int64_t t0 = s0 + (int64_t)cpos * chunk;
     const int L = min(chunk, len - cpos * chunk); // valid tokens in this chunk
-    const int K = P.conv_k, C = P.c_conv, G = P.h_v / P.h_k;
+    const int K = KC > 0 ? KC : P.conv_k, C = P.c_conv, G = P.h_v / P.h_k;
     T* win = reinterpret_cast<T*>(P.window) + ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
+
+    // ---- a and b of the chunk's tokens for every value head of the group,
+    // fetched with the staging loads (log a clamped; zero past L).
+    for (int e = tid; e < G * CP; e += kThreads) {
+        const int hl = e / CP, t = e % CP;
+        float la = 0.f, bt = 0.f;
+        if (t < L) {
+            const int64_t tok = t0 + t;
+            la = fmaxf(__logf(a[tok * P.h_v + g * G + hl]), kLogDecayMin);
+            bt = b[tok * P.h_v + g * G + hl];
+        }
+        s_la[hl][t] = la;
+        s_bb[hl][t] = bt;
+    }
 
     // ---- stage the raw q|k rows with 16-byte loads: window rows before the
     // sequence start, zeros past the chunk's valid tokens.
@@ -349,22 +367,22 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     // which no later token of the channel reads.
     for (int c = tid; c < 2 * D; c += kThreads) {
         const int gc = (c >= D ? P.h_k * D + g * D + (c - D) : g * D + c);
-        float w[kMaxConvK], line[kMaxConvK - 1];
+        float w[KM], line[KM - 1];
 #pragma unroll
-        for (int m = 0; m < kMaxConvK; ++m) w[m] = m < K ? conv_w[(int64_t)gc * K + m] : 0.f;
+        for (int m = 0; m < KM; ++m) w[m] = m < K ? conv_w[(int64_t)gc * K + m] : 0.f;
 #pragma unroll
-        for (int m = 0; m < kMaxConvK - 1; ++m) line[m] = m < K - 1 ? xr[m * LD + c] : 0.f;
+        for (int m = 0; m < KM - 1; ++m) line[m] = m < K - 1 ? xr[m * LD + c] : 0.f;
 #pragma unroll 4
         for (int t = 0; t < CP; ++t) {
             const float x = xr[(t + K - 1) * LD + c];
             float z = 0.f;
 #pragma unroll
-            for (int m = 0; m < kMaxConvK - 1; ++m)
+            for (int m = 0; m < KM - 1; ++m)
                 if (m < K - 1) z = fmaf(w[m], line[m], z);
             z = fmaf(w[K - 1], x, z);
             xr[t * LD + c] = t < L ? silu(z) : 0.f;
 #pragma unroll
-            for (int m = 0; m < kMaxConvK - 1; ++m)
+            for (int m = 0; m < KM - 1; ++m)
                 line[m] = (m == K - 2) ? x : (m < K - 2 ? line[m + 1] : line[m]);
         }
     }
@@ -455,12 +473,8 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         const int hv = g * G + hl;
         // cumulative log-decay and b for the chunk's tokens (zero past L)
         if (wave == 0) {
-            float la = 0.f, bt = 0.f;
-            if (lane < CP && lane < L) {
-                const int64_t tok = t0 + lane;
-                la = fmaxf(__logf(a[tok * P.h_v + hv]), kLogDecayMin);
-                bt = b[tok * P.h_v + hv];
-            }
+            float la = lane < CP ? s_la[hl][lane] : 0.f;
+            const float bt = lane < CP ? s_bb[hl][lane] : 0.f;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {   // inclusive prefix sum (CP <= 64)
                 const float y = __shfl_up(la, o);
@@ -480,60 +494,84 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int t = ti * 16 + q4 * 4 + r;   // row (later token)
                     const int s = jt * 16 + m16;          // column
-                    float av = 0.f, pv = 0.f;
-                    if (jt <= ti && s <= t) {
-                        const float dec = __expf(s_g[t] - s_g[s]);
-                        pv = qk[jt][r] * dec;
-                        if (s < t) av = s_b[t] * dec * kk[jt][r];
-                    }
-                    sA[t * LT + s] = av;
-                    sP[t * LT + s] = pv;
+                    const float dec = __expf(fminf(s_g[t] - s_g[s], 0.f));
+                    const bool low = jt <= ti && s <= t;
+                    sA[t * LT + s] = (low && s < t) ? s_b[t] * dec * kk[jt][r] : 0.f;
+                    sP[t * LT + s] = low ? qk[jt][r] * dec : 0.f;
                 }
             }
         }
         __syncthreads();
 
-        // (I+A)^-1, blocked by 16: diagonal blocks by forward substitution (one
-        // wave per block; lane = column * 4 + part, parts split the inner sum),
-        // then off-diagonal blocks T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj.
+        // (I+A)^-1, blocked by 16.  Diagonal blocks by forward substitution,
+        // one wave per block: lane = 4 * column c + part p; part p owns columns
+        // 4p..4p+3 of the block's A rows (in registers) and the matching rows
+        // of T's column c.  Entries of T not yet computed are still zero, so
+        // row r of T is -sum over the whole row of A times T, no predicates.
         if (wave < NT) {
             const int blk = wave * 16;
-            const int col = lane >> 2, part = lane & 3;
-            float tcol[16];   // T[blk+r][blk+col] for the rows done so far
+            const int c = lane >> 2, pp = lane & 3;
+            float ar[16][4];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ar[r][i] = sA[(blk + r) * LT + blk + 4 * pp + i];
+            float tq[4] = {0.f, 0.f, 0.f, 0.f};   // T[blk + 4pp + i][blk + c]
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float acc = 0.f;
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    if (m < r && (m & 3) == part && m >= col)
-                        acc = fmaf(sA[(blk + r) * LT + blk + m], tcol[m], acc);
+                for (int i = 0; i < 4; ++i) acc = fmaf(ar[r][i], tq[i], acc);
                 acc = group_sum<4>(acc);
-                tcol[r] = (r == col) ? 1.f : (r > col ? -acc : 0.f);
-                if (part == 0) sT[(blk + r) * LT + blk + col] = tcol[r];
+                const float trc = (r == c) ? 1.f : (r > c ? -acc : 0.f);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tq[i] = (4 * pp + i == r) ? trc : tq[i];
+                if (pp == 0) sT[(blk + r) * LT + blk + c] = trc;
             }
         }
         __syncthreads();
+        // Off-diagonal blocks by distance: M = sum_{m=bj}^{bi-1} A_{bi,m} T_{m,bj}
+        // (kept in the zero upper block (bj, bi) of A), then T_{bi,bj} = -T_{bi,bi} M.
+        // One 1x4 strip per quad of lanes; each lane of the quad sums a quarter
+        // of the inner index, then the quad adds up (DPP).  (NT-dist)*256 lanes
+        // of work per distance: every thread runs the same number of passes.
+#pragma unroll
         for (int dist = 1; dist < NT; ++dist) {
-            for (int e = tid; e < (NT - dist) * 256; e += kThreads) {
-                const int bi = e / 256 + dist, bj = bi - dist;
-                const int r = (e % 256) / 16, c = e % 16;
-                // M = sum_{m=bj}^{bi-1} A[bi][m] T[m][bj], kept in the zero
-                // upper block (bj, bi) of A
-                float acc = 0.f;
-                for (int mb = bj; mb < bi; ++mb)
-                    for (int x = 0; x < 16; ++x)
-                        acc = fmaf(sA[(bi * 16 + r) * LT + mb * 16 + x],
-                                   sT[(mb * 16 + x) * LT + bj * 16 + c], acc);
-                sA[(bj * 16 + r) * LT + bi * 16 + c] = acc;
+            const int nsub = (NT - dist) * 256;
+            for (int e = tid; e < nsub; e += kThreads) {
+                const int pp = e & 3, item = e >> 2;
+                const int bj = item / 64, bi = bj + dist;
+                const int r = (item % 64) / 4, c4 = (item % 4) * 4;
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < dist; ++kb) {
+                    const int mb = bj + kb;
+#pragma unroll
+                    for (int x4 = 0; x4 < 4; ++x4) {
+                        const int x = 4 * pp + x4;
+                        acc += sA[(bi * 16 + r) * LT + mb * 16 + x] *
+                               *reinterpret_cast<const f32x4*>(sT + (mb * 16 + x) * LT + bj * 16 + c4);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = group_sum<4>(acc[i]);
+                if (pp == 0) *reinterpret_cast<f32x4*>(sA + (bj * 16 + r) * LT + bi * 16 + c4) = acc;
             }
             __syncthreads();
-            for (int e = tid; e < (NT - dist) * 256; e += kThreads) {
-                const int bi = e / 256 + dist, bj = bi - dist;
-                const int r = (e % 256) / 16, c = e % 16;
-                float acc = 0.f;
-                for (int x = 0; x < 16; ++x)
-                    acc = fmaf(sT[(bi * 16 + r) * LT + bi * 16 + x], sA[(bj * 16 + x) * LT + bi * 16 + c], acc);
-                sT[(bi * 16 + r) * LT + bj * 16 + c] = -acc;
+            for (int e = tid; e < nsub; e += kThreads) {
+                const int pp = e & 3, item = e >> 2;
+                const int bj = item / 64, bi = bj + dist;
+                const int r = (item % 64) / 4, c4 = (item % 4) * 4;
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int x4 = 0; x4 < 4; ++x4) {
+                    const int x = 4 * pp + x4;
+                    acc += sT[(bi * 16 + r) * LT + bi * 16 + x] *
+                           *reinterpret_cast<const f32x4*>(sA + (bj * 16 + x) * LT + bi * 16 + c4);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = group_sum<4>(acc[i]);
+                if (pp == 0) *reinterpret_cast<f32x4*>(sT + (bi * 16 + r) * LT + bj * 16 + c4) = -acc;
             }
             __syncthreads();
         }
@@ -548,8 +586,7 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         for (int f = wave; f < NTP; f += kThreads / 64) {
             const int tp = f / (NT * NKC), tile = (f / NKC) % NT, kc = f % NKC;
             float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (tp ? sP : sT)[(tile * 16 + m16) * LT + kc * 32 + q4 * 8 + e];
+            ld8(x, (tp ? sP : sT) + (tile * 16 + m16) * LT + kc * 32 + q4 * 8);
             store_frag(gtp, f, lane, split8(x));
         }
         if (tid < CP) W.gl[((int64_t)ci * P.h_v + hv) * CP + tid] = s_g[tid];
@@ -592,7 +629,7 @@ struct ScanLds {
     static constexpr size_t bytes = (size_t)total * sizeof(float);
 };
 
-template <int D, int CP, typename T>
+template <int D, int CP, int KC, typename T>
 __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ v,
@@ -635,7 +672,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     const int len = cu[j + 1] - (int)s0;
     if (len <= 0) return;
     const int G = P.h_v / P.h_k, g = h / G;
-    const int K = P.conv_k, C = P.c_conv;
+    const int K = KC > 0 ? KC : P.conv_k, C = P.c_conv;
+    constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
     const int ci0 = W.seq_coff[j], n_ch = W.seq_coff[j + 1] - ci0;
     const int row0 = rb * kRows;
     T* win = reinterpret_cast<T*>(P.window) + ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
@@ -727,12 +765,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         if (tid < CP) s_g[buf * CP + tid] = rg;
     };
     // conv+SiLU of the block's v channels for chunk cc from s_raw[buf].  All
-    // kMaxConvK taps are applied (weights past conv_k are zero, and raw rows
-    // past the chunk are zero), so there is no branch between the LDS reads.
+    // KM taps are applied (weights past conv_k are zero, and raw rows past the
+    // chunk are zero), so there is no branch between the LDS reads.
     const int cch = tid % kRows;
-    float wv[kMaxConvK];
+    float wv[KM];
 #pragma unroll
-    for (int m = 0; m < kMaxConvK; ++m) wv[m] = m < K ? conv_w[(int64_t)(gc0 + cch) * K + m] : 0.f;
+    for (int m = 0; m < KM; ++m) wv[m] = m < K ? conv_w[(int64_t)(gc0 + cch) * K + m] : 0.f;
     auto conv_v = [&](int cc, int buf) {
         const int L = min(chunk, len - cc * chunk);
         const float* src = s_raw + buf * NRAW * kRows;
@@ -741,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         for (int t = tid / kRows; t < CP; t += kThreads / kRows) {
             float z = 0.f;
 #pragma unroll
-            for (int m = 0; m < kMaxConvK; ++m) z = fmaf(wv[m], src[(t + m) * kRows + cch], z);
+            for (int m = 0; m < KM; ++m) z = fmaf(wv[m], src[(t + m) * kRows + cch], z);
             dst[t * kRows + cch] = t < L ? silu(z) : 0.f;
         }
     };
@@ -931,7 +969,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
 template <int D, int CP>
 size_t factor_lds_bytes() {
     const size_t a = (size_t)(kMaxConvK - 1 + CP) * (2 * D + 4) * sizeof(float);
-    const size_t b = (size_t)3 * CP * (CP + 1) * sizeof(float);
+    const size_t b = (size_t)3 * CP * (CP + 4) * sizeof(float);
     return a > b ? a : b;
 }
 
@@ -946,7 +984,7 @@ hipError_t allow_lds(KFn* kernel, size_t bytes, bool* done) {
     return e;
 }
 
-template <int D, int CP, typename T>
+template <int D, int CP, int KC, typename T>
 hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
                       const int32_t* cu, const int32_t* slot_ids, int total, int chunk, int mc,
                       const void* q, const void* k, const void* v, const float* a, const float* b,
@@ -955,35 +993,49 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
     static bool factor_lds = false, scan_lds = false;
     const size_t lf = factor_lds_bytes<D, CP>();
     const size_t ls = ScanLds<D, CP>::bytes;
-    hipError_t e = allow_lds(&prefill_factor_kernel<D, CP, T>, lf, &factor_lds);
+    hipError_t e = allow_lds(&prefill_factor_kernel<D, CP, KC, T>, lf, &factor_lds);
     if (e != hipSuccess) return e;
-    e = allow_lds(&prefill_scan_kernel<D, CP, T>, ls, &scan_lds);
+    e = allow_lds(&prefill_scan_kernel<D, CP, KC, T>, ls, &scan_lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, P, W, cu,
                        n_seq, total, chunk, mc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_factor_kernel<D, CP, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
+    hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
                        stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
                        static_cast<const T*>(k), a, b, conv_w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<D, CP, T>), dim3((D / kRows) * P.h_v * n_seq),
+    hipLaunchKernelGGL((prefill_scan_kernel<D, CP, KC, T>), dim3((D / kRows) * P.h_v * n_seq),
                        dim3(kThreads), ls, stream, P, W, layer, cu, slot_ids, chunk,
                        static_cast<const T*>(v), conv_w, static_cast<T*>(out));
     return hipGetLastError();
 }
 
+template <int D, int KC, typename T>
+hipError_t launch_dk(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq, const int32_t* cu,
+                     const int32_t* slot_ids, int total, int chunk, int mc, const void* q,
+                     const void* k, const void* v, const float* a, const float* b,
+                     const float* conv_w, void* out, hipStream_t stream) {
+    if (chunk == 64)
+        return launch_all<D, 64, KC, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k,
+                                        v, a, b, conv_w, out, stream);
+    return launch_all<D, 32, KC, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k, v,
+                                    a, b, conv_w, out, stream);
+}
+
+// conv_k = 4 (the common width) gets kernels with the taps fixed at compile
+// time; other widths use the runtime-width kernels.
 template <int D, typename T>
 hipError_t launch_d(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq, const int32_t* cu,
                     const int32_t* slot_ids, int total, int chunk, int mc, const void* q,
                     const void* k, const void* v, const float* a, const float* b,
                     const float* conv_w, void* out, hipStream_t stream) {
-    if (chunk == 64)
-        return launch_all<D, 64, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k, v,
-                                    a, b, conv_w, out, stream);
-    return launch_all<D, 32, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k, v, a,
-                                b, conv_w, out, stream);
+    if (pool->view.conv_k == 4)
+        return launch_dk<D, 4, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k, v, a,
+                                  b, conv_w, out, stream);
+    return launch_dk<D, 0, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k, v, a, b,
+                              conv_w, out, stream);
 }
 
 }  // namespace
@@ -1005,6 +1057,7 @@ hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,
     Ws W = carve(workspace, P, n_seq, total_tokens, chunk, &bytes);
     const int64_t mc = max_chunks(n_seq, total_tokens, chunk);
     if (mc > INT32_MAX || n_seq > 65535) return hipErrorNotSupported;
+    if (P.h_v / P.h_k > 4) return hipErrorNotSupported;   // value heads per group kept in LDS
     const bool bf = pool->desc.io_dtype == GDN_BF16;
     const int total = (int)total_tokens, m = (int)mc;
     switch (P.d) {

@@ -172,7 +172,8 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int6
  *              written in 16-byte vectors)
  *   workspace  device, >= gdn_prefill_workspace_bytes, 256-byte aligned;
  *              scratch only, contents undefined afterwards
- * Zero-length sequences are no-ops. */
+ * Zero-length sequences are no-ops.  Returns GDN_ERR_UNSUPPORTED for more
+ * than 4 value heads per q/k head (h_v/h_k > 4). */
 gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
                                const int32_t* cu_seqlens, const int32_t* slot_ids,
                                int64_t total_tokens, int32_t chunk, const void* q, const void* k,

@@ -210,6 +210,37 @@ def test_ragged_edges_vs_oracle(h_k, h_v, d, chunk, io):
     assert torch.equal(pool.state[2], st0[2]) and torch.equal(pool.window[2], wn0[2])
 
 
+@pytest.mark.parametrize("conv_k,chunk", [(2, 32), (3, 64), (8, 16), (6, 64)])
+def test_other_conv_widths_vs_oracle(conv_k, chunk):
+    """Prefill, then decode and verify, with conv widths other than 4 (the
+    runtime-width kernels), continuing from pre-filled slots."""
+    s, io = syn.Shapes(2, 4, 64, 64, conv_k), "bf16"
+    say(f"conv_k={conv_k} chunk={chunk}")
+    rng = np.random.default_rng(60 + conv_k)
+    w_np = syn.draw_conv_weights(rng, s)
+    w = dev(w_np)
+    lens = np.array([3, chunk + 5, 2 * chunk, 1])
+    ids_np = np.array([1, 3, 0, 2], np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tok = syn.draw_tokens(rng, s, (int(cu[-1]),), io)
+    contents = syn.draw_pool_contents(9, ids_np, s, io)
+    pool = make_pool(s, 4, io)
+    load_slots(pool, contents)
+    out = run_prefill(pool, 0, cu, ids_np, tok, w, chunk, io)
+    op = oracle_pool(s, contents, ids_np, form="rank1")
+    ref = op.prefill(0, cu, np.arange(4), tok["q"], tok["k"], tok["v"], tok["a"], tok["b"], w_np)
+    check_out("prefill outputs", host(out), ref, io)
+    d1 = syn.draw_tokens(rng, s, (4,), io)
+    o = torch.empty((4, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    td = tokens_to_dev(d1, io)
+    pool.decode(0, dev(ids_np, torch.int32), td["q"], td["k"], td["v"], td["a"], td["b"], w, o)
+    r1 = op.decode(0, np.arange(4), d1["q"], d1["k"], d1["v"], d1["a"], d1["b"], w_np)
+    check_out("decode outputs", host(o), r1, io)
+    idx = torch.from_numpy(ids_np.astype(np.int64)).cuda()
+    check_f32("states", host(pool.state[idx]), op.S)
+    assert np.array_equal(host(pool.window[idx]), op.X)
+
+
 def test_malformed_cu_seqlens_is_flagged_and_touches_nothing():
     s, io = syn.Shapes(2, 4, 64, 64, 4), "bf16"
     say("malformed cu_seqlens")
