@@ -113,10 +113,12 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
     // LDS: line [K-1+n_tok][nch] raw inputs (window rows, then tokens),
     //      act  [n_tok][nch]     conv+SiLU outputs,
     //      nrm  [n_tok][3]       q scale, k scale, k.q
+    //      obuf [n_tok][G][D]    outputs, over `line` once the front end is done
     const int L = K - 1 + n_tok;
     float* line = smem;
     float* act = line + L * nch;
     float* nrm = act + n_tok * nch;
+    float* obuf = line;   // [n_tok][G][D] outputs; reuses `line` after the front end
 
     // ---- front end: depthwise causal conv + SiLU over the group's channels.
     T* win = reinterpret_cast<T*>(P.window) +
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
             const int64_t tok = (int64_t)i * n_tok + t;
             const float at = a[tok * P.h_v + hv];
             const float bt = b[tok * P.h_v + hv];
-            T* o_row = out + (tok * P.h_v + hv) * D;
+            float* o_row = obuf + (t * G + hl) * D;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 float u = 0.f, pq = 0.f;
@@ -215,11 +217,34 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
                 const float delta = bt * (vi - at * u);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s[p][e] = fmaf(at, s[p][e], delta * kc[e]);
-                if (lr == 0 && row < D) Io<T>::store(o_row, row, fmaf(at, pq, delta * kq));
+                if (lr == 0 && row < D) o_row[row] = fmaf(at, pq, delta * kq);
                 if (t + 1 == commit && row < D) {
                     st_state(rs, voff, p * kPass, f32x4{s[p][0], s[p][1], s[p][2], s[p][3]});
                     st_state(rs, voff + kSeg1, p * kPass, f32x4{s[p][4], s[p][5], s[p][6], s[p][7]});
                 }
+            }
+        }
+    }
+
+    // ---- outputs: staged in LDS, written as 16-byte vectors (for each token
+    // the group's G value heads are contiguous in `out`).
+    __syncthreads();
+    {
+        constexpr int VN = 16 / sizeof(T);
+        const int nvec = n_tok * G * D / VN;
+        for (int e = tid; e < nvec; e += nthr) {
+            const int t = e / (G * D / VN), c = (e % (G * D / VN)) * VN;
+            const float* src = obuf + t * G * D + c;
+            T* dst = out + (((int64_t)i * n_tok + t) * P.h_v + g * G) * D + c;
+            if constexpr (sizeof(T) == 2) {
+                uint4 u;
+                u.x = f32_to_bf16(src[0]) | ((uint32_t)f32_to_bf16(src[1]) << 16);
+                u.y = f32_to_bf16(src[2]) | ((uint32_t)f32_to_bf16(src[3]) << 16);
+                u.z = f32_to_bf16(src[4]) | ((uint32_t)f32_to_bf16(src[5]) << 16);
+                u.w = f32_to_bf16(src[6]) | ((uint32_t)f32_to_bf16(src[7]) << 16);
+                *reinterpret_cast<uint4*>(dst) = u;
+            } else {
+                *reinterpret_cast<float4*>(dst) = make_float4(src[0], src[1], src[2], src[3]);
             }
         }
     }

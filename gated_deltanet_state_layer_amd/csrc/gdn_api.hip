@@ -159,6 +159,7 @@ static gdn_status check_step_args(gdn_pool* pool, int32_t layer, int32_t n, cons
     if (n > 0 && (!slot_ids || !q || !k || !v || !a || !b || !conv_w || !out))
         return GDN_ERR_INVALID_ARG;
     if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
+    if (n > 0 && !aligned(out, 16)) return GDN_ERR_INVALID_ARG;  // 16-byte output vectors
     if (decode_verify_lds_bytes(pool, n_tok) > kMaxLds) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }

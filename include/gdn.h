@@ -125,6 +125,7 @@ gdn_status gdn_slot_reset(gdn_pool* pool, int32_t n, const int32_t* slot_ids, vo
  *   a, b    device fp32 [n][h_v]
  *   conv_w  device fp32 [C_conv][conv_k]        this layer's conv weights
  *   out     device io dtype [n][h_v][d_v]       o = S q^ with the updated S
+ *                                               (16-byte aligned)
  * The state and window of each listed slot advance by one token; every other
  * slot is left bitwise unchanged. */
 gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
@@ -141,7 +142,7 @@ gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32
  *   v          device io dtype [n][n_tok][h_v][d_v]
  *   a, b       device fp32 [n][n_tok][h_v]
  *   accept_len device int32 [n]; values outside 0..n_tok are clamped
- *   out        device io dtype [n][n_tok][h_v][d_v]
+ *   out        device io dtype [n][n_tok][h_v][d_v] (16-byte aligned)
  * Each position's output is bitwise the output of the same number of
  * gdn_decode_step calls. */
 gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
