@@ -22,8 +22,10 @@
 // Every MFMA operand that is not an exact bf16 value is split as hi + lo bf16
 // and multiplied as hi*hi + hi*lo + lo*hi (fp32 accumulate), which keeps the
 // chunked result within fp32-recurrence accuracy.  The factor kernel writes
-// every chunk operand of the scan already split and in MFMA fragment order,
-// so the scan's serial loop only splits what it produces itself.
+// the scan's chunk operands (Q^, K^, T', P) already split and in MFMA fragment
+// order, so the scan's serial loop only splits what it produces itself; the
+// transposed K^ of the state update is read from LDS with the gfx950
+// transposing load instead of being stored twice.
 #include "gdn_common.h"
 
 namespace gdn {
@@ -122,7 +124,6 @@ __device__ __forceinline__ void ld8(float* dst, const float* src) { ld4x2(dst, s
 struct Geom {
     int D, CP, NT, NKS, NKC;
     int nqk() const { return 2 * NT * NKS; }       // Q^ and K^ rows (A of [Q;K] S0^T)
-    int nkt() const { return (D / 16) * NKC; }     // K^T (A of the state update)
     int ntp() const { return 2 * NT * NKC; }       // T' and P
 };
 
@@ -131,8 +132,7 @@ struct Ws {
     int32_t* seq_coff;   // [n_seq+1] first global chunk of each sequence
     int32_t* chunk_seq;  // [max_chunks] sequence owning each chunk
     bf16x8* qkf;         // [max_chunks][h_k][nqk fragments]
-    bf16x8* ktf;         // [max_chunks][h_k][nkt fragments]
-    bf16x8* tpf;         // [max_chunks][h_v][ntp fragments]
+    bf16x8* tpf;         // [max_chunks][h_v][ntp fragments]; all-zero ones unwritten
     float* gl;           // [max_chunks][h_v][CP] cumulative log-decay in the chunk
 };
 
@@ -164,7 +164,6 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
     const size_t o_coff = take((size_t)(n_seq + 1) * 4);
     const size_t o_cseq = take((size_t)mc * 4);
     const size_t o_qk = take((size_t)mc * P.h_k * gm.nqk() * fb);
-    const size_t o_kt = take((size_t)mc * P.h_k * gm.nkt() * fb);
     const size_t o_tp = take((size_t)mc * P.h_v * gm.ntp() * fb);
     const size_t o_g = take((size_t)mc * P.h_v * gm.CP * 4);
     *bytes = off;
@@ -174,7 +173,6 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
     w.seq_coff = reinterpret_cast<int32_t*>(b + o_coff);
     w.chunk_seq = reinterpret_cast<int32_t*>(b + o_cseq);
     w.qkf = reinterpret_cast<bf16x8*>(b + o_qk);
-    w.ktf = reinterpret_cast<bf16x8*>(b + o_kt);
     w.tpf = reinterpret_cast<bf16x8*>(b + o_tp);
     w.gl = reinterpret_cast<float*>(b + o_g);
     return w;
@@ -281,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     constexpr int NT = CP / 16;        // token tiles
     constexpr int NKS = D / 32;        // k-steps over d_k
     constexpr int NKC = CP / 32;       // k-steps over tokens
-    constexpr int NQK = 2 * NT * NKS, NKT = (D / 16) * NKC, NTP = 2 * NT * NKC;
+    constexpr int NQK = 2 * NT * NKS, NTP = 2 * NT * NKC;
     constexpr int VN = Vec<T>::N;
     extern __shared__ __align__(16) float smem[];
     float* xr = smem;                  // [K-1+CP][LD]; row r <-> position t0-(K-1)+r
@@ -418,8 +416,8 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
 
     // ---- q^/k^ fragments for the scan.  [Q;K] S0^T operands: fragment
     // (qk, tile, ks), lane (m, q): token tile*16+m, d_k {32ks+4q+i, 32ks+16+4q+i}
-    // (the d_k order in which the scan holds its state).  State-update
-    // operands K^T: fragment (jt, kc), lane (m, q): d_k 16jt+m, tokens 32kc+8q+e.
+    // (the d_k order in which the scan holds its state).  The scan builds the
+    // state update's K^T operand from these itself (LDS transpose reads).
     {
         bf16x8* gqk = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
         for (int f = wave; f < NQK; f += kThreads / 64) {
@@ -428,14 +426,6 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             float x[8];
             ld4x2(x, row, row + 16);
             store_frag(gqk, f, lane, split8(x));
-        }
-        bf16x8* gkt = W.ktf + ((int64_t)ci * P.h_k + g) * NKT * kFragVecs;
-        for (int f = wave; f < NKT; f += kThreads / 64) {
-            const int jt = f / NKC, kc = f % NKC;
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = xk[(kc * 32 + q4 * 8 + e) * LD + jt * 16 + m16];
-            store_frag(gkt, f, lane, split8(x));
         }
     }
 
@@ -581,10 +571,13 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             sT[t * LT + s] = (s <= t) ? sT[t * LT + s] * s_b[s] : 0.f;
         }
         __syncthreads();
-        // T' and P fragments: (tp, tile, kc), lane (m, q): row tile*16+m, cols 32kc+8q+e.
+        // T' and P fragments: (tp, tile, kc), lane (m, q): row tile*16+m, cols
+        // 32kc+8q+e.  Both are lower triangular: fragments with kc > tile/2 are
+        // all zero and are not written (the scan never fetches them).
         bf16x8* gtp = W.tpf + ((int64_t)ci * P.h_v + hv) * NTP * kFragVecs;
         for (int f = wave; f < NTP; f += kThreads / 64) {
             const int tp = f / (NT * NKC), tile = (f / NKC) % NT, kc = f % NKC;
+            if (kc > tile / 2) continue;
             float x[8];
             ld8(x, (tp ? sP : sT) + (tile * 16 + m16) * LT + kc * 32 + q4 * 8);
             store_frag(gtp, f, lane, split8(x));
@@ -606,7 +599,8 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
 //      diag(exp(g_last - g)) U;
 //   3. O = XQ + P U for the tile is written out; wave w < D/32 updates state
 //      tiles 2w, 2w+1 of S^T (d_k x rows), S^T <- exp(g_last) S^T + K^T (decayed
-//      U), and republishes them.
+//      U), and republishes them.  K^T comes from the chunk's K^ rows, staged
+//      in LDS by phase 1 and read back with transposing loads.
 // The next chunk's fragments (registers) are fetched while the current chunk
 // computes; raw v rows and g run one chunk further ahead (registers, then a
 // second LDS buffer).
@@ -625,9 +619,27 @@ struct ScanLds {
     static constexpr int raw = vv + 2 * CP * kRows;            // [2][NRAW][16] raw v rows
     static constexpr int gg = raw + 2 * NRAW * kRows;          // [2][CP] cumulative log-decay
     static constexpr int win = gg + 2 * CP;                    // [kMaxConvK-1][16] old window
-    static constexpr int total = win + (kMaxConvK - 1) * kRows;
+    // K^ of the chunk, bf16 planes hi and lo, [CP][D] with the 16-element
+    // column groups of each row XOR-swizzled (kswz), so the rows read
+    // together by a transpose read fall in disjoint banks.
+    static constexpr int KRS = D;
+    static constexpr int kn = (win + (kMaxConvK - 1) * kRows + 3) / 4 * 4;
+    static constexpr int total = kn + CP * KRS;                // 2 planes of bf16 = CP*KRS floats
     static constexpr size_t bytes = (size_t)total * sizeof(float);
 };
+
+// Transposing LDS read (gfx950): lane 16g+j receives element j%4 of the four
+// bf16 at the address of lane 16g+4e+j/4, for e = 0..3.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+    return (16 * ((row & 3) + 4 * ((row >> 3) & 1))) & (D - 16);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
 
 template <int D, int CP, int KC, typename T>
 __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
@@ -638,8 +650,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     constexpr int NKS = D / 32;       // 32-wide k-steps over d_k
     constexpr int NT = CP / 16;       // token tiles
     constexpr int NKC = CP / 32;      // 32-wide k-steps over tokens
-    constexpr int NQK = 2 * NT * NKS, NKT = (D / 16) * NKC, NTP = 2 * NT * NKC;
+    constexpr int NQK = 2 * NT * NKS, NTP = 2 * NT * NKC;
     constexpr int NRAW = S::NRAW;
+    constexpr int KRS = S::KRS;
     extern __shared__ __align__(16) float smem[];
     bf16x8* s_stf = reinterpret_cast<bf16x8*>(smem) + S::stf;
     bf16x8* s_rf = reinterpret_cast<bf16x8*>(smem) + S::rf;
@@ -649,6 +662,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     float* s_raw = smem + S::raw;
     float* s_g = smem + S::gg;
     float* s_win = smem + S::win;
+    __bf16* s_kh = reinterpret_cast<__bf16*>(smem + S::kn);   // K^ hi plane
+    __bf16* s_kl = s_kh + CP * KRS;                            // K^ lo plane
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
@@ -693,7 +708,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     Frag fqk[2][NKS];      // Q and K fragments of token tile tw
     Frag ftt[NKC];         // T' fragments of token tile tw
     Frag fpp[NKC];         // P fragments of token tile tw
-    Frag fkt[2][NKC];      // K^T fragments of state tiles 2sw, 2sw+1
     auto load_qk = [&](int ci) {
         const bf16x8* base = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
 #pragma unroll
@@ -702,22 +716,38 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             fqk[1][ks] = load_frag(base, (1 * NT + tw) * NKS + ks, lane);
         }
     };
-    auto load_t = [&](int ci) {
-        const bf16x8* base = W.tpf + ((int64_t)ci * P.h_v + h) * NTP * kFragVecs;
+    // T' and P fragments through a buffer descriptor over the (chunk, head)
+    // block: the all-zero fragments above the diagonal (kc > tw/2) get an
+    // offset past its end, which returns zeros without touching memory.
+    constexpr int kFragBytes = kFragVecs * 16;
+    auto tp_frag = [&](int ci, int tp, Frag* dst) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16x8*>(W.tpf + ((int64_t)ci * P.h_v + h) * NTP * kFragVecs), 0,
+            NTP * kFragBytes, 0x00020000);
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) ftt[kc] = load_frag(base, (0 * NT + tw) * NKC + kc, lane);
+        for (int kc = 0; kc < NKC; ++kc) {
+            const int off = kc <= tw / 2 ? ((tp * NT + tw) * NKC + kc) * kFragBytes : NTP * kFragBytes;
+            dst[kc].hi = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + lane * 16, 0, 0));
+            dst[kc].lo = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 + lane * 16, 0, 0));
+        }
     };
-    auto load_p = [&](int ci) {
-        const bf16x8* base = W.tpf + ((int64_t)ci * P.h_v + h) * NTP * kFragVecs;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) fpp[kc] = load_frag(base, (1 * NT + tw) * NKC + kc, lane);
-    };
-    auto load_kt = [&](int ci) {
-        const bf16x8* base = W.ktf + ((int64_t)ci * P.h_k + g) * NKT * kFragVecs;
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) fkt[uu][kc] = load_frag(base, (2 * sw + uu) * NKC + kc, lane);
+    auto load_t = [&](int ci) { tp_frag(ci, 0, ftt); };
+    auto load_p = [&](int ci) { tp_frag(ci, 1, fpp); };
+    // L2 prefetch of a chunk's Q^/K^ and T'/P blocks: the D/16 workgroups of
+    // a head (same XCD) each touch their share of its 128-byte lines with one
+    // dword load per line.  Issued after the step's last fragment loads and
+    // consumed one step later, so no fragment load waits behind it.
+    constexpr int LQ = NQK * kFragBytes / 128, LTP = NTP * kFragBytes / 128;
+    constexpr int PSH = (LQ + LTP + NRB - 1) / NRB;             // lines per workgroup
+    static_assert(PSH <= kThreads, "one prefetch line per thread");
+    uint32_t pf_sink = 0, pf_val = 0;
+    auto prefetch = [&](int ci) {
+        const int li = min(rb * PSH + min(tid, PSH - 1), LQ + LTP - 1);
+        const char* p = li < LQ
+            ? reinterpret_cast<const char*>(W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs) + li * 128
+            : reinterpret_cast<const char*>(W.tpf + ((int64_t)ci * P.h_v + h) * NTP * kFragVecs) + (li - LQ) * 128;
+        pf_sink ^= pf_val;
+        pf_val = *reinterpret_cast<const uint32_t*>(p);
     };
     // Raw v rows of chunk cc (left context first) and its g, fetched into
     // registers: one 16-byte vector per (row, part) and one g per token.  The
@@ -819,7 +849,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         s_win[r * kRows + c] = Io<T>::load(win, (int64_t)r * C + gc0 + c);
     }
     for (int e = tid; e < 2 * NRAW * kRows; e += kThreads) s_raw[e] = 0.f;
-    load_kt(ci0);
     load_qk(ci0);
     load_t(ci0);
     load_p(ci0);
@@ -861,6 +890,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                 acc[ks] = acc[NKS + ks] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             mma3_n<2 * NKS>(acc, fa, fb);
+            // K^ rows of this token tile into LDS in natural [token][d_k]
+            // order (fragment elements 0-3 are d_k 32ks+4q.., 4-7 are +16).
+            if (wave < NT) {
+                const int kr = tw * 16 + m16, sz = kswz<D>(kr);
+                __bf16* kh = s_kh + kr * KRS;
+                __bf16* kl = s_kl + kr * KRS;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const Frag& f = fqk[1][ks];
+                    const int c0 = (ks * 32 + q4 * 4) ^ sz, c1 = (ks * 32 + 16 + q4 * 4) ^ sz;
+                    *reinterpret_cast<bf16x4*>(kh + c0) = __builtin_shufflevector(f.hi, f.hi, 0, 1, 2, 3);
+                    *reinterpret_cast<bf16x4*>(kh + c1) = __builtin_shufflevector(f.hi, f.hi, 4, 5, 6, 7);
+                    *reinterpret_cast<bf16x4*>(kl + c0) = __builtin_shufflevector(f.lo, f.lo, 0, 1, 2, 3);
+                    *reinterpret_cast<bf16x4*>(kl + c1) = __builtin_shufflevector(f.lo, f.lo, 4, 5, 6, 7);
+                }
+            }
             f32x4 aq = acc[0], ak = acc[NKS];
 #pragma unroll
             for (int ks = 1; ks < NKS; ++ks) {
@@ -924,7 +969,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                 acc[kc] = kc == 0 ? xq : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int uu = 0; uu < 2; ++uu) {
-                    fa[NKC + uu * NKC + kc] = fkt[uu][kc];
+                    // K^T operand of state tile 2sw+uu (rows d_k 16(2sw+uu)+m,
+                    // k = tokens 32kc+8q..): transpose reads of the staged K^.
+                    // (rows r and r+4 share their swizzle: r % 8 < 4)
+                    const int kr = kc * 32 + q4 * 8 + (m16 >> 2);
+                    const int ko = kr * KRS + (((2 * sw + uu) * 16 + 4 * (m16 & 3)) ^ kswz<D>(kr));
+                    Frag kt;
+                    kt.hi = __builtin_shufflevector(lds_read_tr(s_kh + ko), lds_read_tr(s_kh + ko + 4 * KRS),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+                    kt.lo = __builtin_shufflevector(lds_read_tr(s_kl + ko), lds_read_tr(s_kl + ko + 4 * KRS),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+                    fa[NKC + uu * NKC + kc] = kt;
                     fb[NKC + uu * NKC + kc] = uub;
                     acc[NKC + uu * NKC + kc] = kc == 0 ? st[uu] * dlast : f32x4{0.f, 0.f, 0.f, 0.f};
                 }
@@ -950,12 +1005,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             }
             publish_state();
             load_p(cn);
-            load_kt(cn);
         }
         if (nxt) conv_v(cc + 1, buf ^ 1);
         fetch_raw(min(cc + 2, n_ch - 1));
+        prefetch(ci0 + min(cc + 2, n_ch - 1));
         __syncthreads();
     }
+    // Keep the prefetch loads alive: OR-ing 0 into the error word changes nothing.
+    if ((pf_sink ^ pf_val) == 0x7fc00001u) atomicOr(P.err, 0);
 
     // ---- store the state block back to the slot.
     if (wave < NKS) {   // waves >= NKS hold copies of tile set NKS-1
