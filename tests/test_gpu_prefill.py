@@ -166,6 +166,39 @@ def test_varlen_batched_prefill_into_slots():
     assert torch.equal(pool.state[mask], st0[mask]) and torch.equal(pool.window[mask], wn0[mask])
 
 
+@pytest.mark.parametrize("d,chunk,lens,io", [
+    (32, 16, [2000, 704, 1500], "f32"),
+    (64, 64, [5000, 4500], "bf16"),
+])
+def test_long_unequal_sequences_vs_oracle(d, chunk, lens, io):
+    """Long packed sequences of unequal length (hundreds of chunk steps, one
+    a whole number of chunks) with a continuing slot, against the oracle on
+    every head of the layer."""
+    s = syn.Shapes(1, 2, d, d, 4)
+    say(f"long sequences: d={d} chunk={chunk} lens={lens} io={io}")
+    rng = np.random.default_rng(7 * d + chunk)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    tok = syn.draw_tokens(rng, s, (T,), io)
+    w_np = syn.draw_conv_weights(rng, s)
+    ids_np = np.array([3, 0, 5][:len(lens)], np.int32)
+    pool = make_pool(s, 6, io)
+    scramble_pool(pool, 41)
+    contents = syn.draw_pool_contents(99, np.array([0]), s, io)   # slot 0 continues
+    load_slots(pool, contents)
+    pool.reset(dev(ids_np[ids_np != 0], torch.int32))
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    out = run_prefill(pool, 0, cu, ids_np, tok, dev(w_np), chunk, io)
+    torch.cuda.synchronize()
+    assert pool.error() == 0
+    res = _oracle_groups(s, [0], tok, w_np, cu, ids_np,
+                         contents={int(k): v for k, v in contents.items()})
+    _check_groups(pool, res, out, ids_np, io)
+    untouched = [i for i in range(6) if i not in ids_np]
+    assert torch.equal(pool.state[untouched], st0[untouched])
+    assert torch.equal(pool.window[untouched], wn0[untouched])
+
+
 @pytest.mark.parametrize("h_k,h_v,d,chunk,io", [
     (2, 2, 32, 16, "f32"), (1, 4, 64, 32, "bf16"), (2, 4, 128, 64, "bf16"), (1, 2, 128, 32, "f32"),
     (2, 2, 64, 64, "f32")])
