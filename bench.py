@@ -37,10 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 # same way (profiles/decode_hbm_traffic.txt).  Valid only for the kernel
 # source they were taken on: DECODE_SRC_SHA256 is checked at run time and the
 # traffic is reported as null when the source has changed since.
-DECODE_TRAFFIC = {"fetch_kib": 67803.4, "write_kib": 134760.7,
-                  "copy_fetch_scale": 536870912 / (262155.9 * 1024),
+DECODE_TRAFFIC = {"fetch_kib": 67794.5, "write_kib": 134770.1,
+                  "copy_fetch_scale": 536870912 / (262155.95 * 1024),
                   "copy_write_scale": 536870912 / (524288.0 * 1024)}
-DECODE_SRC_SHA256 = "70c14dd2c9aa4d751c40641baa8d14668ad239b468231f51801171db4c5c3941"
+DECODE_SRC_SHA256 = "9337a68e7577e869c8ff58e42f2e42001ec8bfeb57f787308eb07f6cfca28417"
 
 
 def decode_traffic_bytes():
@@ -64,8 +64,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-verify", action="store_true")
-    p.add_argument("--only", choices=["decode", "verify", "prefill", "copy"], default=None,
+    p.add_argument("--only", choices=["decode", "verify", "prefill", "copy", "gemm"], default=None,
                    help="run one workload only (for profiling)")
+    p.add_argument("--prefill-case", choices=["single", "split512", "varlen", "all"], default="all",
+                   help="prefill workloads to run (for profiling one of them)")
     return p.parse_args()
 
 
@@ -100,6 +102,20 @@ def time_launches(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps * 1e-3   # seconds per launch
 
 
+def launch_percentiles(fn, n, torch):
+    """Per-launch durations (events around each launch on the current
+    stream): p10 / median / p90 in microseconds."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"p10_us": float(np.percentile(d, 10)), "median_us": float(np.median(d)),
+            "p90_us": float(np.percentile(d, 90))}
+
+
 def bench_decode(args, torch, G, syn):
     s = syn.QWEN3_NEXT
     n_slots, N, n_sets = 256, 64, 4
@@ -131,6 +147,7 @@ def bench_decode(args, torch, G, syn):
            "state_gbps": state_bytes / t / 1e9}
     if args.only == "decode":   # profiling run: the timed loop only
         return res
+    res["per_launch"] = launch_percentiles(step, max(200, args.steps), torch)
     # Hot-cache figure: the same 64 slots every step.
     t_hot = time_launches(lambda i: step(0), max(20, args.steps // 4), 5, torch)
     # Small batches (latency-bound at N=1).
@@ -142,8 +159,29 @@ def bench_decode(args, torch, G, syn):
         o = out[:n]
         small[n] = time_launches(lambda i: pool.decode(0, ids, qq, kk, vv, aa, bb, w, o),
                                  max(50, args.steps // 4), 10, torch)
+    # The step's cost does not depend on how long the context is: decode the
+    # same 64 slots after a 64-token and after an 8192-token prefill of each
+    # (context tokens drawn on the device; timing only).
+    ctx = {}
+    d0 = sets[0]
+    for L in (64, 8192):
+        cu = torch.arange(0, (N + 1) * L, L, dtype=torch.int32, device="cuda")
+        T = N * L
+        qk = torch.randn((T, 2, s.h_k, s.d_k), generator=gen, device="cuda")
+        qk = qk / qk.norm(dim=-1, keepdim=True)
+        qc, kc = qk[:, 0].bfloat16().contiguous(), qk[:, 1].bfloat16().contiguous()
+        vc = torch.randn((T, s.h_v, s.d_v), generator=gen, device="cuda").bfloat16()
+        bc = torch.sigmoid(torch.randn((T, s.h_v), generator=gen, device="cuda"))
+        ac = torch.exp(-torch.nn.functional.softplus(torch.randn((T, s.h_v), generator=gen, device="cuda")))
+        oc = torch.empty((T, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(pool.prefill_workspace_bytes(N, T, 64), dtype=torch.uint8, device="cuda")
+        pool.reset(d0["ids"])
+        pool.prefill(0, cu, d0["ids"], T, 64, qc, kc, vc, ac, bc, w, oc, ws)
+        del qk, qc, kc, vc, bc, ac, oc, ws
+        ctx[str(L)] = time_launches(lambda i: step(0), max(50, args.steps // 4), 10, torch) * 1e6
     assert pool.error() == 0
     res.update({
+        "after_context_us": ctx,
         "sec_hot": t_hot, "hot_gbps": bytes_launch / t_hot / 1e9,
         "small": {str(n): {"us": small[n] * 1e6, "tok_s": n / small[n],
                            "gbps": (n * per_slot + s.c_conv * s.conv_k * 4) / small[n] / 1e9}
@@ -236,17 +274,22 @@ def bench_prefill(args, torch, G, syn):
     out = torch.empty((T, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
     ids = torch.tensor([1], dtype=torch.int32, device="cuda")
     reps = max(10, args.steps // 10)
-    t1 = _time_prefill(args, torch, pool, [(0, T, [0, T])], ids, d, w, out, C, reps)
-    t16 = _time_prefill(args, torch, pool, [(c0, c0 + 512, [0, 512]) for c0 in range(0, T, 512)],
-                        ids, d, w, out, C, reps)
-    b = T * tok_bytes + state_rw
-    res["single"] = {"workload": "one 8192-token sequence, chunk 64", "us": t1 * 1e6,
-                     "tok_s": T / t1, "GBps": b / t1 / 1e9, "alg_TFLOPs": fl_tok * T / t1 / 1e12,
-                     "mfma_frac_alg": fl_tok * T / t1 / 1e12 / BF16_PEAK_TFLOPS}
-    res["split512"] = {"workload": "the same sequence as 16 calls of 512 tokens", "us": t16 * 1e6,
-                       "tok_s": T / t16}
+    want = lambda c: args.prefill_case in ("all", c)
+    if want("single"):
+        t1 = _time_prefill(args, torch, pool, [(0, T, [0, T])], ids, d, w, out, C, reps)
+        b = T * tok_bytes + state_rw
+        res["single"] = {"workload": "one 8192-token sequence, chunk 64", "us": t1 * 1e6,
+                         "tok_s": T / t1, "GBps": b / t1 / 1e9, "alg_TFLOPs": fl_tok * T / t1 / 1e12,
+                         "mfma_frac_alg": fl_tok * T / t1 / 1e12 / BF16_PEAK_TFLOPS}
+    if want("split512"):
+        t16 = _time_prefill(args, torch, pool, [(c0, c0 + 512, [0, 512]) for c0 in range(0, T, 512)],
+                            ids, d, w, out, C, reps)
+        res["split512"] = {"workload": "the same sequence as 16 calls of 512 tokens", "us": t16 * 1e6,
+                           "tok_s": T / t16}
     assert pool.error() == 0
     del pool, d, out
+    if not want("varlen"):
+        return res
     # Varlen: 16 sequences, lengths uniform in [128, 4096].
     case = syn.varlen_case()
     cu = case["cu_seqlens"]
@@ -264,6 +307,18 @@ def bench_prefill(args, torch, G, syn):
                      "mfma_frac_alg": fl_tok * Tv / tv / 1e12 / BF16_PEAK_TFLOPS}
     assert pool.error() == 0
     return res
+
+
+def bench_gemm(args, torch):
+    """torch's bf16 GEMM (8192^3, hipBLASLt): the measured dense-MFMA
+    reference next to the published peak."""
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn((n, n), generator=g, device="cuda").bfloat16()
+    y = torch.randn((n, n), generator=g, device="cuda").bfloat16()
+    z = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    t = time_launches(lambda i: torch.matmul(x, y, out=z), max(10, args.steps // 20), 3, torch)
+    return {"shape": [n, n, n], "us": t * 1e6, "TFLOPs": 2 * n ** 3 / t / 1e12}
 
 
 def bench_copy(args, torch):
@@ -325,6 +380,9 @@ def main():
     if args.only in (None, "copy"):
         res["copy"] = bench_copy(args, torch)
         print("# copy done", file=sys.stderr, flush=True)
+    if args.only in (None, "gemm"):
+        res["gemm"] = bench_gemm(args, torch)
+        print("# gemm done", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu and args.only is None:
         cpu = cpu_baseline(syn)
@@ -350,8 +408,10 @@ def main():
                      "frac": dec["gbps"] / HBM_PEAK_GBPS, "traffic": decode_traffic_bytes(),
                      "kernel": "decode_verify_kernel<128,bf16>",
                      "bytes_per_launch": dec["bytes"], "us_per_launch": dec["sec"] * 1e6},
+        "decode_per_launch": dec.get("per_launch"),
         "decode_hot_cache_GBps": dec.get("hot_gbps"),
         "decode_small_batches": dec.get("small"),
+        "decode_after_context_us": dec.get("after_context_us"),
     }
     if "verify" in res:
         v = res["verify"]
@@ -363,6 +423,8 @@ def main():
         line["prefill"] = res["prefill"]
     if res.get("copy"):
         line["copy_reference"] = res["copy"]
+    if res.get("gemm"):
+        line["mfma_reference"] = res["gemm"]
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
