@@ -102,6 +102,30 @@ def time_launches(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps * 1e-3   # seconds per launch
 
 
+def time_graph(fn, n_inner, replays, torch):
+    """Seconds per call of fn, captured n_inner times into one HIP graph and
+    replayed: the device-side rate without the host launch cost."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(n_inner):
+                fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (replays * n_inner)
+
+
 def launch_percentiles(fn, n, torch):
     """Per-launch durations (events around each launch on the current
     stream): p10 / median / p90 in microseconds."""
@@ -150,15 +174,18 @@ def bench_decode(args, torch, G, syn):
     res["per_launch"] = launch_percentiles(step, max(200, args.steps), torch)
     # Hot-cache figure: the same 64 slots every step.
     t_hot = time_launches(lambda i: step(0), max(20, args.steps // 4), 5, torch)
-    # Small batches (latency-bound at N=1).
-    small = {}
+    # Small batches (latency-bound at N=1): launched from the Python loop
+    # (host launch rate included) and replayed from a captured HIP graph of
+    # 50 steps (device time per step).
+    small, small_graph = {}, {}
     for n in (1, 4, 16):
         d = sets[0]
         ids = d["ids"][:n].clone()
         qq, kk, vv, aa, bb = (d[m][:n].contiguous() for m in "qkvab")
         o = out[:n]
-        small[n] = time_launches(lambda i: pool.decode(0, ids, qq, kk, vv, aa, bb, w, o),
-                                 max(50, args.steps // 4), 10, torch)
+        fn = lambda: pool.decode(0, ids, qq, kk, vv, aa, bb, w, o)
+        small[n] = time_launches(lambda i: fn(), max(50, args.steps // 4), 10, torch)
+        small_graph[n] = time_graph(fn, 50, 4, torch)
     # The step's cost does not depend on how long the context is: decode the
     # same 64 slots after a 64-token and after an 8192-token prefill of each
     # (context tokens drawn on the device; timing only).
@@ -183,7 +210,8 @@ def bench_decode(args, torch, G, syn):
     res.update({
         "after_context_us": ctx,
         "sec_hot": t_hot, "hot_gbps": bytes_launch / t_hot / 1e9,
-        "small": {str(n): {"us": small[n] * 1e6, "tok_s": n / small[n],
+        "small": {str(n): {"us": small[n] * 1e6, "graph_us": small_graph[n] * 1e6,
+                           "tok_s": n / small[n], "graph_tok_s": n / small_graph[n],
                            "gbps": (n * per_slot + s.c_conv * s.conv_k * 4) / small[n] / 1e9}
                   for n in small},
     })

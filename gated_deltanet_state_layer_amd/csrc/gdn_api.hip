@@ -43,7 +43,9 @@ void layout(const gdn_pool_desc* d, size_t* state_bytes, size_t* window_bytes, s
     const size_t c_conv = 2 * (size_t)d->h_k * d->d_k + (size_t)d->h_v * d->d_v;
     *state_bytes = (size_t)d->n_slots * d->n_layers * d->h_v * d->d_v * d->d_k * sizeof(float);
     *window_bytes = (size_t)d->n_slots * d->n_layers * (d->conv_k - 1) * c_conv * io;
-    *aux_bytes = align_up(*window_bytes, kAlign) + kAlign;
+    // windows | meta block (error word) | row-split decode counters
+    *aux_bytes = align_up(*window_bytes, kAlign) + kAlign +
+                 align_up((size_t)d->n_slots * d->n_layers * d->h_k * sizeof(int32_t), kAlign);
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -112,6 +114,7 @@ gdn_status gdn_pool_create(const gdn_pool_desc* desc, void* state_buf, void* aux
     v.state = static_cast<float*>(state_buf);
     v.window = aux_buf;
     v.err = reinterpret_cast<int32_t*>(static_cast<char*>(aux_buf) + align_up(p->window_bytes, kAlign));
+    v.ctr = reinterpret_cast<int32_t*>(static_cast<char*>(aux_buf) + align_up(p->window_bytes, kAlign) + kAlign);
     v.n_slots = desc->n_slots;
     v.n_layers = desc->n_layers;
     v.h_k = desc->h_k;
@@ -174,10 +177,14 @@ gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32
         st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
         if (st != GDN_OK) return st;
     }
-    return launch_decode_verify(pool, layer, n, slot_ids, 1, q, k, v, a, b, conv_w, nullptr, out,
-                                s) == hipSuccess
-               ? GDN_OK
-               : GDN_ERR_HIP;
+    // Few entries: split each head's rows over several workgroups so that
+    // more CUs stream the state (same arithmetic, bitwise equal results).
+    const int nrb = decode_rows_split(pool, n);
+    const hipError_t e = nrb > 1 ? launch_decode_rows(pool, nrb, layer, n, slot_ids, q, k, v, a, b,
+                                                      conv_w, out, s)
+                                 : launch_decode_verify(pool, layer, n, slot_ids, 1, q, k, v, a, b,
+                                                        conv_w, nullptr, out, s);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,

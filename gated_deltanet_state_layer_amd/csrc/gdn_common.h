@@ -75,6 +75,7 @@ struct PoolView {
     float* state;         // [n_slots][n_layers][h_v][d_v][d_k]
     void* window;         // [n_slots][n_layers][conv_k-1][C_conv] io dtype
     int32_t* err;         // sticky error word
+    int32_t* ctr;         // [n_slots][n_layers][h_k] row-split decode counters (0 between calls)
     int32_t n_slots, n_layers, h_k, h_v, d, conv_k, c_conv;
     float q_scale, eps;
 };
@@ -101,6 +102,13 @@ hipError_t launch_decode_verify(const gdn_pool* pool, int32_t layer, int32_t n,
                                 const void* k, const void* v, const float* a, const float* b,
                                 const float* conv_w, const int32_t* accept_len, void* out,
                                 hipStream_t stream);
+// Low-batch decode with the rows of each head split over workgroups:
+// the split factor for n entries (1 = use the one-workgroup kernel).
+int decode_rows_split(const gdn_pool* pool, int32_t n);
+hipError_t launch_decode_rows(const gdn_pool* pool, int nrb, int32_t layer, int32_t n,
+                              const int32_t* slot_ids, const void* q, const void* k, const void* v,
+                              const float* a, const float* b, const float* conv_w, void* out,
+                              hipStream_t stream);
 size_t prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
                                int32_t chunk);
 hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,

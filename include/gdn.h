@@ -50,7 +50,9 @@
  *       (row 0 = oldest raw input; C_conv = 2*h_k*d_k + h_v*d_v channels in
  *       the order q heads | k heads | v heads, each head's d contiguous),
  *       then, at the next 256-byte boundary, a 256-byte meta block whose
- *       first int32 is the sticky device error word.
+ *       first int32 is the sticky device error word, then int32
+ *       [n_slots][n_layers][h_k] counters of the low-batch decode path
+ *       (zero between calls; zeroed by gdn_pool_create).
  *
  * Activations: per token, raw q, k are [h_k][d_k] and v is [h_v][d_v] in the
  * io dtype; a and b are [h_v] fp32, already activated (a in (0,1], b in
@@ -119,7 +121,9 @@ gdn_status gdn_slot_reset(gdn_pool* pool, int32_t n, const int32_t* slot_ids, vo
 
 /* One decode token for each of n entries; entry i reads and writes slot
  * slot_ids[i] of layer `layer` (baseRT issue #31, "Why this looks tractable":
- * a slot index in the recurrence kernels).
+ * a slot index in the recurrence kernels).  With few entries the rows of each
+ * state tile are spread over several workgroups; results are bitwise the
+ * same either way.
  *   q, k    device io dtype [n][h_k][d_k]      raw (pre-conv) inputs
  *   v       device io dtype [n][h_v][d_v]
  *   a, b    device fp32 [n][h_v]

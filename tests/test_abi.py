@@ -45,11 +45,11 @@ def test_pool_bytes_layout(lib):
     sb, ab = B.pool_bytes(d)
     assert sb == 256 * 32 * 128 * 128 * 4
     win = 256 * 3 * (2 * 16 * 128 + 32 * 128) * 2
-    assert ab == (win + 255) // 256 * 256 + 256
+    assert ab == (win + 255) // 256 * 256 + 256 + (256 * 1 * 16 * 4 + 255) // 256 * 256
     d = B.make_desc(3, 2, 2, 2, 32, 32, 4, B.GDN_F32)
     sb, ab = B.pool_bytes(d)
     assert sb == 3 * 2 * 2 * 32 * 32 * 4
-    assert ab == (3 * 2 * 3 * 192 * 4 + 255) // 256 * 256 + 256
+    assert ab == (3 * 2 * 3 * 192 * 4 + 255) // 256 * 256 + 256 + 256   # 3*2*2 counters
 
 
 @pytest.mark.parametrize("field,value,status", [

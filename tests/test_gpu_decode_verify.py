@@ -107,6 +107,45 @@ def test_batched_decode_is_bitwise_batch_invariant():
     assert torch.equal(pa.state, pb.state) and torch.equal(pa.window, pb.window)
 
 
+@pytest.mark.parametrize("h_k,h_v,d,io,n", [(16, 32, 128, "bf16", 1), (16, 32, 128, "bf16", 4),
+                                            (16, 32, 128, "f32", 16), (4, 4, 128, "f32", 1),
+                                            (2, 4, 64, "bf16", 3)])
+def test_row_split_decode_is_bitwise_one_workgroup_decode(h_k, h_v, d, io, n):
+    """Few entries: decode spreads each head's rows over several workgroups
+    (the q/k window rolled by the last of them).  Three consecutive steps,
+    with a padding entry, equal the one-workgroup kernel (verify with one
+    token, accept_len 1) bitwise, and every roll counter is back to zero."""
+    s = syn.Shapes(h_k, h_v, d, d, 4)
+    say(f"row-split decode: {s} io={io} n={n}")
+    rng = np.random.default_rng(300 + n + d)
+    n_slots = 3 * n + 2
+    ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
+    ids_pad = np.concatenate([ids_np, [-1]]).astype(np.int32)
+    w = dev(syn.draw_conv_weights(rng, s))
+    contents = syn.draw_pool_contents(55, ids_np, s, io)
+    pa = make_pool(s, n_slots, io)
+    load_slots(pa, contents)
+    pb = make_pool(s, n_slots, io)
+    load_slots(pb, contents)
+    ids = dev(ids_pad, torch.int32)
+    one = dev(np.ones(n + 1, np.int32), torch.int32)
+    for step in range(3):
+        tok = syn.draw_tokens(rng, s, (n + 1,), io)
+        td = tokens_to_dev(tok, io)
+        oa = _decode(pa, 0, ids, td, w, io)
+        tv = tokens_to_dev({m: tok[m][:, None] for m in tok}, io)
+        ob = _verify(pb, 0, ids, 1, tv, w, one)[:, 0]
+        torch.cuda.synchronize()
+        assert torch.equal(oa[:n], ob[:n]), f"step {step}: outputs differ"
+        assert torch.isnan(oa[n].float()).all(), "padding entry's output was written"
+    assert torch.equal(pa.state, pb.state) and torch.equal(pa.window, pb.window)
+    assert pa.error() == 0
+    win_bytes = pa.window.numel() * pa.window.element_size()
+    off = (win_bytes + 255) // 256 * 256 + 256
+    ctr = pa._aux_buf[off:off + n_slots * h_k * 4].view(torch.int32)
+    assert not ctr.any(), "a roll counter is not back to zero"
+
+
 def test_padding_and_out_of_range_ids():
     s, io = syn.Shapes(2, 4, 64, 64, 4), "bf16"
     say("padding / out-of-range ids")
