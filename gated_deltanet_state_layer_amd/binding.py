@@ -28,7 +28,8 @@ GDN_VALIDATE = 1
 EXPORTED = (
     "gdn_pool_bytes", "gdn_pool_create", "gdn_pool_destroy", "gdn_slot_reset",
     "gdn_decode_step", "gdn_verify_step", "gdn_prefill_workspace_bytes",
-    "gdn_prefill_chunked", "gdn_pool_error", "gdn_status_string",
+    "gdn_prefill_chunked", "gdn_prefill_chunked_ckpt", "gdn_slot_copy", "gdn_pool_error",
+    "gdn_status_string",
 )
 
 
@@ -68,10 +69,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_pool_create": [ctypes.POINTER(PoolDesc), P, P, P, ctypes.POINTER(P)],
         "gdn_pool_destroy": [P],
         "gdn_slot_reset": [P, I32, P, P],
+        "gdn_slot_copy": [P, I32, P, P, P],
         "gdn_decode_step": [P, I32, I32, P, P, P, P, P, P, P, P, P],
         "gdn_verify_step": [P, I32, I32, P, I32, P, P, P, P, P, P, P, P, P],
         "gdn_prefill_workspace_bytes": [P, I32, I64, I32, PSZ],
         "gdn_prefill_chunked": [P, I32, I32, P, P, I64, I32, P, P, P, P, P, P, P, P, SZ, P],
+        "gdn_prefill_chunked_ckpt": [P, I32, I32, P, P, I64, I32, P, P, P, P, P, P, P, I32, P, P,
+                                     P, SZ, P],
         "gdn_pool_error": [P, P, ctypes.POINTER(I32)],
     }
     for name, args in sig.items():
@@ -167,6 +171,11 @@ class Pool:
         _check(lib.gdn_slot_reset(self._h, int(slot_ids.numel()), _ptr(slot_ids), _stream(stream)),
                "gdn_slot_reset")
 
+    def copy(self, src_ids, dst_ids, stream=None):
+        lib = load_library()
+        _check(lib.gdn_slot_copy(self._h, int(src_ids.numel()), _ptr(src_ids), _ptr(dst_ids),
+                                 _stream(stream)), "gdn_slot_copy")
+
     def decode(self, layer, slot_ids, q, k, v, a, b, conv_w, out, stream=None):
         lib = load_library()
         _check(lib.gdn_decode_step(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), _ptr(q),
@@ -198,6 +207,20 @@ class Pool:
                                        total_tokens, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                        _ptr(b), _ptr(conv_w), _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream(stream)), "gdn_prefill_chunked")
+        return out
+
+    def prefill_ckpt(self, layer, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v, a, b,
+                     conv_w, out, ckpt_every, ckpt_offsets, ckpt_slots, workspace=None,
+                     stream=None):
+        lib = load_library()
+        n_seq = int(slot_ids.numel())
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib.gdn_prefill_chunked_ckpt(self._h, layer, n_seq, _ptr(cu_seqlens),
+                                            _ptr(slot_ids), total_tokens, chunk, _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(out),
+                                            ckpt_every, _ptr(ckpt_offsets), _ptr(ckpt_slots),
+                                            _ptr(workspace), ws_bytes, _stream(stream)),
+               "gdn_prefill_chunked_ckpt")
         return out
 
     def error(self, stream=None) -> int:

@@ -81,6 +81,69 @@ gdn_status host_check_seqlens(const int32_t* cu, int32_t n_seq, int64_t total, h
     return GDN_OK;
 }
 
+// Host check of the checkpoint lists (GDN_VALIDATE): offsets from 0,
+// non-decreasing; every sequence and checkpoint slot in range and distinct.
+gdn_status host_check_ckpt(const int32_t* slot_ids, int32_t n_seq, const int32_t* off,
+                           const int32_t* slots, int32_t n_slots, hipStream_t s) {
+    std::vector<int32_t> ho(n_seq + 1), hs(n_seq);
+    if (hipMemcpyAsync(ho.data(), off, (n_seq + 1) * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(hs.data(), slot_ids, n_seq * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (ho[0] != 0) return GDN_ERR_BAD_INDEX;
+    for (int j = 0; j < n_seq; ++j)
+        if (ho[j + 1] < ho[j]) return GDN_ERR_BAD_INDEX;
+    std::vector<int32_t> hc(ho[n_seq]);
+    if (!hc.empty() &&
+        (hipMemcpyAsync(hc.data(), slots, hc.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+         hipStreamSynchronize(s) != hipSuccess))
+        return GDN_ERR_HIP;
+    std::vector<int32_t> seen;
+    for (int32_t x : hs) if (x >= 0) seen.push_back(x);
+    for (int32_t x : hc) if (x >= 0) seen.push_back(x);
+    for (int32_t x : seen) if (x >= n_slots) return GDN_ERR_BAD_INDEX;
+    std::sort(seen.begin(), seen.end());
+    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return GDN_ERR_BAD_INDEX;
+    return GDN_OK;
+}
+
+gdn_status prefill_common(gdn_pool* pool, int32_t layer, int32_t n_seq, const int32_t* cu_seqlens,
+                          const int32_t* slot_ids, int64_t total_tokens, int32_t chunk,
+                          const void* q, const void* k, const void* v, const float* a,
+                          const float* b, const float* conv_w, void* out, int32_t ckpt_every,
+                          const int32_t* ckpt_offsets, const int32_t* ckpt_slots, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!pool || layer < 0 || layer >= pool->desc.n_layers || n_seq < 0 || total_tokens < 0)
+        return GDN_ERR_INVALID_ARG;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (total_tokens > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (ckpt_every < 0 || ckpt_every % chunk != 0) return GDN_ERR_INVALID_ARG;
+    if (n_seq == 0) return GDN_OK;
+    if (!cu_seqlens || !slot_ids || !conv_w) return GDN_ERR_INVALID_ARG;
+    if (ckpt_every > 0 && (!ckpt_offsets || !ckpt_slots)) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !k || !v || !a || !b || !out)) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)))
+        return GDN_ERR_INVALID_ARG;
+    const size_t need = prefill_workspace_bytes(pool, n_seq, total_tokens, chunk);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, kAlign)) return GDN_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    if (pool->desc.flags & GDN_VALIDATE) {
+        gdn_status st = ckpt_every > 0
+                            ? host_check_ckpt(slot_ids, n_seq, ckpt_offsets, ckpt_slots,
+                                              pool->desc.n_slots, s)
+                            : host_check_ids(slot_ids, n_seq, pool->desc.n_slots, s);
+        if (st != GDN_OK) return st;
+        st = host_check_seqlens(cu_seqlens, n_seq, total_tokens, s);
+        if (st != GDN_OK) return st;
+    }
+    const Ckpt ck{ckpt_every / chunk, ckpt_offsets, ckpt_slots};
+    hipError_t e = launch_prefill(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q,
+                                  k, v, a, b, conv_w, out, workspace, ck, s);
+    if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace gdn
 
@@ -219,29 +282,48 @@ gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
                                int64_t total_tokens, int32_t chunk, const void* q, const void* k,
                                const void* v, const float* a, const float* b, const float* conv_w,
                                void* out, void* workspace, size_t workspace_bytes, void* stream) {
-    if (!pool || layer < 0 || layer >= pool->desc.n_layers || n_seq < 0 || total_tokens < 0)
-        return GDN_ERR_INVALID_ARG;
-    if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
-    if (total_tokens > INT32_MAX) return GDN_ERR_UNSUPPORTED;
-    if (n_seq == 0) return GDN_OK;
-    if (!cu_seqlens || !slot_ids || !conv_w) return GDN_ERR_INVALID_ARG;
-    if (total_tokens > 0 && (!q || !k || !v || !a || !b || !out)) return GDN_ERR_INVALID_ARG;
-    if (total_tokens > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)))
-        return GDN_ERR_INVALID_ARG;
-    const size_t need = prefill_workspace_bytes(pool, n_seq, total_tokens, chunk);
-    if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
-    if (workspace && !aligned(workspace, kAlign)) return GDN_ERR_INVALID_ARG;
+    return prefill_common(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v,
+                          a, b, conv_w, out, 0, nullptr, nullptr, workspace, workspace_bytes,
+                          stream);
+}
+
+gdn_status gdn_prefill_chunked_ckpt(gdn_pool* pool, int32_t layer, int32_t n_seq,
+                                    const int32_t* cu_seqlens, const int32_t* slot_ids,
+                                    int64_t total_tokens, int32_t chunk, const void* q,
+                                    const void* k, const void* v, const float* a, const float* b,
+                                    const float* conv_w, void* out, int32_t ckpt_every,
+                                    const int32_t* ckpt_offsets, const int32_t* ckpt_slots,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_common(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v,
+                          a, b, conv_w, out, ckpt_every, ckpt_offsets, ckpt_slots, workspace,
+                          workspace_bytes, stream);
+}
+
+gdn_status gdn_slot_copy(gdn_pool* pool, int32_t n, const int32_t* src_ids,
+                         const int32_t* dst_ids, void* stream) {
+    if (!pool || n < 0 || (n > 0 && (!src_ids || !dst_ids))) return GDN_ERR_INVALID_ARG;
+    if (n == 0) return GDN_OK;
+    if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
     hipStream_t s = as_stream(stream);
     if (pool->desc.flags & GDN_VALIDATE) {
-        gdn_status st = host_check_ids(slot_ids, n_seq, pool->desc.n_slots, s);
-        if (st != GDN_OK) return st;
-        st = host_check_seqlens(cu_seqlens, n_seq, total_tokens, s);
-        if (st != GDN_OK) return st;
+        // sources in range; destinations in range, distinct and not sources
+        std::vector<int32_t> hs(n), hd(n);
+        if (hipMemcpyAsync(hs.data(), src_ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipMemcpyAsync(hd.data(), dst_ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return GDN_ERR_HIP;
+        std::vector<int32_t> dst;
+        for (int i = 0; i < n; ++i) {
+            if (hs[i] >= pool->desc.n_slots || hd[i] >= pool->desc.n_slots) return GDN_ERR_BAD_INDEX;
+            if (hs[i] >= 0 && hd[i] >= 0) dst.push_back(hd[i]);
+        }
+        std::sort(dst.begin(), dst.end());
+        if (std::adjacent_find(dst.begin(), dst.end()) != dst.end()) return GDN_ERR_BAD_INDEX;
+        for (int i = 0; i < n; ++i)
+            if (hs[i] >= 0 && hd[i] >= 0 && std::binary_search(dst.begin(), dst.end(), hs[i]))
+                return GDN_ERR_BAD_INDEX;
     }
-    hipError_t e = launch_prefill(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q,
-                                  k, v, a, b, conv_w, out, workspace, s);
-    if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return launch_slot_copy(pool, n, src_ids, dst_ids, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 gdn_status gdn_pool_error(gdn_pool* pool, void* stream, int32_t* device_error) {

@@ -97,6 +97,15 @@ namespace gdn {
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_slot_reset(const gdn_pool* pool, int32_t n, const int32_t* slot_ids,
                              hipStream_t stream);
+hipError_t launch_slot_copy(const gdn_pool* pool, int32_t n, const int32_t* src_ids,
+                            const int32_t* dst_ids, hipStream_t stream);
+// Prefill checkpoints: after every `every_chunks` chunks of sequence j,
+// checkpoint m goes to slot slots[off[j] + m] (if m < off[j+1] - off[j]).
+struct Ckpt {
+    int every_chunks;      // 0: none
+    const int32_t* off;    // [n_seq+1]
+    const int32_t* slots;  // [off[n_seq]]
+};
 hipError_t launch_decode_verify(const gdn_pool* pool, int32_t layer, int32_t n,
                                 const int32_t* slot_ids, int32_t n_tok, const void* q,
                                 const void* k, const void* v, const float* a, const float* b,
@@ -115,6 +124,6 @@ hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,
                           const int32_t* cu_seqlens, const int32_t* slot_ids,
                           int64_t total_tokens, int32_t chunk, const void* q, const void* k,
                           const void* v, const float* a, const float* b, const float* conv_w,
-                          void* out, void* workspace, hipStream_t stream);
+                          void* out, void* workspace, Ckpt ck, hipStream_t stream);
 
 }  // namespace gdn

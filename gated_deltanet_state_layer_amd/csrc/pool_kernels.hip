@@ -34,7 +34,41 @@ __global__ __launch_bounds__(kThreads) void slot_reset_kernel(PoolView P, const 
     for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < window16_per_slot; j += stride) wn[j] = z;
 }
 
+// Copy the state tiles and conv windows of every layer of slot src_ids[i]
+// to slot dst_ids[i] (a state "saved and copied whole": "Project: adding the
+// hybrid model Qwen3.5", prefix-cache notes).  grid = (blocks per slot, n).
+__global__ __launch_bounds__(kThreads) void slot_copy_kernel(PoolView P, const int32_t* src_ids,
+                                                            const int32_t* dst_ids,
+                                                            size_t state16_per_slot,
+                                                            size_t window16_per_slot) {
+    const int src = src_ids[blockIdx.y], dst = dst_ids[blockIdx.y];
+    if (src < 0 || dst < 0) return;
+    if (src >= P.n_slots || dst >= P.n_slots) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(P.err, kErrSlotRange);
+        return;
+    }
+    const float4* ss = reinterpret_cast<const float4*>(P.state) + (size_t)src * state16_per_slot;
+    float4* sd = reinterpret_cast<float4*>(P.state) + (size_t)dst * state16_per_slot;
+    const float4* ws = reinterpret_cast<const float4*>(P.window) + (size_t)src * window16_per_slot;
+    float4* wd = reinterpret_cast<float4*>(P.window) + (size_t)dst * window16_per_slot;
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < state16_per_slot; j += stride) sd[j] = ss[j];
+    for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < window16_per_slot; j += stride) wd[j] = ws[j];
+}
+
 }  // namespace
+
+hipError_t launch_slot_copy(const gdn_pool* pool, int32_t n, const int32_t* src_ids,
+                            const int32_t* dst_ids, hipStream_t stream) {
+    const PoolView& P = pool->view;
+    const size_t state16 = (size_t)P.n_layers * P.h_v * P.d * P.d / 4;
+    const size_t win16 = (size_t)P.n_layers * (P.conv_k - 1) * P.c_conv * pool->io_size / 16;
+    size_t blocks = (state16 + kThreads * 4 - 1) / (kThreads * 4);
+    blocks = blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks);
+    hipLaunchKernelGGL(slot_copy_kernel, dim3((unsigned)blocks, n), dim3(kThreads), 0, stream, P,
+                       src_ids, dst_ids, state16, win16);
+    return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
     const size_t n16 = bytes / 16;  // callers pass multiples of 16 bytes

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ q,
     const T* __restrict__ k, const float* __restrict__ a, const float* __restrict__ b,
-    const float* __restrict__ conv_w) {
+    const float* __restrict__ conv_w, Ckpt ck) {
     constexpr int LD = 2 * D + 4;      // row of the staged q|k lines (floats)
     constexpr int LT = CP + 4;         // padded row of A, T, P (16-byte aligned)
     constexpr int NT = CP / 16;        // token tiles
@@ -360,6 +360,21 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             Io<T>::store(win, (int64_t)m * C + (isk ? P.h_k * D : 0) + g * D + cc, x);
         }
         __syncthreads();
+    }
+    // A checkpoint after this chunk (full, ending on a multiple of the
+    // checkpoint interval) holds these channels' last conv_k-1 raw rows.
+    if (ck.every_chunks > 0 && L == chunk && (cpos + 1) % ck.every_chunks == 0) {
+        const int m = (cpos + 1) / ck.every_chunks - 1;
+        const int cs = m < ck.off[j + 1] - ck.off[j] ? ck.slots[ck.off[j] + m] : -1;
+        if (cs >= 0 && cs < P.n_slots) {
+            T* cwin = reinterpret_cast<T*>(P.window) + ((int64_t)cs * P.n_layers + layer) * (int64_t)(K - 1) * C;
+            for (int e = tid; e < (K - 1) * 2 * D; e += kThreads) {
+                const int r = e / (2 * D), c = e % (2 * D);
+                const int gc = c >= D ? P.h_k * D + g * D + (c - D) : g * D + c;
+                Io<T>::store(cwin, (int64_t)r * C + gc, xr[(chunk + r) * LD + c]);
+            }
+        }
+        __syncthreads();   // the conv below overwrites staged rows
     }
     // ---- conv + SiLU in place, one channel per thread: y_t lands in row t,
     // which no later token of the channel reads.
@@ -645,7 +660,7 @@ template <int D, int CP, int KC, typename T>
 __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ v,
-    const float* __restrict__ conv_w, T* __restrict__ out) {
+    const float* __restrict__ conv_w, T* __restrict__ out, Ckpt ck) {
     using S = ScanLds<D, CP>;
     constexpr int NKS = D / 32;       // 32-wide k-steps over d_k
     constexpr int NT = CP / 16;       // token tiles
@@ -1006,6 +1021,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             publish_state();
             load_p(cn);
         }
+        // Checkpoint after a full chunk ending on a multiple of the interval:
+        // this block's state rows and its v channels' last conv_k-1 raw rows.
+        if (ck.every_chunks > 0 && (cc + 1) % ck.every_chunks == 0 && (cc + 1) * chunk <= len) {
+            const int m = (cc + 1) / ck.every_chunks - 1;
+            const int cs = m < ck.off[j + 1] - ck.off[j] ? ck.slots[ck.off[j] + m] : -1;
+            if (cs >= 0 && cs < P.n_slots) {
+                float* cb = P.state + (((int64_t)cs * P.n_layers + layer) * P.h_v + h) * (int64_t)D * D;
+                if (wave < NKS) {
+#pragma unroll
+                    for (int uu = 0; uu < 2; ++uu)
+                        *reinterpret_cast<float4*>(cb + (int64_t)(row0 + m16) * D + (2 * wave + uu) * 16 + q4 * 4) =
+                            make_float4(st[uu][0], st[uu][1], st[uu][2], st[uu][3]);
+                }
+                if (tid < (K - 1) * kRows) {
+                    const int r = tid / kRows, c = tid % kRows;
+                    T* cwin = reinterpret_cast<T*>(P.window) + ((int64_t)cs * P.n_layers + layer) * (int64_t)(K - 1) * C;
+                    Io<T>::store(cwin, (int64_t)r * C + gc0 + c, s_raw[buf * NRAW * kRows + (chunk + r) * kRows + c]);
+                }
+            }
+        }
         if (nxt) conv_v(cc + 1, buf ^ 1);
         fetch_raw(min(cc + 2, n_ch - 1));
         prefetch(ci0 + min(cc + 2, n_ch - 1));
@@ -1045,7 +1080,7 @@ template <int D, int CP, int KC, typename T>
 hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
                       const int32_t* cu, const int32_t* slot_ids, int total, int chunk, int mc,
                       const void* q, const void* k, const void* v, const float* a, const float* b,
-                      const float* conv_w, void* out, hipStream_t stream) {
+                      const float* conv_w, void* out, Ckpt ck, hipStream_t stream) {
     const PoolView& P = pool->view;
     static bool factor_lds = false, scan_lds = false;
     const size_t lf = factor_lds_bytes<D, CP>();
@@ -1060,12 +1095,12 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
                        stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
-                       static_cast<const T*>(k), a, b, conv_w);
+                       static_cast<const T*>(k), a, b, conv_w, ck);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<D, CP, KC, T>), dim3((D / kRows) * P.h_v * n_seq),
                        dim3(kThreads), ls, stream, P, W, layer, cu, slot_ids, chunk,
-                       static_cast<const T*>(v), conv_w, static_cast<T*>(out));
+                       static_cast<const T*>(v), conv_w, static_cast<T*>(out), ck);
     return hipGetLastError();
 }
 
@@ -1073,12 +1108,12 @@ template <int D, int KC, typename T>
 hipError_t launch_dk(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq, const int32_t* cu,
                      const int32_t* slot_ids, int total, int chunk, int mc, const void* q,
                      const void* k, const void* v, const float* a, const float* b,
-                     const float* conv_w, void* out, hipStream_t stream) {
+                     const float* conv_w, void* out, Ckpt ck, hipStream_t stream) {
     if (chunk == 64)
         return launch_all<D, 64, KC, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k,
-                                        v, a, b, conv_w, out, stream);
+                                        v, a, b, conv_w, out, ck, stream);
     return launch_all<D, 32, KC, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k, v,
-                                    a, b, conv_w, out, stream);
+                                    a, b, conv_w, out, ck, stream);
 }
 
 // conv_k = 4 (the common width) gets kernels with the taps fixed at compile
@@ -1087,12 +1122,12 @@ template <int D, typename T>
 hipError_t launch_d(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq, const int32_t* cu,
                     const int32_t* slot_ids, int total, int chunk, int mc, const void* q,
                     const void* k, const void* v, const float* a, const float* b,
-                    const float* conv_w, void* out, hipStream_t stream) {
+                    const float* conv_w, void* out, Ckpt ck, hipStream_t stream) {
     if (pool->view.conv_k == 4)
         return launch_dk<D, 4, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k, v, a,
-                                  b, conv_w, out, stream);
+                                  b, conv_w, out, ck, stream);
     return launch_dk<D, 0, T>(pool, W, layer, n_seq, cu, slot_ids, total, chunk, mc, q, k, v, a, b,
-                              conv_w, out, stream);
+                              conv_w, out, ck, stream);
 }
 
 }  // namespace
@@ -1108,7 +1143,7 @@ hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,
                           const int32_t* cu_seqlens, const int32_t* slot_ids,
                           int64_t total_tokens, int32_t chunk, const void* q, const void* k,
                           const void* v, const float* a, const float* b, const float* conv_w,
-                          void* out, void* workspace, hipStream_t stream) {
+                          void* out, void* workspace, Ckpt ck, hipStream_t stream) {
     const PoolView& P = pool->view;
     size_t bytes = 0;
     Ws W = carve(workspace, P, n_seq, total_tokens, chunk, &bytes);
@@ -1121,9 +1156,9 @@ hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,
 #define GDN_CASE(DD)                                                                             \
     case DD:                                                                                     \
         return bf ? launch_d<DD, uint16_t>(pool, W, layer, n_seq, cu_seqlens, slot_ids, total,   \
-                                           chunk, m, q, k, v, a, b, conv_w, out, stream)         \
+                                           chunk, m, q, k, v, a, b, conv_w, out, ck, stream)     \
                   : launch_d<DD, float>(pool, W, layer, n_seq, cu_seqlens, slot_ids, total,      \
-                                        chunk, m, q, k, v, a, b, conv_w, out, stream);
+                                        chunk, m, q, k, v, a, b, conv_w, out, ck, stream);
         GDN_CASE(32)
         GDN_CASE(64)
         GDN_CASE(128)

@@ -119,6 +119,16 @@ gdn_status gdn_pool_destroy(gdn_pool* pool);
  * adding the hybrid model Qwen3.5", table "What to do", row "State"). */
 gdn_status gdn_slot_reset(gdn_pool* pool, int32_t n, const int32_t* slot_ids, void* stream);
 
+/* Copy the state and conv window of every layer of slot src_ids[i] to slot
+ * dst_ids[i] (device int32[n] each), bit for bit: a state is saved and
+ * copied whole, e.g. from a prefill checkpoint into a new request's slot
+ * ("Project: adding the hybrid model Qwen3.5", prefix-cache notes: cache hits
+ * only where a state checkpoint was stored).  An entry with a negative id is
+ * skipped.  Destinations must be distinct and must not be sources of the same
+ * call (else the copies race; GDN_VALIDATE rejects it). */
+gdn_status gdn_slot_copy(gdn_pool* pool, int32_t n, const int32_t* src_ids, const int32_t* dst_ids,
+                         void* stream);
+
 /* One decode token for each of n entries; entry i reads and writes slot
  * slot_ids[i] of layer `layer` (baseRT issue #31, "Why this looks tractable":
  * a slot index in the recurrence kernels).  With few entries the rows of each
@@ -185,6 +195,29 @@ gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
                                const void* v, const float* a, const float* b,
                                const float* conv_w, void* out, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* gdn_prefill_chunked that also stores state checkpoints inside the
+ * sequences, for prefix caching (the pages: a cache hit is only possible
+ * where a state checkpoint was stored, and a state is copied whole).
+ *   ckpt_every    tokens between checkpoints, a positive multiple of `chunk`
+ *                 (0: none; the call is then gdn_prefill_chunked)
+ *   ckpt_offsets  device int32 [n_seq+1], from 0, non-decreasing: sequence j
+ *                 owns checkpoint rows [ckpt_offsets[j], ckpt_offsets[j+1])
+ *   ckpt_slots    device int32 [ckpt_offsets[n_seq]]: pool slots receiving them
+ * Checkpoint m of sequence j is written to slot ckpt_slots[ckpt_offsets[j]+m]
+ * for every m with (m+1)*ckpt_every <= its length and m below its row count:
+ * layer `layer`'s state and conv window after its first (m+1)*ckpt_every
+ * tokens, exactly what the sequence's own slot would hold had the sequence
+ * ended there (within the prefill's tolerance).  A negative checkpoint slot
+ * is skipped.  Checkpoint slots must differ from each other and from
+ * slot_ids (GDN_VALIDATE checks). */
+gdn_status gdn_prefill_chunked_ckpt(gdn_pool* pool, int32_t layer, int32_t n_seq,
+                                    const int32_t* cu_seqlens, const int32_t* slot_ids,
+                                    int64_t total_tokens, int32_t chunk, const void* q,
+                                    const void* k, const void* v, const float* a, const float* b,
+                                    const float* conv_w, void* out, int32_t ckpt_every,
+                                    const int32_t* ckpt_offsets, const int32_t* ckpt_slots,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronise `stream`, then read and clear the sticky device error word
  * (0 = none; bit 0 = a slot id >= n_slots was skipped; bit 1 = a malformed

@@ -79,6 +79,9 @@ def test_null_arguments_are_rejected_before_any_device_work(lib):
     assert lib.gdn_decode_step(nul, 0, 1, *([nul] * 9)) == -1
     assert lib.gdn_verify_step(nul, 0, 1, nul, 2, *([nul] * 9)) == -1
     assert lib.gdn_prefill_chunked(nul, 0, 1, nul, nul, 8, 64, *([nul] * 8), 0, nul) == -1
+    assert lib.gdn_prefill_chunked_ckpt(nul, 0, 1, nul, nul, 8, 64, *([nul] * 7), 64, nul, nul,
+                                        nul, 0, nul) == -1
+    assert lib.gdn_slot_copy(nul, 1, nul, nul, nul) == -1
     n = ctypes.c_size_t()
     assert lib.gdn_prefill_workspace_bytes(nul, 1, 8, 64, ctypes.byref(n)) == -1
     e = ctypes.c_int32()
