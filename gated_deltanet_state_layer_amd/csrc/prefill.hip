@@ -645,9 +645,14 @@ struct ScanLds {
 
 // Transposing LDS read (gfx950): lane 16g+j receives element j%4 of the four
 // bf16 at the address of lane 16g+4e+j/4, for e = 0..3.
+// XOR swizzle (in elements, a multiple of 4) of row `row` of the staged K^
+// planes: both the transposing reads and the 8-byte staging writes run at the
+// LDS's full rate with it (measured on gfx950 with 8 waves per CU: about 4
+// cycles per wave instruction, against 10 for the writes with a 16-element
+// swizzle and 13-40 unswizzled).
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
-    return (16 * ((row & 3) + 4 * ((row >> 3) & 1))) & (D - 16);
+    return (4 * ((row & 1) | (((row >> 3) & 1) << 1)) + 16 * ((row >> 1) & 7)) & (D - 4);
 }
 __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -723,13 +728,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     Frag fqk[2][NKS];      // Q and K fragments of token tile tw
     Frag ftt[NKC];         // T' fragments of token tile tw
     Frag fpp[NKC];         // P fragments of token tile tw
-    auto load_qk = [&](int ci) {
+    // qk = 0: Q^ (used in phase 2), 1: K^ (phase 1); each is refetched for
+    // the next chunk right after its last use.
+    auto load_qk = [&](int ci, int qk) {
         const bf16x8* base = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            fqk[0][ks] = load_frag(base, (0 * NT + tw) * NKS + ks, lane);
-            fqk[1][ks] = load_frag(base, (1 * NT + tw) * NKS + ks, lane);
-        }
+        for (int ks = 0; ks < NKS; ++ks) fqk[qk][ks] = load_frag(base, (qk * NT + tw) * NKS + ks, lane);
     };
     // T' and P fragments through a buffer descriptor over the (chunk, head)
     // block: the all-zero fragments above the diagonal (kc > tw/2) get an
@@ -864,7 +868,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         s_win[r * kRows + c] = Io<T>::load(win, (int64_t)r * C + gc0 + c);
     }
     for (int e = tid; e < 2 * NRAW * kRows; e += kThreads) s_raw[e] = 0.f;
-    load_qk(ci0);
+    load_qk(ci0, 1);
+    load_qk(ci0, 0);
     load_t(ci0);
     load_p(ci0);
     fetch_raw(0);
@@ -891,20 +896,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         const float* gb = s_g + buf * CP;
         const float glast = gb[CP - 1];
 
-        // (1) X_Q, X_K for token tile tw; XQ in registers; R to LDS.
+        // (1) X_K for token tile tw; R = V - diag(gamma) X_K to LDS.  (X_Q
+        // only feeds the output: it is computed in phase 2, where it fills
+        // the gaps of the short U chain.)
         f32x4 xq;
         {
-            Frag fa[2 * NKS], fb[2 * NKS];
-            f32x4 acc[2 * NKS];
+            Frag fb[NKS];
+            f32x4 acc[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const Frag bs = load_frag(s_stf, ks, lane);
-                fa[ks] = fqk[0][ks];
-                fa[NKS + ks] = fqk[1][ks];
-                fb[ks] = fb[NKS + ks] = bs;
-                acc[ks] = acc[NKS + ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+                fb[ks] = load_frag(s_stf, ks, lane);
+                acc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            mma3_n<2 * NKS>(acc, fa, fb);
+            mma3_n<NKS>(acc, fqk[1], fb);
             // K^ rows of this token tile into LDS in natural [token][d_k]
             // order (fragment elements 0-3 are d_k 32ks+4q.., 4-7 are +16).
             if (wave < NT) {
@@ -921,49 +925,57 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                     *reinterpret_cast<bf16x4*>(kl + c1) = __builtin_shufflevector(f.lo, f.lo, 4, 5, 6, 7);
                 }
             }
-            f32x4 aq = acc[0], ak = acc[NKS];
+            f32x4 ak = acc[0];
 #pragma unroll
-            for (int ks = 1; ks < NKS; ++ks) {
-                aq += acc[ks];
-                ak += acc[NKS + ks];
-            }
+            for (int ks = 1; ks < NKS; ++ks) ak += acc[ks];
             const float* vb = s_v + buf * CP * kRows;
             float r4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = tw * 16 + q4 * 4 + i;
-                const float gam = __expf(gb[t]);
-                xq[i] = gam * aq[i];
-                r4[i] = vb[t * kRows + m16] - gam * ak[i];
+                r4[i] = vb[t * kRows + m16] - __expf(gb[t]) * ak[i];
             }
             store_frag4(s_rf, tw >> 1, dst_lane, dst_e0, r4);
-            load_qk(cn);
+            load_qk(cn, 1);
         }
         __syncthreads();
 
-        // (2) U = T' R for token tile tw; U and the decayed U to LDS.
+        // (2) U = T' R for token tile tw (U and the decayed U to LDS),
+        //     interleaved with X_Q = Q S0^T (S0 is still the published state).
         {
-            Frag fr[NKC];
-            f32x4 acc[NKC];
+            constexpr int NJ = NKC + NKS;
+            Frag fa[NJ], fb[NJ];
+            f32x4 acc[NJ];
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
-                fr[kc] = load_frag(s_rf, kc, lane);
-                acc[kc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                fa[kc] = ftt[kc];
+                fb[kc] = load_frag(s_rf, kc, lane);
             }
-            mma3_n<NKC>(acc, ftt, fr);
-            f32x4 uv = acc[0];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                fa[NKC + ks] = fqk[0][ks];
+                fb[NKC + ks] = load_frag(s_stf, ks, lane);
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma3_n<NJ>(acc, fa, fb);
+            f32x4 uv = acc[0], aq = acc[NKC];
 #pragma unroll
             for (int kc = 1; kc < NKC; ++kc) uv += acc[kc];
+#pragma unroll
+            for (int ks = 1; ks < NKS; ++ks) aq += acc[NKC + ks];
             float u4[4], uu4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = tw * 16 + q4 * 4 + i;
                 u4[i] = uv[i];
                 uu4[i] = uv[i] * __expf(glast - gb[t]);
+                xq[i] = __expf(gb[t]) * aq[i];
             }
             store_frag4(s_uf, tw >> 1, dst_lane, dst_e0, u4);
             store_frag4(s_uuf, tw >> 1, dst_lane, dst_e0, uu4);
             load_t(cn);
+            load_qk(cn, 0);
         }
         if (nxt) store_raw(cc + 1, buf ^ 1, false);
         __syncthreads();
@@ -987,12 +999,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                     // K^T operand of state tile 2sw+uu (rows d_k 16(2sw+uu)+m,
                     // k = tokens 32kc+8q..): transpose reads of the staged K^.
                     // (rows r and r+4 share their swizzle: r % 8 < 4)
-                    const int kr = kc * 32 + q4 * 8 + (m16 >> 2);
-                    const int ko = kr * KRS + (((2 * sw + uu) * 16 + 4 * (m16 & 3)) ^ kswz<D>(kr));
+                    const int kr = kc * 32 + q4 * 8 + (m16 >> 2), kc0 = (2 * sw + uu) * 16 + 4 * (m16 & 3);
+                    const int ko0 = kr * KRS + (kc0 ^ kswz<D>(kr));
+                    const int ko1 = (kr + 4) * KRS + (kc0 ^ kswz<D>(kr + 4));
                     Frag kt;
-                    kt.hi = __builtin_shufflevector(lds_read_tr(s_kh + ko), lds_read_tr(s_kh + ko + 4 * KRS),
+                    kt.hi = __builtin_shufflevector(lds_read_tr(s_kh + ko0), lds_read_tr(s_kh + ko1),
                                                     0, 1, 2, 3, 4, 5, 6, 7);
-                    kt.lo = __builtin_shufflevector(lds_read_tr(s_kl + ko), lds_read_tr(s_kl + ko + 4 * KRS),
+                    kt.lo = __builtin_shufflevector(lds_read_tr(s_kl + ko0), lds_read_tr(s_kl + ko1),
                                                     0, 1, 2, 3, 4, 5, 6, 7);
                     fa[NKC + uu * NKC + kc] = kt;
                     fb[NKC + uu * NKC + kc] = uub;
