@@ -802,13 +802,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             if (r < K - 1 + CP) {
                 const int64_t p = t0 - (K - 1) + r;
                 const bool valid = p < t0 + L;
-                const bool from_win = first && p < s0;
+                float x[VN];
 #pragma unroll
-                for (int i = 0; i < VN; ++i) {
-                    float x = valid ? Vec<T>::at(rv[it], i) : 0.f;
-                    if (from_win) x = s_win[(K - 1 + (int)(p - s0)) * kRows + cv + i];
-                    dst[r * kRows + cv + i] = x;
+                for (int i = 0; i < VN; ++i) x[i] = valid ? Vec<T>::at(rv[it], i) : 0.f;
+                if (first && p < s0) {   // window rows before the sequence start
+#pragma unroll
+                    for (int i = 0; i < VN; ++i) x[i] = s_win[(K - 1 + (int)(p - s0)) * kRows + cv + i];
                 }
+#pragma unroll
+                for (int i = 0; i < VN; i += 4)
+                    *reinterpret_cast<float4*>(dst + r * kRows + cv + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
             }
         }
         if (tid < CP) s_g[buf * CP + tid] = rg;
@@ -820,17 +823,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     float wv[KM];
 #pragma unroll
     for (int m = 0; m < KM; ++m) wv[m] = m < K ? conv_w[(int64_t)(gc0 + cch) * K + m] : 0.f;
+    // One channel and TPT consecutive tokens per thread; the outputs are
+    // stored channel-major ([channel][token]) so phase 1 reads a lane's four
+    // tokens as one vector.
+    constexpr int TPT = CP / (kThreads / kRows);
+    static_assert(TPT == 2 || TPT == 4, "tokens per thread in the v conv");
     auto conv_v = [&](int cc, int buf) {
         const int L = min(chunk, len - cc * chunk);
         const float* src = s_raw + buf * NRAW * kRows;
         float* dst = s_v + buf * CP * kRows;
+        const int tt = (tid / kRows) * TPT;
+        float xr[TPT + KM - 1];
 #pragma unroll
-        for (int t = tid / kRows; t < CP; t += kThreads / kRows) {
+        for (int m = 0; m < TPT + KM - 1; ++m) xr[m] = src[(tt + m) * kRows + cch];
+        float y[TPT];
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
             float z = 0.f;
 #pragma unroll
-            for (int m = 0; m < KM; ++m) z = fmaf(wv[m], src[(t + m) * kRows + cch], z);
-            dst[t * kRows + cch] = t < L ? silu(z) : 0.f;
+            for (int m = 0; m < KM; ++m) z = fmaf(wv[m], xr[i + m], z);
+            y[i] = tt + i < L ? silu(z) : 0.f;
         }
+        if constexpr (TPT == 4)
+            *reinterpret_cast<float4*>(dst + cch * CP + tt) = make_float4(y[0], y[1], y[2], y[3]);
+        else
+            *reinterpret_cast<float2*>(dst + cch * CP + tt) = make_float2(y[0], y[1]);
     };
     // Publish this wave's state tiles as the B fragment of k-step sw.
     f32x4 st[2];
@@ -895,6 +912,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         const int64_t trel = (int64_t)cc * chunk;      // chunk start relative to s0
         const float* gb = s_g + buf * CP;
         const float glast = gb[CP - 1];
+        const float4 g4 = *reinterpret_cast<const float4*>(gb + tw * 16 + q4 * 4);   // this lane's 4 tokens
 
         // (1) X_K for token tile tw; R = V - diag(gamma) X_K to LDS.  (X_Q
         // only feeds the output: it is computed in phase 2, where it fills
@@ -928,13 +946,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             f32x4 ak = acc[0];
 #pragma unroll
             for (int ks = 1; ks < NKS; ++ks) ak += acc[ks];
-            const float* vb = s_v + buf * CP * kRows;
-            float r4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tw * 16 + q4 * 4 + i;
-                r4[i] = vb[t * kRows + m16] - __expf(gb[t]) * ak[i];
-            }
+            const float4 v4 = *reinterpret_cast<const float4*>(s_v + buf * CP * kRows + m16 * CP + tw * 16 + q4 * 4);
+            const float r4[4] = {v4.x - __expf(g4.x) * ak[0], v4.y - __expf(g4.y) * ak[1],
+                                 v4.z - __expf(g4.z) * ak[2], v4.w - __expf(g4.w) * ak[3]};
             store_frag4(s_rf, tw >> 1, dst_lane, dst_e0, r4);
             load_qk(cn, 1);
         }
@@ -965,12 +979,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
 #pragma unroll
             for (int ks = 1; ks < NKS; ++ks) aq += acc[NKC + ks];
             float u4[4], uu4[4];
+            const float gl4[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = tw * 16 + q4 * 4 + i;
                 u4[i] = uv[i];
-                uu4[i] = uv[i] * __expf(glast - gb[t]);
-                xq[i] = __expf(gb[t]) * aq[i];
+                uu4[i] = uv[i] * __expf(glast - gl4[i]);
+                xq[i] = __expf(gl4[i]) * aq[i];
             }
             store_frag4(s_uf, tw >> 1, dst_lane, dst_e0, u4);
             store_frag4(s_uuf, tw >> 1, dst_lane, dst_e0, uu4);
