@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     float* sP = sT + CP * LT;          // [CP][LT]
     constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
     constexpr int kMaxGroup = 4;                   // value heads per group kept in LDS
-    __shared__ float s_rq[CP], s_rk[CP], s_g[CP], s_b[CP];
+    __shared__ float s_g[CP], s_b[CP];
     __shared__ float s_la[kMaxGroup][CP], s_bb[kMaxGroup][CP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -324,26 +324,40 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     }
 
     // ---- stage the raw q|k rows with 16-byte loads: window rows before the
-    // sequence start, zeros past the chunk's valid tokens.
+    // sequence start, zeros past the chunk's valid tokens.  Every load of a
+    // thread is issued before the first is used (source pointer selected,
+    // position clamped into the chunk), so the staging costs one round trip.
     {
         const int nrow = K - 1 + CP;
         constexpr int vpr = 2 * D / VN;
-        for (int e = tid; e < nrow * vpr; e += kThreads) {
+        constexpr int NST = ((KM - 1 + CP) * vpr + kThreads - 1) / kThreads;
+        uint4 raw[NST];
+#pragma unroll
+        for (int it = 0; it < NST; ++it) {
+            const int e = min(tid + it * kThreads, nrow * vpr - 1);
             const int r = e / vpr, cv = (e % vpr) * VN;
             const bool isk = cv >= D;
             const int cc = isk ? cv - D : cv;
             const int64_t p = t0 - (K - 1) + r;
-            float x[VN];
-            if (p >= t0 + L) {
+            const int64_t pc = p >= t0 + L ? t0 + L - 1 : p;   // zeroed when stored
+            const T* src = pc >= s0
+                ? (isk ? k : q) + (pc * P.h_k + g) * D + cc
+                : win + (int64_t)(K - 1 + (pc - s0)) * C + (isk ? P.h_k * D : 0) + g * D + cc;
+            raw[it] = *reinterpret_cast<const uint4*>(src);
+        }
 #pragma unroll
-                for (int i = 0; i < VN; ++i) x[i] = 0.f;
-            } else if (p >= s0) {
-                Vec<T>::load(x, (isk ? k : q) + (p * P.h_k + g) * D + cc);
-            } else {
-                Vec<T>::load(x, win + (int64_t)(K - 1 + (p - s0)) * C + (isk ? P.h_k * D : 0) + g * D + cc);
+        for (int it = 0; it < NST; ++it) {
+            const int e = tid + it * kThreads;
+            if (e < nrow * vpr) {
+                const int r = e / vpr, cv = (e % vpr) * VN;
+                const bool valid = t0 - (K - 1) + r < t0 + L;
+                float x[VN];
+#pragma unroll
+                for (int i = 0; i < VN; ++i) x[i] = valid ? Vec<T>::at(raw[it], i) : 0.f;
+#pragma unroll
+                for (int i = 0; i < VN; i += 4)
+                    *reinterpret_cast<float4*>(xr + r * LD + cv + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
             }
-#pragma unroll
-            for (int i = 0; i < VN; ++i) xr[r * LD + cv + i] = x[i];
         }
     }
     __syncthreads();
@@ -401,31 +415,36 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     }
     __syncthreads();
 
-    // ---- per-token q/k norms (one wave per token).
-    for (int t = wave; t < CP; t += kThreads / 64) {
-        float sq = 0.f, sk = 0.f;
-        for (int c = lane; c < D; c += 64) {
-            const float x = xq[t * LD + c], y = xk[t * LD + c];
-            sq = fmaf(x, x, sq);
-            sk = fmaf(y, y, sk);
+    // ---- q/k normalisation: a quad of lanes per token (lane part p sums
+    // channels [p*D/4, (p+1)*D/4) of q and of k, the quad adds up), then the
+    // same lanes scale their channels in place.
+    {
+        const int t = wave * 16 + (lane >> 2), part = lane & 3;
+        constexpr int CPL = D / 4;
+        if (t < CP) {   // uniform per wave
+            float* rq_row = xq + t * LD + part * CPL;
+            float* rk_row = xk + t * LD + part * CPL;
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int j = 0; j < CPL; j += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(rq_row + j);
+                const float4 y = *reinterpret_cast<const float4*>(rk_row + j);
+                sq = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, sq))));
+                sk = fmaf(y.x, y.x, fmaf(y.y, y.y, fmaf(y.z, y.z, fmaf(y.w, y.w, sk))));
+            }
+            sq = group_sum<4>(sq);
+            sk = group_sum<4>(sk);
+            const float rq = P.q_scale / sqrtf(sq + P.eps), rk = 1.0f / sqrtf(sk + P.eps);
+#pragma unroll
+            for (int j = 0; j < CPL; j += 4) {
+                float4 x = *reinterpret_cast<const float4*>(rq_row + j);
+                float4 y = *reinterpret_cast<const float4*>(rk_row + j);
+                x.x *= rq; x.y *= rq; x.z *= rq; x.w *= rq;
+                y.x *= rk; y.y *= rk; y.z *= rk; y.w *= rk;
+                *reinterpret_cast<float4*>(rq_row + j) = x;
+                *reinterpret_cast<float4*>(rk_row + j) = y;
+            }
         }
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
-        if (lane == 0) {
-            s_rq[t] = P.q_scale / sqrtf(sq + P.eps);
-            s_rk[t] = 1.0f / sqrtf(sk + P.eps);
-        }
-    }
-    __syncthreads();
-    for (int e = tid; e < CP * D / 4; e += kThreads) {
-        const int t = e / (D / 4), c = (e % (D / 4)) * 4;
-        float4 x = *reinterpret_cast<float4*>(xq + t * LD + c);
-        float4 y = *reinterpret_cast<float4*>(xk + t * LD + c);
-        const float rq = s_rq[t], rk = s_rk[t];
-        x.x *= rq; x.y *= rq; x.z *= rq; x.w *= rq;
-        y.x *= rk; y.y *= rk; y.z *= rk; y.w *= rk;
-        *reinterpret_cast<float4*>(xq + t * LD + c) = x;
-        *reinterpret_cast<float4*>(xk + t * LD + c) = y;
     }
     __syncthreads();
 
