@@ -290,7 +290,8 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     float* sP = sT + CP * LT;          // [CP][LT]
     constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
     constexpr int kMaxGroup = 4;                   // value heads per group kept in LDS
-    __shared__ float s_g[CP], s_b[CP];
+    __shared__ __align__(16) float s_g[CP];
+    __shared__ __align__(16) float s_b[CP];
     __shared__ float s_la[kMaxGroup][CP], s_bb[kMaxGroup][CP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -510,18 +511,28 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             }
         }
         __syncthreads();
-        // A (strictly lower) and P (lower incl. diagonal) into LDS.
+        // A (strictly lower) and P (lower incl. diagonal) into LDS.  The lane's
+        // four rows share their g and b (one vector read each); blocks above
+        // the diagonal are plain zeros.
         if (ti < NT) {
+            const float4 gt4 = *reinterpret_cast<const float4*>(s_g + ti * 16 + q4 * 4);
+            const float4 bt4 = *reinterpret_cast<const float4*>(s_b + ti * 16 + q4 * 4);
+            const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w}, bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) {
+                const int s = jt * 16 + m16;          // column
+                const float gs = s_g[s];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = ti * 16 + q4 * 4 + r;   // row (later token)
-                    const int s = jt * 16 + m16;          // column
-                    const float dec = __expf(fminf(s_g[t] - s_g[s], 0.f));
-                    const bool low = jt <= ti && s <= t;
-                    sA[t * LT + s] = (low && s < t) ? s_b[t] * dec * kk[jt][r] : 0.f;
-                    sP[t * LT + s] = low ? qk[jt][r] * dec : 0.f;
+                    float av = 0.f, pv = 0.f;
+                    if (jt <= ti) {
+                        const float dec = __expf(fminf(gt[r] - gs, 0.f));
+                        av = s < t ? bt[r] * dec * kk[jt][r] : 0.f;
+                        pv = s <= t ? qk[jt][r] * dec : 0.f;
+                    }
+                    sA[t * LT + s] = av;
+                    sP[t * LT + s] = pv;
                 }
             }
         }
@@ -599,21 +610,22 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             }
             __syncthreads();
         }
-        // T' = T diag(b) (lower triangle incl. diagonal).
-        for (int e = tid; e < CP * CP; e += kThreads) {
-            const int t = e / CP, s = e % CP;
-            sT[t * LT + s] = (s <= t) ? sT[t * LT + s] * s_b[s] : 0.f;
-        }
-        __syncthreads();
-        // T' and P fragments: (tp, tile, kc), lane (m, q): row tile*16+m, cols
-        // 32kc+8q+e.  Both are lower triangular: fragments with kc > tile/2 are
-        // all zero and are not written (the scan never fetches them).
+        // T' = T diag(b) and P fragments: (tp, tile, kc), lane (m, q): row
+        // tile*16+m, cols 32kc+8q+e.  Both are lower triangular: fragments with
+        // kc > tile/2 are all zero and are not written (the scan never fetches
+        // them); inside the others T's upper part is masked here.
         bf16x8* gtp = W.tpf + ((int64_t)ci * P.h_v + hv) * NTP * kFragVecs;
         for (int f = wave; f < NTP; f += kThreads / 64) {
             const int tp = f / (NT * NKC), tile = (f / NKC) % NT, kc = f % NKC;
             if (kc > tile / 2) continue;
             float x[8];
             ld8(x, (tp ? sP : sT) + (tile * 16 + m16) * LT + kc * 32 + q4 * 8);
+            if (tp == 0) {
+                float bb[8];
+                ld8(bb, s_b + kc * 32 + q4 * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = kc * 32 + q4 * 8 + e <= tile * 16 + m16 ? x[e] * bb[e] : 0.f;
+            }
             store_frag(gtp, f, lane, split8(x));
         }
         if (tid < CP) W.gl[((int64_t)ci * P.h_v + hv) * CP + tid] = s_g[tid];
