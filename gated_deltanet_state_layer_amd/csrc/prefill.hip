@@ -130,7 +130,7 @@ struct Geom {
 struct Ws {
     int32_t* hdr;        // [0]: number of chunks, or -1 if cu_seqlens is malformed
     int32_t* seq_coff;   // [n_seq+1] first global chunk of each sequence
-    int32_t* chunk_seq;  // [max_chunks] sequence owning each chunk
+    int4* crec;          // [max_chunks][2] per chunk: {sequence, slot, s0, len}, {position, 0, 0, 0}
     bf16x8* qkf;         // [max_chunks][h_k][nqk fragments]
     bf16x8* tpf;         // [max_chunks][h_v][ntp fragments]; all-zero ones unwritten
     float* gl;           // [max_chunks][h_v][CP] cumulative log-decay in the chunk
@@ -162,7 +162,7 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
     };
     const size_t o_hdr = take(256);
     const size_t o_coff = take((size_t)(n_seq + 1) * 4);
-    const size_t o_cseq = take((size_t)mc * 4);
+    const size_t o_cseq = take((size_t)mc * 2 * sizeof(int4));
     const size_t o_qk = take((size_t)mc * P.h_k * gm.nqk() * fb);
     const size_t o_tp = take((size_t)mc * P.h_v * gm.ntp() * fb);
     const size_t o_g = take((size_t)mc * P.h_v * gm.CP * 4);
@@ -171,7 +171,7 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
     Ws w;
     w.hdr = reinterpret_cast<int32_t*>(b + o_hdr);
     w.seq_coff = reinterpret_cast<int32_t*>(b + o_coff);
-    w.chunk_seq = reinterpret_cast<int32_t*>(b + o_cseq);
+    w.crec = reinterpret_cast<int4*>(b + o_cseq);
     w.qkf = reinterpret_cast<bf16x8*>(b + o_qk);
     w.tpf = reinterpret_cast<bf16x8*>(b + o_tp);
     w.gl = reinterpret_cast<float*>(b + o_g);
@@ -181,14 +181,15 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
 // ------------------------------------------------------------------- prep
 
 // One workgroup: check cu_seqlens, count chunks per sequence, prefix-sum them
-// and record which sequence owns each chunk.  A malformed cu_seqlens marks
+// and write each chunk's record (its sequence, slot, start, length and
+// position), so a factor workgroup finds all of it with one load.  A malformed cu_seqlens marks
 // the workspace invalid (the other kernels then do nothing) and sets the
 // sticky error bit.
 constexpr int kPrepThreads = 1024;
 
 __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
-    PoolView P, Ws W, const int32_t* __restrict__ cu, int n_seq, int total, int chunk,
-    int max_chunks) {
+    PoolView P, Ws W, const int32_t* __restrict__ cu, const int32_t* __restrict__ slot_ids, int n_seq,
+    int total, int chunk, int max_chunks) {
     __shared__ int part[kPrepThreads];
     __shared__ int bad;
     const int tid = threadIdx.x;
@@ -224,8 +225,12 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     int c = part[tid] - cnt;  // exclusive prefix
     for (int j = j0; j < j1; ++j) {
         W.seq_coff[j] = c;
-        const int n = (cu[j + 1] - cu[j] + chunk - 1) / chunk;
-        for (int q = 0; q < n; ++q) W.chunk_seq[c + q] = j;
+        const int s = cu[j], n = (cu[j + 1] - s + chunk - 1) / chunk;
+        const int4 r0 = make_int4(j, slot_ids[j], s, cu[j + 1] - s);
+        for (int q = 0; q < n; ++q) {
+            W.crec[2 * (c + q)] = r0;
+            W.crec[2 * (c + q) + 1] = make_int4(q, 0, 0, 0);
+        }
         c += n;
     }
     if (tid == 0) {
@@ -297,31 +302,29 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
     const int ci = blockIdx.x, g = blockIdx.y;
+    const int4 rec0 = W.crec[2 * ci], rec1 = W.crec[2 * ci + 1];   // read with the count
     const int n_chunks = W.hdr[0];
     if (ci >= n_chunks) return;        // also when the workspace is invalid (-1)
-    const int j = W.chunk_seq[ci];
-    const int slot = slot_ids[j];
+    const int j = rec0.x, slot = rec0.y;
     if (slot < 0 || slot >= P.n_slots) return;
-    const int64_t s0 = cu[j];
-    const int len = cu[j + 1] - (int)s0;
-    const int cpos = ci - W.seq_coff[j];          // chunk index inside the sequence
+    const int64_t s0 = rec0.z;
+    const int len = rec0.w;
+    const int cpos = rec1.x;                      // chunk index inside the sequence
     const int64_t t0 = s0 + (int64_t)cpos * chunk;
     const int L = min(chunk, len - cpos * chunk); // valid tokens in this chunk
     const int K = KC > 0 ? KC : P.conv_k, C = P.c_conv, G = P.h_v / P.h_k;
     T* win = reinterpret_cast<T*>(P.window) + ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
 
     // ---- a and b of the chunk's tokens for every value head of the group,
-    // fetched with the staging loads (log a clamped; zero past L).
-    for (int e = tid; e < G * CP; e += kThreads) {
-        const int hl = e / CP, t = e % CP;
-        float la = 0.f, bt = 0.f;
-        if (t < L) {
-            const int64_t tok = t0 + t;
-            la = fmaxf(__logf(a[tok * P.h_v + g * G + hl]), kLogDecayMin);
-            bt = b[tok * P.h_v + g * G + hl];
-        }
-        s_la[hl][t] = la;
-        s_bb[hl][t] = bt;
+    // fetched with the staging loads (unconditional, positions clamped into
+    // the chunk; log a clamped; zero past L).  G * CP <= kThreads.
+    static_assert(kMaxGroup * 64 <= kThreads, "one a/b value per thread");
+    const int ab_hl = min(tid / CP, G - 1), ab_t = tid % CP;
+    float ab_a, ab_b;
+    {
+        const int64_t tok = t0 + min(ab_t, L - 1);
+        ab_a = a[tok * P.h_v + g * G + ab_hl];
+        ab_b = b[tok * P.h_v + g * G + ab_hl];
     }
 
     // ---- stage the raw q|k rows with 16-byte loads: window rows before the
@@ -332,19 +335,28 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         const int nrow = K - 1 + CP;
         constexpr int vpr = 2 * D / VN;
         constexpr int NST = ((KM - 1 + CP) * vpr + kThreads - 1) / kThreads;
+        static_assert(kThreads % vpr == 0, "a thread keeps its column across iterations");
+        constexpr int RPI = kThreads / vpr;               // rows per iteration
+        const int cv0 = (tid % vpr) * VN, r0 = tid / vpr;
+        const bool isk0 = cv0 >= D;
+        const int cc0 = isk0 ? cv0 - D : cv0;
+        const int64_t tstride = (int64_t)P.h_k * D;       // elements between tokens
+        const T* tok_base = (isk0 ? k : q) + t0 * tstride + g * D + cc0;   // token t0 of the column
+        const T* win_base = win + (isk0 ? P.h_k * D : 0) + g * D + cc0;
         uint4 raw[NST];
 #pragma unroll
         for (int it = 0; it < NST; ++it) {
-            const int e = min(tid + it * kThreads, nrow * vpr - 1);
-            const int r = e / vpr, cv = (e % vpr) * VN;
-            const bool isk = cv >= D;
-            const int cc = isk ? cv - D : cv;
-            const int64_t p = t0 - (K - 1) + r;
-            const int64_t pc = p >= t0 + L ? t0 + L - 1 : p;   // zeroed when stored
-            const T* src = pc >= s0
-                ? (isk ? k : q) + (pc * P.h_k + g) * D + cc
-                : win + (int64_t)(K - 1 + (pc - s0)) * C + (isk ? P.h_k * D : 0) + g * D + cc;
+            const int r = min(r0 + it * RPI, nrow - 1);
+            const int dt = min(r - (K - 1), L - 1);       // token offset from t0, clamped into the chunk
+            const int64_t p = t0 + dt;
+            const T* src = p >= s0 ? tok_base + (int64_t)dt * tstride
+                                   : win_base + (int64_t)(K - 1 + (int)(p - s0)) * C;
             raw[it] = *reinterpret_cast<const uint4*>(src);
+        }
+        // a/b arrive with the first staging loads; consume them only now
+        if (tid < G * CP) {
+            s_la[ab_hl][ab_t] = ab_t < L ? fmaxf(__logf(ab_a), kLogDecayMin) : 0.f;
+            s_bb[ab_hl][ab_t] = ab_t < L ? ab_b : 0.f;
         }
 #pragma unroll
         for (int it = 0; it < NST; ++it) {
@@ -1148,7 +1160,7 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
     e = allow_lds(&prefill_scan_kernel<D, CP, KC, T>, ls, &scan_lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, P, W, cu,
-                       n_seq, total, chunk, mc);
+                       slot_ids, n_seq, total, chunk, mc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
