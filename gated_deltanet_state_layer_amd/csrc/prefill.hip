@@ -190,7 +190,9 @@ constexpr int kPrepThreads = 1024;
 __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     PoolView P, Ws W, const int32_t* __restrict__ cu, const int32_t* __restrict__ slot_ids, int n_seq,
     int total, int chunk, int max_chunks) {
+    constexpr int kCoffLds = 4096;   // chunk offsets kept in LDS up to this many sequences
     __shared__ int part[kPrepThreads];
+    __shared__ int s_coff[kCoffLds + 1];
     __shared__ int bad;
     const int tid = threadIdx.x;
     if (tid == 0) bad = 0;
@@ -223,19 +225,31 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
         return;
     }
     int c = part[tid] - cnt;  // exclusive prefix
+    const bool in_lds = n_seq <= kCoffLds;
     for (int j = j0; j < j1; ++j) {
         W.seq_coff[j] = c;
-        const int s = cu[j], n = (cu[j + 1] - s + chunk - 1) / chunk;
-        const int4 r0 = make_int4(j, slot_ids[j], s, cu[j + 1] - s);
-        for (int q = 0; q < n; ++q) {
-            W.crec[2 * (c + q)] = r0;
-            W.crec[2 * (c + q) + 1] = make_int4(q, 0, 0, 0);
-        }
-        c += n;
+        if (in_lds) s_coff[j] = c;
+        c += (cu[j + 1] - cu[j] + chunk - 1) / chunk;
     }
     if (tid == 0) {
         W.seq_coff[n_seq] = n_chunks;
+        if (in_lds) s_coff[n_seq] = n_chunks;
         W.hdr[0] = n_chunks;
+    }
+    __syncthreads();
+    // Chunk records, one thread per chunk: the owning sequence is the j with
+    // coff[j] <= chunk < coff[j+1] (binary search; empty sequences own none).
+    for (int ch = tid; ch < n_chunks; ch += kPrepThreads) {
+        int lo = 0, hi = n_seq;   // coff[lo] <= ch < coff[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            const int v = in_lds ? s_coff[mid] : W.seq_coff[mid];
+            if (v <= ch) lo = mid;
+            else hi = mid;
+        }
+        const int s = cu[lo];
+        W.crec[2 * ch] = make_int4(lo, slot_ids[lo], s, cu[lo + 1] - s);
+        W.crec[2 * ch + 1] = make_int4(ch - (in_lds ? s_coff[lo] : W.seq_coff[lo]), 0, 0, 0);
     }
 }
 
