@@ -77,6 +77,8 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
     const int nch = (2 + G) * D;  // channels owned by this group
     int commit = n_tok;
     if (accept_len) commit = min(max(accept_len[i], 0), n_tok);
+    // Without outputs (commit only) the tokens after accept_len are not run.
+    const int t_end = NTOK > 0 ? NTOK : (out ? n_tok : commit);
 
     // ---- state tile mapping: each row split over LPR lanes, 8 columns per
     // lane (two 16-byte segments, D/2 apart); RPP rows per pass.
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
         const int hv = g * G + hl;
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(slot_state + (int64_t)hv * D * D, kTileBytes);
         if (r > 0) load_tile(rs);
-        for (int t = 0; t < n_tok; ++t) {
+        for (int t = 0; t < t_end; ++t) {
             const float* y = act + t * nch;
             const float rq = nrm[t * 3 + 0], rk = nrm[t * 3 + 1], kq = nrm[t * 3 + 2];
             float kc[8], qc[8];
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
     // ---- outputs: staged in LDS, written as 16-byte vectors (for each token
     // the group's G value heads are contiguous in `out`).
     __syncthreads();
-    {
+    if (out) {
         constexpr int VN = 16 / sizeof(T);
         const int nvec = n_tok * G * D / VN;
         for (int e = tid; e < nvec; e += nthr) {

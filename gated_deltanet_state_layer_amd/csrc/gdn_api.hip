@@ -218,14 +218,14 @@ gdn_status gdn_slot_reset(gdn_pool* pool, int32_t n, const int32_t* slot_ids, vo
 static gdn_status check_step_args(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
                                   int32_t n_tok, const void* q, const void* k, const void* v,
                                   const float* a, const float* b, const float* conv_w,
-                                  const void* out) {
+                                  const void* out, bool out_optional = false) {
     if (!pool) return GDN_ERR_INVALID_ARG;
     if (layer < 0 || layer >= pool->desc.n_layers || n < 0) return GDN_ERR_INVALID_ARG;
     if (n_tok < 1 || n_tok > kMaxVerifyTokens) return GDN_ERR_INVALID_ARG;
-    if (n > 0 && (!slot_ids || !q || !k || !v || !a || !b || !conv_w || !out))
+    if (n > 0 && (!slot_ids || !q || !k || !v || !a || !b || !conv_w || (!out && !out_optional)))
         return GDN_ERR_INVALID_ARG;
     if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
-    if (n > 0 && !aligned(out, 16)) return GDN_ERR_INVALID_ARG;  // 16-byte output vectors
+    if (n > 0 && out && !aligned(out, 16)) return GDN_ERR_INVALID_ARG;  // 16-byte output vectors
     if (decode_verify_lds_bytes(pool, n_tok) > kMaxLds) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
@@ -254,7 +254,7 @@ gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32
                            int32_t n_tok, const void* q, const void* k, const void* v,
                            const float* a, const float* b, const float* conv_w,
                            const int32_t* accept_len, void* out, void* stream) {
-    gdn_status st = check_step_args(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, out);
+    gdn_status st = check_step_args(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, out, true);
     if (st != GDN_OK) return st;
     if (n > 0 && !accept_len) return GDN_ERR_INVALID_ARG;
     if (n == 0) return GDN_OK;

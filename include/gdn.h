@@ -152,11 +152,16 @@ gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32
  * the slot untouched).  No per-position state copies are stored ("Plan
  * (research-based)", sections "What the research found" and "Why >150 is
  * still reachable": the per-position state is the costly part of verify).
+ * When acceptance is only known after sampling, call it twice: with
+ * accept_len all 0 for the outputs (the slots stay as they are), then with the
+ * sampled accept_len and out = NULL to commit (no outputs are written and
+ * tokens past accept_len are not run); drafts never touch the slot until
+ * they are accepted, as with the pages' output-only reconstruction.
  *   q, k       device io dtype [n][n_tok][h_k][d_k]
  *   v          device io dtype [n][n_tok][h_v][d_v]
  *   a, b       device fp32 [n][n_tok][h_v]
  *   accept_len device int32 [n]; values outside 0..n_tok are clamped
- *   out        device io dtype [n][n_tok][h_v][d_v] (16-byte aligned)
+ *   out        device io dtype [n][n_tok][h_v][d_v] (16-byte aligned), or NULL
  * Each position's output is bitwise the output of the same number of
  * gdn_decode_step calls. */
 gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,

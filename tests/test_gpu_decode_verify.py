@@ -271,6 +271,38 @@ def test_verify_is_bitwise_sequential_decode(n_tok):
     assert torch.equal(pv.window[idx], want_win)
 
 
+def test_verify_then_commit_after_sampling_equals_one_call():
+    """Acceptance known only after sampling: verify with accept_len 0 (the
+    outputs; slots untouched), then commit with the sampled accept_len and no
+    outputs.  Outputs, states and windows equal one verify call with that
+    accept_len, bitwise; a commit of 0 changes nothing."""
+    s, io, n_tok = syn.QWEN3_NEXT, "bf16", 4
+    say("verify, then commit")
+    rng = np.random.default_rng(70)
+    n, n_slots = 24, 40
+    ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
+    acc_np = (np.arange(n) % (n_tok + 1)).astype(np.int32)      # 0..4
+    w = dev(syn.draw_conv_weights(rng, s))
+    tok = syn.draw_tokens(rng, s, (n, n_tok), io)
+    td = tokens_to_dev(tok, io)
+    contents = syn.draw_pool_contents(88, ids_np, s, io)
+    pa, pb = make_pool(s, n_slots, io), make_pool(s, n_slots, io)
+    load_slots(pa, contents)
+    load_slots(pb, contents)
+    st0, wn0 = pb.state.clone(), pb.window.clone()
+    ids = dev(ids_np, torch.int32)
+    out_a = _verify(pa, 0, ids, n_tok, td, w, dev(acc_np, torch.int32))
+    out_b = _verify(pb, 0, ids, n_tok, td, w, dev(np.zeros(n, np.int32), torch.int32))
+    torch.cuda.synchronize()
+    assert torch.equal(pb.state, st0) and torch.equal(pb.window, wn0), "accept_len 0 touched a slot"
+    assert torch.equal(out_a, out_b)
+    pb.verify(0, ids, n_tok, td["q"], td["k"], td["v"], td["a"], td["b"], w,
+              dev(acc_np, torch.int32), None)
+    torch.cuda.synchronize()
+    assert torch.equal(pa.state, pb.state) and torch.equal(pa.window, pb.window)
+    assert pb.error() == 0
+
+
 def test_repeated_verify_rounds_match_oracle():
     """Several verify rounds with mixed acceptance on the same slots."""
     s, io = syn.Shapes(4, 8, 128, 128, 4), "bf16"
