@@ -43,6 +43,24 @@ DECODE_TRAFFIC = {"fetch_kib": 67794.5, "write_kib": 134768.0,
 DECODE_SRC_SHA256 = "08e24e0af70fe899cf5a9f07220e50a66bc30351c4fd003e372642c811c0726b"
 
 
+# Executed bf16 MFMA flops of the prefill kernels per token, from rocprofv3
+# counter runs (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, factor + scan, median
+# dispatch; profiles/prefill_mfma_counters.txt): the hi/lo bf16 split and the
+# padded tiles make them ~3.4x the algorithmic flops.  Valid for the prefill
+# source they were taken on (PREFILL_SRC_SHA256), else reported as null.
+PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
+                               "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
+PREFILL_SRC_SHA256 = "2e69d8ca8dc15a151b0085fb27b75add22221272986125b75ef0f4e9185f172d"
+
+
+def prefill_exec_flop_per_token(case):
+    import hashlib
+    src = os.path.join(ROOT, "gated_deltanet_state_layer_amd", "csrc", "prefill.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != PREFILL_SRC_SHA256:
+        return None
+    return PREFILL_MFMA_FLOP_PER_TOKEN.get(case)
+
+
 def decode_traffic_bytes():
     """Counter-based HBM bytes per decode launch, or None if unmeasured or stale."""
     import hashlib
@@ -309,6 +327,8 @@ def bench_prefill(args, torch, G, syn):
         res["single"] = {"workload": "one 8192-token sequence, chunk 64", "us": t1 * 1e6,
                          "tok_s": T / t1, "GBps": b / t1 / 1e9, "alg_TFLOPs": fl_tok * T / t1 / 1e12,
                          "mfma_frac_alg": fl_tok * T / t1 / 1e12 / BF16_PEAK_TFLOPS}
+        ex = prefill_exec_flop_per_token("single")
+        res["single"]["mfma_frac_exec"] = None if ex is None else ex * T / t1 / 1e12 / BF16_PEAK_TFLOPS
     if want("split512"):
         t16 = _time_prefill(args, torch, pool, [(c0, c0 + 512, [0, 512]) for c0 in range(0, T, 512)],
                             ids, d, w, out, C, reps)
@@ -333,6 +353,8 @@ def bench_prefill(args, torch, G, syn):
                      "us": tv * 1e6, "tok_s": Tv / tv, "GBps": bv / tv / 1e9,
                      "alg_TFLOPs": fl_tok * Tv / tv / 1e12,
                      "mfma_frac_alg": fl_tok * Tv / tv / 1e12 / BF16_PEAK_TFLOPS}
+    ex = prefill_exec_flop_per_token("varlen")
+    res["varlen"]["mfma_frac_exec"] = None if ex is None else ex * Tv / tv / 1e12 / BF16_PEAK_TFLOPS
     assert pool.error() == 0
     return res
 
