@@ -50,7 +50,7 @@ DECODE_SRC_SHA256 = "08e24e0af70fe899cf5a9f07220e50a66bc30351c4fd003e372642c811c
 # source they were taken on (PREFILL_SRC_SHA256), else reported as null.
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
-PREFILL_SRC_SHA256 = "2e69d8ca8dc15a151b0085fb27b75add22221272986125b75ef0f4e9185f172d"
+PREFILL_SRC_SHA256 = "563535a5180a8b3e128a9475a5d0dfb1450b11f531169ecf03df028901d3bad6"
 
 
 def prefill_exec_flop_per_token(case):

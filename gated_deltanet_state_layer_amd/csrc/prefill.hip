@@ -663,12 +663,12 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
 
 // One workgroup per (sequence, value head, block of 16 state rows), 256
 // threads, serial over the sequence's chunks.  Per chunk (three phases):
-//   1. wave w < CP/16 takes token tile w: X_Q = Q S0^T and X_K = K S0^T for
-//      its 16 tokens (B operand: the state block, published split in LDS),
-//      XQ = diag(gamma) X_Q stays in registers, R = V - diag(gamma) X_K goes
-//      to LDS as B fragments;
+//   1. wave w < CP/16 takes token tile w: X_K = K S0^T for its 16 tokens
+//      (B operand: the state block, published split in LDS), and
+//      R = V - diag(gamma) X_K goes to LDS as B fragments;
 //   2. U = T' R for the tile, published as B fragments with its decayed copy
-//      diag(exp(g_last - g)) U;
+//      diag(exp(g_last - g)) U; interleaved with it, X_Q = Q S0^T, and
+//      XQ = diag(gamma) X_Q stays in registers;
 //   3. O = XQ + P U for the tile is written out; wave w < D/32 updates state
 //      tiles 2w, 2w+1 of S^T (d_k x rows), S^T <- exp(g_last) S^T + K^T (decayed
 //      U), and republishes them.  K^T comes from the chunk's K^ rows, staged
