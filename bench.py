@@ -50,7 +50,7 @@ DECODE_SRC_SHA256 = "08e24e0af70fe899cf5a9f07220e50a66bc30351c4fd003e372642c811c
 # source they were taken on (PREFILL_SRC_SHA256), else reported as null.
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
-PREFILL_SRC_SHA256 = "563535a5180a8b3e128a9475a5d0dfb1450b11f531169ecf03df028901d3bad6"
+PREFILL_SRC_SHA256 = "6356880038620ba2528751444f6608042bd29eb63e6f9dad41e8a67fd56cfcbe"
 
 
 def prefill_exec_flop_per_token(case):
@@ -82,7 +82,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-verify", action="store_true")
-    p.add_argument("--only", choices=["decode", "verify", "prefill", "copy", "gemm"], default=None,
+    p.add_argument("--no-ring", action="store_true")
+    p.add_argument("--only", choices=["decode", "verify", "ring", "prefill", "copy", "gemm"],
+                   default=None,
                    help="run one workload only (for profiling)")
     p.add_argument("--prefill-case", choices=["single", "split512", "varlen", "all"], default="all",
                    help="prefill workloads to run (for profiling one of them)")
@@ -264,6 +266,89 @@ def bench_verify(args, torch, G, syn):
             "accepted_tok_s": float(case["accept_len"].sum()) / t}
 
 
+def ring_record_bytes(s):
+    """Bytes of one committed token in the verify ring: k^ per q/k head, v
+    per value head, a and b per value head (fp32)."""
+    return (s.h_k * s.d_k + s.h_v * s.d_v + 2 * s.h_v) * 4
+
+
+def bench_ring(args, torch, G, syn):
+    """Speculative decoding with acceptance known only after sampling, on
+    the verify ring (ring of 8 = twice the 4-token speculation): per cycle,
+    gdn_ring_verify (outputs) then gdn_ring_commit (the sampled accept_len).
+    Same slots, tokens and alternating 128-slot halves as the one-call verify
+    leg; beside it, the same cycle done with the one-call kernel (verify with
+    accept_len 0, then a commit-only call)."""
+    s = syn.QWEN3_NEXT
+    n_slots, N, n_tok, L = 256, 128, 4, 8
+    case = syn.verify_case()
+    tok = case["tokens"]
+    d = {n: torch.from_numpy(tok[n]).cuda() for n in "ab"}
+    d.update({n: torch.from_numpy(tok[n]).bfloat16().cuda() for n in "qkv"})
+    w = torch.from_numpy(case["conv_w"]).cuda()
+    perm = np.random.default_rng(7).permutation(n_slots).astype(np.int32)
+    ids = [torch.from_numpy(perm[:N].copy()).cuda(), torch.from_numpy(perm[N:].copy()).cuda()]
+    rng = np.random.default_rng(11)
+    accs_np = [rng.integers(1, n_tok + 1, size=N).astype(np.int32) for _ in range(8)]
+    accs = [torch.from_numpy(x).cuda() for x in accs_np]
+    zeros = torch.zeros(N, dtype=torch.int32, device="cuda")
+    out = torch.empty((N, n_tok, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    pool = G.Pool(G.make_desc(n_slots, 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16,
+                              ring_len=L))
+    pool.state.normal_(generator=torch.Generator(device="cuda").manual_seed(4321))
+
+    def cycle(i):
+        h, a_ = ids[i % 2], accs[(i // 2) % len(accs)]
+        pool.ring_verify(0, h, n_tok, d["q"], d["k"], d["v"], d["a"], d["b"], w, out)
+        pool.ring_commit(0, h, n_tok, d["q"], d["k"], d["v"], d["a"], d["b"], w, a_)
+
+    steps, warm = max(50, args.steps // 2), 20
+    t_cycle = time_launches(cycle, steps, warm, torch)
+    # ring fill at each verify and folds at each commit, replayed on the host
+    # for the same call sequence (warm-up cycles 0.., then timed cycles 0..)
+    cnt = [np.zeros(N, np.int64), np.zeros(N, np.int64)]
+    fill, folds, fold_fill, n_acc = 0, 0, 0, 0
+    for phase, n_cyc in (("warm", warm), ("timed", steps)):
+        for i in range(n_cyc):
+            c, a_ = cnt[i % 2], accs_np[(i // 2) % len(accs_np)]
+            f = c + a_ > L
+            if phase == "timed":
+                fill += int(c.sum())
+                folds += int(f.sum())
+                fold_fill += int((c + a_)[f].sum())
+                n_acc += int(a_.sum())
+            cnt[i % 2] = np.where(f, 0, c + a_)
+    # verify alone at the rings' final fill (repeatable: it writes nothing)
+    t_ver = time_launches(lambda i: pool.ring_verify(0, ids[i % 2], n_tok, d["q"], d["k"], d["v"],
+                                                    d["a"], d["b"], w, out), steps, 10, torch)
+    assert pool.error() == 0
+    rec = ring_record_bytes(s)
+    state = s.h_v * s.d_v * s.d_k * 4
+    per_ver = verify_bytes_per_slot(s, n_tok) - state - (s.conv_k - 1) * s.c_conv * 2  # no state or window write
+    ver_bytes = N * per_ver + int(cnt[0].sum() + cnt[1].sum()) // 2 * rec + s.c_conv * s.conv_k * 4
+    # the same cycle with the one-call kernel: outputs (accept_len 0), then commit only
+    plain = G.Pool(G.make_desc(n_slots, 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16))
+    plain.state.normal_(generator=torch.Generator(device="cuda").manual_seed(4321))
+
+    def split_cycle(i):
+        h, a_ = ids[i % 2], accs[(i // 2) % len(accs)]
+        plain.verify(0, h, n_tok, d["q"], d["k"], d["v"], d["a"], d["b"], w, zeros, out)
+        plain.verify(0, h, n_tok, d["q"], d["k"], d["v"], d["a"], d["b"], w, a_, None)
+
+    t_split = time_launches(split_cycle, steps, warm, torch)
+    assert plain.error() == 0
+    return {"workload": f"{N} slots x {n_tok} draft tokens, accept_len U{{1..{n_tok}}} after "
+                        f"sampling, ring of {L}",
+            "cycle_us": t_cycle * 1e6, "verify_us": t_ver * 1e6,
+            "commit_us": (t_cycle - t_ver) * 1e6,
+            "accepted_tok_s": n_acc / steps / t_cycle,
+            "fold_rate": folds / (steps * N),
+            "mean_ring_fill": fill / (steps * N),
+            "verify_GBps": ver_bytes / t_ver / 1e9,
+            "verify_hbm_frac": ver_bytes / t_ver / 1e9 / HBM_PEAK_GBPS,
+            "one_call_kernel_split_cycle_us": t_split * 1e6}
+
+
 def prefill_flops_per_token(s, C):
     """Algorithmic flops per token of the chunked form (2 per multiply-add,
     triangular products counted as triangles), per chunk divided by C:
@@ -424,6 +509,9 @@ def main():
     if args.only in (None, "verify") and not args.no_verify:
         res["verify"] = bench_verify(args, torch, G, syn)
         print(f"# verify done: {res['verify']['sec'] * 1e6:.1f} us", file=sys.stderr, flush=True)
+    if args.only in (None, "ring") and not args.no_ring:
+        res["ring"] = bench_ring(args, torch, G, syn)
+        print(f"# ring done: {res['ring']['cycle_us']:.1f} us/cycle", file=sys.stderr, flush=True)
     if args.only in (None, "prefill") and not args.no_prefill:
         res["prefill"] = bench_prefill(args, torch, G, syn)
         print("# prefill done", file=sys.stderr, flush=True)
@@ -469,6 +557,8 @@ def main():
                           "us": v["sec"] * 1e6, "tok_s": v["tok_s"],
                           "accepted_tok_s": v["accepted_tok_s"], "GBps": v["gbps"],
                           "hbm_frac": v["gbps"] / HBM_PEAK_GBPS}
+    if res.get("ring"):
+        line["verify_ring"] = res["ring"]
     if res.get("prefill"):
         line["prefill"] = res["prefill"]
     if res.get("copy"):

@@ -21,6 +21,7 @@ GDN_ERR_UNSUPPORTED = -2
 GDN_ERR_BAD_INDEX = -3
 GDN_ERR_WORKSPACE = -4
 GDN_ERR_HIP = -5
+GDN_ERR_RING = -6
 GDN_F32 = 0
 GDN_BF16 = 1
 GDN_VALIDATE = 1
@@ -28,8 +29,8 @@ GDN_VALIDATE = 1
 EXPORTED = (
     "gdn_pool_bytes", "gdn_pool_create", "gdn_pool_destroy", "gdn_slot_reset",
     "gdn_decode_step", "gdn_verify_step", "gdn_prefill_workspace_bytes",
-    "gdn_prefill_chunked", "gdn_prefill_chunked_ckpt", "gdn_slot_copy", "gdn_pool_error",
-    "gdn_status_string",
+    "gdn_prefill_chunked", "gdn_prefill_chunked_ckpt", "gdn_slot_copy", "gdn_ring_verify",
+    "gdn_ring_commit", "gdn_ring_flush", "gdn_pool_error", "gdn_status_string",
 )
 
 
@@ -46,7 +47,7 @@ class PoolDesc(ctypes.Structure):
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
         ("conv_k", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
         ("q_scale", ctypes.c_float), ("norm_eps", ctypes.c_float),
-        ("flags", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32), ("ring_len", ctypes.c_int32),
     ]
 
 
@@ -76,6 +77,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_prefill_chunked": [P, I32, I32, P, P, I64, I32, P, P, P, P, P, P, P, P, SZ, P],
         "gdn_prefill_chunked_ckpt": [P, I32, I32, P, P, I64, I32, P, P, P, P, P, P, P, I32, P, P,
                                      P, SZ, P],
+        "gdn_ring_verify": [P, I32, I32, P, I32, P, P, P, P, P, P, P, P],
+        "gdn_ring_commit": [P, I32, I32, P, I32, P, P, P, P, P, P, P, P],
+        "gdn_ring_flush": [P, I32, I32, P, P],
         "gdn_pool_error": [P, P, ctypes.POINTER(I32)],
     }
     for name, args in sig.items():
@@ -114,9 +118,26 @@ def _io_torch(io_dtype: int):
 
 
 def make_desc(n_slots, n_layers, h_k, h_v, d_k, d_v, conv_k, io_dtype=GDN_BF16,
-              q_scale=0.0, norm_eps=0.0, flags=0) -> PoolDesc:
+              q_scale=0.0, norm_eps=0.0, flags=0, ring_len=0) -> PoolDesc:
     return PoolDesc(n_slots, n_layers, h_k, h_v, d_k, d_v, conv_k, io_dtype,
-                    q_scale, norm_eps, flags)
+                    q_scale, norm_eps, flags, ring_len)
+
+
+def ring_layout(desc: PoolDesc):
+    """Byte offsets of the verify ring inside the aux buffer (the layout
+    include/gdn.h documents): (count offset, record offset, floats per
+    (slot, layer) record block), or None without a ring."""
+    if desc.ring_len == 0:
+        return None
+    up = lambda x, a: (x + a - 1) // a * a
+    io = 2 if desc.io_dtype == GDN_BF16 else 4
+    sl = desc.n_slots * desc.n_layers
+    c_conv = 2 * desc.h_k * desc.d_k + desc.h_v * desc.d_v
+    win = sl * (desc.conv_k - 1) * c_conv * io
+    cnt = up(win, 256) + 256 + up(sl * desc.h_k * 4, 256)
+    rec = cnt + 2 * up(sl * 4, 256)
+    stride = up(desc.ring_len * (desc.h_k * desc.d_k + desc.h_v * desc.d_v + 2 * desc.h_v), 64)
+    return cnt, rec, stride
 
 
 def pool_bytes(desc: PoolDesc):
@@ -153,6 +174,15 @@ class Pool:
         nwin = desc.n_slots * desc.n_layers * (desc.conv_k - 1) * self.c_conv
         self.window = self._aux_buf[: nwin * io_size].view(self.io_torch).view(
             desc.n_slots, desc.n_layers, desc.conv_k - 1, self.c_conv)
+        rl = ring_layout(desc)
+        self.ring_count = self.ring_records = None
+        if rl is not None:
+            cnt, rec, stride = rl
+            sl = desc.n_slots * desc.n_layers
+            self.ring_count = self._aux_buf[cnt: cnt + 4 * sl].view(torch.int32).view(
+                desc.n_slots, desc.n_layers)
+            self.ring_records = self._aux_buf[rec: rec + 4 * sl * stride].view(torch.float32).view(
+                desc.n_slots, desc.n_layers, stride)
 
     def close(self):
         if getattr(self, "_h", None):
@@ -190,6 +220,24 @@ class Pool:
                                    _ptr(accept_len), _ptr(out), _stream(stream)),
                "gdn_verify_step")
         return out
+
+    def ring_verify(self, layer, slot_ids, n_tok, q, k, v, a, b, conv_w, out, stream=None):
+        lib = load_library()
+        _check(lib.gdn_ring_verify(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), n_tok,
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
+                                   _ptr(out), _stream(stream)), "gdn_ring_verify")
+        return out
+
+    def ring_commit(self, layer, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len, stream=None):
+        lib = load_library()
+        _check(lib.gdn_ring_commit(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), n_tok,
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
+                                   _ptr(accept_len), _stream(stream)), "gdn_ring_commit")
+
+    def ring_flush(self, layer, slot_ids, stream=None):
+        lib = load_library()
+        _check(lib.gdn_ring_flush(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids),
+                                  _stream(stream)), "gdn_ring_flush")
 
     def prefill_workspace_bytes(self, n_seq, total_tokens, chunk):
         lib = load_library()

@@ -32,20 +32,46 @@ gdn_status check_desc(const gdn_pool_desc* d) {
         std::isinf(d->norm_eps))
         return GDN_ERR_INVALID_ARG;
     if (d->flags & ~GDN_VALIDATE) return GDN_ERR_INVALID_ARG;
+    if (d->ring_len < 0) return GDN_ERR_INVALID_ARG;
+    if (d->ring_len > kMaxRingSolve - kMaxVerifyTokens) return GDN_ERR_UNSUPPORTED;
     if (d->d_k != d->d_v) return GDN_ERR_UNSUPPORTED;
     if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return GDN_ERR_UNSUPPORTED;
     if (d->conv_k < 2 || d->conv_k > kMaxConvK) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
-void layout(const gdn_pool_desc* d, size_t* state_bytes, size_t* window_bytes, size_t* aux_bytes) {
+// Byte offsets inside the aux buffer (the layout documented in gdn.h).
+struct AuxLayout {
+    size_t window_bytes, meta, ctr, ring_cnt, ring_arr, ring, total;
+    int64_t ring_stride;   // floats per (slot, layer) ring block
+};
+
+AuxLayout aux_layout(const gdn_pool_desc* d) {
+    AuxLayout x{};
     const size_t io = d->io_dtype == GDN_BF16 ? 2 : 4;
     const size_t c_conv = 2 * (size_t)d->h_k * d->d_k + (size_t)d->h_v * d->d_v;
+    const size_t sl = (size_t)d->n_slots * d->n_layers;
+    x.window_bytes = sl * (d->conv_k - 1) * c_conv * io;
+    // windows | meta block (error word) | row-split decode counters | ring
+    x.meta = align_up(x.window_bytes, kAlign);
+    x.ctr = x.meta + kAlign;
+    x.total = x.ctr + align_up(sl * d->h_k * sizeof(int32_t), kAlign);
+    if (d->ring_len > 0) {
+        const size_t per_tok = (size_t)d->h_k * d->d_k + (size_t)d->h_v * d->d_v + 2 * (size_t)d->h_v;
+        x.ring_stride = (int64_t)align_up(d->ring_len * per_tok, 64);
+        x.ring_cnt = x.total;
+        x.ring_arr = x.ring_cnt + align_up(sl * sizeof(int32_t), kAlign);
+        x.ring = x.ring_arr + align_up(sl * sizeof(int32_t), kAlign);
+        x.total = x.ring + sl * x.ring_stride * sizeof(float);
+    }
+    return x;
+}
+
+void layout(const gdn_pool_desc* d, size_t* state_bytes, size_t* window_bytes, size_t* aux_bytes) {
     *state_bytes = (size_t)d->n_slots * d->n_layers * d->h_v * d->d_v * d->d_k * sizeof(float);
-    *window_bytes = (size_t)d->n_slots * d->n_layers * (d->conv_k - 1) * c_conv * io;
-    // windows | meta block (error word) | row-split decode counters
-    *aux_bytes = align_up(*window_bytes, kAlign) + kAlign +
-                 align_up((size_t)d->n_slots * d->n_layers * d->h_k * sizeof(int32_t), kAlign);
+    const AuxLayout x = aux_layout(d);
+    *window_bytes = x.window_bytes;
+    *aux_bytes = x.total;
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -107,6 +133,23 @@ gdn_status host_check_ckpt(const int32_t* slot_ids, int32_t n_seq, const int32_t
     return GDN_OK;
 }
 
+// GDN_VALIDATE for the one-call path on a ring pool: every listed slot's ring
+// for `layer` must be empty (the call reads and writes the state tile).
+gdn_status host_check_rings_empty(const gdn_pool* pool, int32_t layer, const int32_t* ids,
+                                  int32_t n, hipStream_t s) {
+    if (pool->desc.ring_len == 0 || n == 0) return GDN_OK;
+    const size_t sl = (size_t)pool->desc.n_slots * pool->desc.n_layers;
+    std::vector<int32_t> h(n), cnt(sl);
+    if (hipMemcpyAsync(h.data(), ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(cnt.data(), pool->view.ring_cnt, sl * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return GDN_ERR_HIP;
+    for (int32_t x : h)
+        if (x >= 0 && x < pool->desc.n_slots && cnt[(size_t)x * pool->desc.n_layers + layer] != 0)
+            return GDN_ERR_RING;
+    return GDN_OK;
+}
+
 gdn_status prefill_common(gdn_pool* pool, int32_t layer, int32_t n_seq, const int32_t* cu_seqlens,
                           const int32_t* slot_ids, int64_t total_tokens, int32_t chunk,
                           const void* q, const void* k, const void* v, const float* a,
@@ -135,6 +178,15 @@ gdn_status prefill_common(gdn_pool* pool, int32_t layer, int32_t n_seq, const in
                             : host_check_ids(slot_ids, n_seq, pool->desc.n_slots, s);
         if (st != GDN_OK) return st;
         st = host_check_seqlens(cu_seqlens, n_seq, total_tokens, s);
+        if (st != GDN_OK) return st;
+        st = host_check_rings_empty(pool, layer, slot_ids, n_seq, s);
+        if (st == GDN_OK && ckpt_every > 0) {
+            int32_t n_ck = 0;
+            if (hipMemcpyAsync(&n_ck, ckpt_offsets + n_seq, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+                hipStreamSynchronize(s) != hipSuccess)
+                return GDN_ERR_HIP;
+            st = host_check_rings_empty(pool, layer, ckpt_slots, n_ck, s);
+        }
         if (st != GDN_OK) return st;
     }
     const Ckpt ck{ckpt_every / chunk, ckpt_offsets, ckpt_slots};
@@ -176,8 +228,15 @@ gdn_status gdn_pool_create(const gdn_pool_desc* desc, void* state_buf, void* aux
     PoolView& v = p->view;
     v.state = static_cast<float*>(state_buf);
     v.window = aux_buf;
-    v.err = reinterpret_cast<int32_t*>(static_cast<char*>(aux_buf) + align_up(p->window_bytes, kAlign));
-    v.ctr = reinterpret_cast<int32_t*>(static_cast<char*>(aux_buf) + align_up(p->window_bytes, kAlign) + kAlign);
+    const AuxLayout ax = aux_layout(desc);
+    char* aux = static_cast<char*>(aux_buf);
+    v.err = reinterpret_cast<int32_t*>(aux + ax.meta);
+    v.ctr = reinterpret_cast<int32_t*>(aux + ax.ctr);
+    v.ring_len = desc->ring_len;
+    v.ring_cnt = desc->ring_len > 0 ? reinterpret_cast<int32_t*>(aux + ax.ring_cnt) : nullptr;
+    v.ring_arr = desc->ring_len > 0 ? reinterpret_cast<int32_t*>(aux + ax.ring_arr) : nullptr;
+    v.ring = desc->ring_len > 0 ? reinterpret_cast<float*>(aux + ax.ring) : nullptr;
+    v.ring_stride = ax.ring_stride;
     v.n_slots = desc->n_slots;
     v.n_layers = desc->n_layers;
     v.h_k = desc->h_k;
@@ -238,6 +297,7 @@ gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32
     hipStream_t s = as_stream(stream);
     if (pool->desc.flags & GDN_VALIDATE) {
         st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+        if (st == GDN_OK) st = host_check_rings_empty(pool, layer, slot_ids, n, s);
         if (st != GDN_OK) return st;
     }
     // Few entries: split each head's rows over several workgroups so that
@@ -261,6 +321,7 @@ gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32
     hipStream_t s = as_stream(stream);
     if (pool->desc.flags & GDN_VALIDATE) {
         st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+        if (st == GDN_OK) st = host_check_rings_empty(pool, layer, slot_ids, n, s);
         if (st != GDN_OK) return st;
     }
     return launch_decode_verify(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len,
@@ -326,6 +387,54 @@ gdn_status gdn_slot_copy(gdn_pool* pool, int32_t n, const int32_t* src_ids,
     return launch_slot_copy(pool, n, src_ids, dst_ids, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+static gdn_status ring_call(gdn_pool* pool, RingOp op, int32_t layer, int32_t n,
+                            const int32_t* slot_ids, int32_t n_tok, const void* q, const void* k,
+                            const void* v, const float* a, const float* b, const float* conv_w,
+                            const int32_t* accept_len, void* out, void* stream) {
+    if (!pool || layer < 0 || layer >= pool->desc.n_layers || n < 0) return GDN_ERR_INVALID_ARG;
+    if (pool->desc.ring_len == 0) return GDN_ERR_UNSUPPORTED;
+    if (op != RingOp::kFlush) {
+        if (n_tok < 1 || n_tok > kMaxVerifyTokens) return GDN_ERR_INVALID_ARG;
+        if (pool->desc.ring_len + n_tok > kMaxRingSolve) return GDN_ERR_UNSUPPORTED;
+        if (n > 0 && (!q || !k || !v || !a || !b || !conv_w)) return GDN_ERR_INVALID_ARG;
+        if (n > 0 && op == RingOp::kVerify && !out) return GDN_ERR_INVALID_ARG;
+        if (n > 0 && op == RingOp::kCommit && !accept_len) return GDN_ERR_INVALID_ARG;
+    }
+    if (n > 0 && !slot_ids) return GDN_ERR_INVALID_ARG;
+    if (n == 0) return GDN_OK;
+    hipStream_t s = as_stream(stream);
+    if (pool->desc.flags & GDN_VALIDATE) {
+        const gdn_status st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+        if (st != GDN_OK) return st;
+    }
+    const hipError_t e = launch_ring(pool, op, layer, n, slot_ids, op == RingOp::kFlush ? 0 : n_tok,
+                                     q, k, v, a, b, conv_w, accept_len, out, s);
+    if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_ring_verify(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                           int32_t n_tok, const void* q, const void* k, const void* v,
+                           const float* a, const float* b, const float* conv_w, void* out,
+                           void* stream) {
+    return ring_call(pool, RingOp::kVerify, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w,
+                     nullptr, out, stream);
+}
+
+gdn_status gdn_ring_commit(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                           int32_t n_tok, const void* q, const void* k, const void* v,
+                           const float* a, const float* b, const float* conv_w,
+                           const int32_t* accept_len, void* stream) {
+    return ring_call(pool, RingOp::kCommit, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w,
+                     accept_len, nullptr, stream);
+}
+
+gdn_status gdn_ring_flush(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                          void* stream) {
+    return ring_call(pool, RingOp::kFlush, layer, n, slot_ids, 0, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
 gdn_status gdn_pool_error(gdn_pool* pool, void* stream, int32_t* device_error) {
     if (!pool || !device_error) return GDN_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
@@ -349,6 +458,7 @@ const char* gdn_status_string(gdn_status status) {
         case GDN_ERR_BAD_INDEX: return "slot id out of range or repeated, or malformed cu_seqlens";
         case GDN_ERR_WORKSPACE: return "prefill workspace too small";
         case GDN_ERR_HIP: return "HIP runtime error";
+        case GDN_ERR_RING: return "a listed slot's verify ring is not empty (flush it first)";
         default: return "unknown status";
     }
 }

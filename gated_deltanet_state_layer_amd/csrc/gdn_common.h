@@ -75,7 +75,17 @@ struct PoolView {
     float* state;         // [n_slots][n_layers][h_v][d_v][d_k]
     void* window;         // [n_slots][n_layers][conv_k-1][C_conv] io dtype
     int32_t* err;         // sticky error word
-    int32_t* ctr;         // [n_slots][n_layers][h_k] row-split decode counters (0 between calls)
+    int32_t* ctr;         // [n_slots][n_layers][h_k] arrival counters of the row-split decode
+                          // and the ring commit (0 between calls)
+    // verify ring (ring_len > 0): committed-token count per (slot, layer), the
+    // ring commit's per-slot group counters (0 between calls) and the token records,
+    // ring_stride floats per (slot, layer): k^ [L][h_k][d], v [L][h_v][d],
+    // a [L][h_v], b [L][h_v]
+    int32_t* ring_cnt;
+    int32_t* ring_arr;
+    float* ring;
+    int64_t ring_stride;
+    int32_t ring_len;
     int32_t n_slots, n_layers, h_k, h_v, d, conv_k, c_conv;
     float q_scale, eps;
 };
@@ -118,6 +128,13 @@ hipError_t launch_decode_rows(const gdn_pool* pool, int nrb, int32_t layer, int3
                               const int32_t* slot_ids, const void* q, const void* k, const void* v,
                               const float* a, const float* b, const float* conv_w, void* out,
                               hipStream_t stream);
+// Verify ring (pools with ring_len > 0).
+constexpr int kMaxRingSolve = 32;   // ring_len + n_tok
+enum class RingOp { kVerify, kCommit, kFlush };
+hipError_t launch_ring(const gdn_pool* pool, RingOp op, int32_t layer, int32_t n,
+                       const int32_t* slot_ids, int32_t n_tok, const void* q, const void* k,
+                       const void* v, const float* a, const float* b, const float* conv_w,
+                       const int32_t* accept_len, void* out, hipStream_t stream);
 size_t prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
                                int32_t chunk);
 hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,

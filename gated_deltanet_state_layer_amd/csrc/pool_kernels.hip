@@ -15,7 +15,7 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float4* p, size_t n
 }
 
 // A reused request slot starts from zero: clear its state tiles and conv
-// windows for every layer ("Project: adding the hybrid model Qwen3.5",
+// windows and empty its verify rings for every layer ("Project: adding the hybrid model Qwen3.5",
 // "What to do", row "State").  grid = (blocks per slot, n entries).
 __global__ __launch_bounds__(kThreads) void slot_reset_kernel(PoolView P, const int32_t* slot_ids,
                                                              size_t state16_per_slot,
@@ -32,10 +32,13 @@ __global__ __launch_bounds__(kThreads) void slot_reset_kernel(PoolView P, const 
     const size_t stride = (size_t)gridDim.x * kThreads;
     for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < state16_per_slot; j += stride) st[j] = z;
     for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < window16_per_slot; j += stride) wn[j] = z;
+    // an empty verify ring (its records need no clearing)
+    if (P.ring_len > 0 && blockIdx.x == 0)
+        for (int l = threadIdx.x; l < P.n_layers; l += kThreads) P.ring_cnt[(int64_t)slot * P.n_layers + l] = 0;
 }
 
-// Copy the state tiles and conv windows of every layer of slot src_ids[i]
-// to slot dst_ids[i] (a state "saved and copied whole": "Project: adding the
+// Copy the state tiles, conv windows and verify rings of every layer of slot
+// src_ids[i] to slot dst_ids[i] (a state "saved and copied whole": "Project: adding the
 // hybrid model Qwen3.5", prefix-cache notes).  grid = (blocks per slot, n).
 __global__ __launch_bounds__(kThreads) void slot_copy_kernel(PoolView P, const int32_t* src_ids,
                                                             const int32_t* dst_ids,
@@ -54,6 +57,15 @@ __global__ __launch_bounds__(kThreads) void slot_copy_kernel(PoolView P, const i
     const size_t stride = (size_t)gridDim.x * kThreads;
     for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < state16_per_slot; j += stride) sd[j] = ss[j];
     for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < window16_per_slot; j += stride) wd[j] = ws[j];
+    if (P.ring_len > 0) {   // the verify ring: counts and records of every layer
+        const size_t ring16 = (size_t)P.n_layers * P.ring_stride / 4;
+        const float4* rs = reinterpret_cast<const float4*>(P.ring) + (size_t)src * ring16;
+        float4* rd = reinterpret_cast<float4*>(P.ring) + (size_t)dst * ring16;
+        for (size_t j = (size_t)blockIdx.x * kThreads + threadIdx.x; j < ring16; j += stride) rd[j] = rs[j];
+        if (blockIdx.x == 0)
+            for (int l = threadIdx.x; l < P.n_layers; l += kThreads)
+                P.ring_cnt[(int64_t)dst * P.n_layers + l] = P.ring_cnt[(int64_t)src * P.n_layers + l];
+    }
 }
 
 }  // namespace

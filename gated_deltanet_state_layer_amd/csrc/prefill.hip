@@ -27,58 +27,16 @@
 // transposed K^ of the state update is read from LDS with the gfx950
 // transposing load instead of being stored twice.
 #include "gdn_common.h"
+#include "mfma_split.h"
 
 namespace gdn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRows = 16;          // state rows (d_v) per scan workgroup
 constexpr float kLogDecayMin = -87.f;
 
 // ------------------------------------------------------------ MFMA helpers
-
-// One lane's share of a 16x16x32 bf16 MFMA operand, split as hi + lo.
-// Lane l = 16 q + m of an A operand holds row m, k = 8q..8q+7; of a B operand
-// column m, k = 8q..8q+7; the fp32 result holds rows 4q..4q+3 of column m.
-struct Frag {
-    bf16x8 hi, lo;
-};
-
-__device__ __forceinline__ Frag split8(const float* x) {
-    Frag r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const __bf16 h = (__bf16)x[j];
-        r.hi[j] = h;
-        r.lo[j] = (__bf16)(x[j] - (float)h);
-    }
-    return r;
-}
-
-// acc += A * B for one 16x16x32 tile.
-__device__ __forceinline__ f32x4 mma3(f32x4 acc, const Frag& a, const Frag& b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
-    return acc;
-}
-
-// acc[j] += a[j] * b[j] for N independent tiles, with the three hi/lo products
-// of all tiles interleaved so that consecutive MFMAs never depend on each
-// other (a dependent MFMA would wait for the previous one to drain).
-template <int N>
-__device__ __forceinline__ void mma3_n(f32x4* acc, const Frag* a, const Frag* b) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j].lo, b[j].hi, acc[j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < N; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j].hi, b[j].lo, acc[j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < N; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j].hi, b[j].hi, acc[j], 0, 0, 0);
-}
 
 // Fragment buffers: [fragment][hi | lo][64 lanes] of 16-byte vectors, 2 KiB
 // per fragment, so a wave reads or writes one half in one coalesced 1 KiB.
@@ -107,15 +65,6 @@ __device__ __forceinline__ void store_frag4(bf16x8* base, int f, int dl, int e0,
     *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base + f * kFragVecs + dl) + e0) = h;
     *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base + f * kFragVecs + 64 + dl) + e0) = l;
 }
-
-__device__ __forceinline__ void ld4x2(float* dst, const float* lo, const float* hi) {
-    const float4 x0 = *reinterpret_cast<const float4*>(lo);
-    const float4 x1 = *reinterpret_cast<const float4*>(hi);
-    dst[0] = x0.x; dst[1] = x0.y; dst[2] = x0.z; dst[3] = x0.w;
-    dst[4] = x1.x; dst[5] = x1.y; dst[6] = x1.z; dst[7] = x1.w;
-}
-
-__device__ __forceinline__ void ld8(float* dst, const float* src) { ld4x2(dst, src, src + 4); }
 
 // --------------------------------------------------------------- workspace
 

@@ -51,8 +51,15 @@
  *       the order q heads | k heads | v heads, each head's d contiguous),
  *       then, at the next 256-byte boundary, a 256-byte meta block whose
  *       first int32 is the sticky device error word, then int32
- *       [n_slots][n_layers][h_k] counters of the low-batch decode path
- *       (zero between calls; zeroed by gdn_pool_create).
+ *       [n_slots][n_layers][h_k] counters of the low-batch decode path and
+ *       the ring commit (zero between calls; zeroed by gdn_pool_create).
+ *     With ring_len = L > 0 (see gdn_ring_verify), then, each at the next
+ *     256-byte boundary: int32 [n_slots][n_layers] ring counts (tokens held,
+ *     0..L), int32 [n_slots][n_layers] ring-commit counters (zero between
+ *     calls), and fp32 ring records, one block per (slot, layer) of
+ *     L*(h_k*d_k + h_v*d_v + 2*h_v) floats rounded up to a multiple of 64:
+ *     k^ [L][h_k][d_k] (post conv, normalised), v [L][h_v][d_v] (post conv),
+ *     a [L][h_v], b [L][h_v].
  *
  * Activations: per token, raw q, k are [h_k][d_k] and v is [h_v][d_v] in the
  * io dtype; a and b are [h_v] fp32, already activated (a in (0,1], b in
@@ -78,6 +85,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_BAD_INDEX (-3)   /* GDN_VALIDATE: slot id out of range or repeated */
 #define GDN_ERR_WORKSPACE (-4)   /* prefill workspace too small */
 #define GDN_ERR_HIP (-5)         /* a HIP runtime call failed */
+#define GDN_ERR_RING (-6)        /* GDN_VALIDATE: a listed slot's verify ring is not empty */
 
 typedef int32_t gdn_dtype;
 #define GDN_F32 0
@@ -98,6 +106,7 @@ typedef struct {
     float q_scale;     /* multiplies the normalised q; 0 -> 1/sqrt(d_k) */
     float norm_eps;    /* eps in x/sqrt(|x|^2+eps); 0 -> 1e-6 */
     uint32_t flags;    /* GDN_VALIDATE or 0 */
+    int32_t ring_len;  /* tokens of the verify ring per slot and layer, 0..24 (0: no ring) */
 } gdn_pool_desc;
 
 /* Bytes the caller must allocate for a pool with this descriptor: the fp32
@@ -114,13 +123,14 @@ gdn_status gdn_pool_create(const gdn_pool_desc* desc, void* state_buf, void* aux
 /* Free the host handle (device buffers are the caller's). */
 gdn_status gdn_pool_destroy(gdn_pool* pool);
 
-/* Zero the state and conv window of every layer of the n listed slots
- * (slot_ids: device int32[n]); a reused slot starts from zero ("Project:
- * adding the hybrid model Qwen3.5", table "What to do", row "State"). */
+/* Zero the state and conv window of every layer of the n listed slots, and
+ * empty their verify rings (slot_ids: device int32[n]); a reused slot starts
+ * from zero ("Project: adding the hybrid model Qwen3.5", table "What to do",
+ * row "State"). */
 gdn_status gdn_slot_reset(gdn_pool* pool, int32_t n, const int32_t* slot_ids, void* stream);
 
-/* Copy the state and conv window of every layer of slot src_ids[i] to slot
- * dst_ids[i] (device int32[n] each), bit for bit: a state is saved and
+/* Copy the state, conv window and verify ring of every layer of slot
+ * src_ids[i] to slot dst_ids[i] (device int32[n] each), bit for bit: a state is saved and
  * copied whole, e.g. from a prefill checkpoint into a new request's slot
  * ("Project: adding the hybrid model Qwen3.5", prefix-cache notes: cache hits
  * only where a state checkpoint was stored).  An entry with a negative id is
@@ -223,6 +233,50 @@ gdn_status gdn_prefill_chunked_ckpt(gdn_pool* pool, int32_t layer, int32_t n_seq
                                     const float* conv_w, void* out, int32_t ckpt_every,
                                     const int32_t* ckpt_offsets, const int32_t* ckpt_slots,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Verify ring ("Plan (research-based): Qwen3.6-35B-A3B", section "What the
+ * research found": an output-only reconstruction from a ring of recent
+ * tokens with the chunked (I+A)^-1 form, the full state written only every
+ * L tokens).  For pools created with ring_len = L > 0.  A slot's state tile
+ * then holds the state as of its last flush, and the ring the post-conv
+ * k^, v, a, b of the c <= L tokens committed since; the slot's logical state
+ * is the tile advanced by those tokens (its conv window is always current).
+ * The one-call path (gdn_decode_step, gdn_verify_step, gdn_prefill_*,
+ * checkpoints) reads and writes the tile directly, so a slot must have an
+ * empty ring when passed to it: call gdn_ring_flush first (GDN_VALIDATE
+ * returns GDN_ERR_RING otherwise).  Reset empties a ring; copy copies it.
+ *
+ * gdn_ring_verify: outputs of n_tok draft tokens (1..8, ring_len + n_tok <=
+ * 32) for each entry, as if they were decoded in order after the slot's
+ * logical state; nothing in the pool is written, so it can be repeated.
+ *   q, k     device io dtype [n][n_tok][h_k][d_k]   raw draft inputs
+ *   v        device io dtype [n][n_tok][h_v][d_v]
+ *   a, b     device fp32 [n][n_tok][h_v]
+ *   out      device io dtype [n][n_tok][h_v][d_v]
+ * Outputs match gdn_verify_step on the same logical state within the
+ * chunked form's rounding (not bitwise). */
+gdn_status gdn_ring_verify(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                           int32_t n_tok, const void* q, const void* k, const void* v,
+                           const float* a, const float* b, const float* conv_w, void* out,
+                           void* stream);
+
+/* gdn_ring_commit: after sampling, commit the first accept_len[i] (clamped to
+ * 0..n_tok) of the same draft tokens (the same q, k, v, a, b as the verify
+ * call).  The conv window advances by them and they join the ring; when the
+ * ring would exceed ring_len, the ring and the accepted tokens are folded
+ * into the state tile instead and the ring is emptied, so each fold covers
+ * at least ring_len + 1 committed tokens.  An entry with accept_len 0 is left
+ * untouched.  Slots whose ring holds tokens must not be given to the one-call
+ * path before gdn_ring_flush. */
+gdn_status gdn_ring_commit(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                           int32_t n_tok, const void* q, const void* k, const void* v,
+                           const float* a, const float* b, const float* conv_w,
+                           const int32_t* accept_len, void* stream);
+
+/* gdn_ring_flush: fold each listed slot's ring into its state tile and empty
+ * it (no-op for empty rings); afterwards the tile is the logical state. */
+gdn_status gdn_ring_flush(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
+                          void* stream);
 
 /* Synchronise `stream`, then read and clear the sticky device error word
  * (0 = none; bit 0 = a slot id >= n_slots was skipped; bit 1 = a malformed

@@ -29,10 +29,10 @@ def io_torch(io):
     return torch.bfloat16 if io == "bf16" else torch.float32
 
 
-def make_pool(s: syn.Shapes, n_slots, io, n_layers=1, flags=0):
+def make_pool(s: syn.Shapes, n_slots, io, n_layers=1, flags=0, ring_len=0):
     import gated_deltanet_state_layer_amd as G
     d = G.make_desc(n_slots, n_layers, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k,
-                    G.GDN_BF16 if io == "bf16" else G.GDN_F32, 0.0, 0.0, flags)
+                    G.GDN_BF16 if io == "bf16" else G.GDN_F32, 0.0, 0.0, flags, ring_len)
     return G.Pool(d)
 
 

@@ -52,9 +52,29 @@ def test_pool_bytes_layout(lib):
     assert ab == (3 * 2 * 3 * 192 * 4 + 255) // 256 * 256 + 256 + 256   # 3*2*2 counters
 
 
+def test_pool_bytes_layout_with_a_verify_ring(lib):
+    from gated_deltanet_state_layer_amd import binding as B
+    base = B.pool_bytes(B.make_desc(256, 1, 16, 32, 128, 128, 4, B.GDN_BF16))[1]
+    d = B.make_desc(256, 1, 16, 32, 128, 128, 4, B.GDN_BF16, ring_len=8)
+    sb, ab = B.pool_bytes(d)
+    assert sb == 256 * 32 * 128 * 128 * 4                 # the state buffer does not change
+    per_tok = 16 * 128 + 32 * 128 + 2 * 32                # k^, v, a, b
+    stride = (8 * per_tok + 63) // 64 * 64
+    assert ab == base + 2 * 1024 + 256 * stride * 4       # counts, commit counters, records
+    cnt, rec, st = B.ring_layout(d)
+    assert (cnt, rec, st) == (base, base + 2048, stride)
+    assert rec % 256 == 0 and ab == rec + 256 * stride * 4
+    assert B.ring_layout(B.make_desc(4, 1, 2, 4, 64, 64, 4)) is None
+    # tiny shapes: the record block is padded to 64 floats (256 bytes)
+    d = B.make_desc(3, 2, 1, 1, 32, 32, 2, B.GDN_F32, ring_len=1)
+    cnt, rec, st = B.ring_layout(d)
+    assert st == 128 and B.pool_bytes(d)[1] == rec + 3 * 2 * 128 * 4
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("n_slots", 0, -1), ("h_v", 3, -1), ("d_k", 96, -2), ("d_v", 32, -2), ("conv_k", 0, -1), ("conv_k", 1, -2),
     ("conv_k", 9, -2), ("io_dtype", 7, -1), ("flags", 8, -1), ("q_scale", -1.0, -1),
+    ("ring_len", -1, -1), ("ring_len", 25, -2),
 ])
 def test_bad_descriptor_is_rejected(lib, field, value, status):
     from gated_deltanet_state_layer_amd import binding as B
@@ -82,6 +102,9 @@ def test_null_arguments_are_rejected_before_any_device_work(lib):
     assert lib.gdn_prefill_chunked_ckpt(nul, 0, 1, nul, nul, 8, 64, *([nul] * 7), 64, nul, nul,
                                         nul, 0, nul) == -1
     assert lib.gdn_slot_copy(nul, 1, nul, nul, nul) == -1
+    assert lib.gdn_ring_verify(nul, 0, 1, nul, 2, *([nul] * 8)) == -1
+    assert lib.gdn_ring_commit(nul, 0, 1, nul, 2, *([nul] * 8)) == -1
+    assert lib.gdn_ring_flush(nul, 0, 1, nul, nul) == -1
     n = ctypes.c_size_t()
     assert lib.gdn_prefill_workspace_bytes(nul, 1, 8, 64, ctypes.byref(n)) == -1
     e = ctypes.c_int32()
@@ -92,6 +115,6 @@ def test_null_arguments_are_rejected_before_any_device_work(lib):
 def test_status_strings(lib):
     from gated_deltanet_state_layer_amd import binding as B
     assert B.status_string(0) == "ok"
-    for s in (-1, -2, -3, -4, -5):
+    for s in (-1, -2, -3, -4, -5, -6):
         assert B.status_string(s) != "unknown status"
     assert B.status_string(42) == "unknown status"
