@@ -126,3 +126,54 @@ def test_graph_replayed_verify_and_prefill_equal_eager():
         assert torch.equal(pa.state, pb.state), f"replay {r}: states differ"
         assert torch.equal(pa.window, pb.window), f"replay {r}: windows differ"
     assert pa.error() == 0
+
+
+def test_graph_replayed_ring_cycle_equals_eager():
+    """A verify-ring cycle (ring_verify then ring_commit with acceptance
+    read from device memory) recorded once and replayed through appends and
+    folds; ring counts, records, states, windows and outputs equal the eager
+    twin at every replay."""
+    s, io, n_tok = syn.QWEN3_NEXT, "bf16", 4
+    say("graph ring cycle")
+    rng = np.random.default_rng(970)
+    n, n_slots = 16, 24
+    ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
+    contents = syn.draw_pool_contents(63, ids_np, s, io)
+    pa, pb = make_pool(s, n_slots, io, ring_len=8), make_pool(s, n_slots, io, ring_len=8)
+    load_slots(pa, contents)
+    load_slots(pb, contents)
+    w = dev(syn.draw_conv_weights(rng, s))
+    ids = dev(ids_np, torch.int32)
+    acc = torch.zeros(n, dtype=torch.int32, device="cuda")
+    vb = {m: torch.zeros((n, n_tok) + sh, dtype=torch.bfloat16 if m in "qkv" else torch.float32,
+                         device="cuda")
+          for m, sh in {"q": (s.h_k, s.d_k), "k": (s.h_k, s.d_k), "v": (s.h_v, s.d_v),
+                        "a": (s.h_v,), "b": (s.h_v,)}.items()}
+    out_a = torch.zeros((n, n_tok, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    out_b = torch.zeros_like(out_a)
+
+    def cycle(pool, out):
+        pool.ring_verify(0, ids, n_tok, vb["q"], vb["k"], vb["v"], vb["a"], vb["b"], w, out)
+        pool.ring_commit(0, ids, n_tok, vb["q"], vb["k"], vb["v"], vb["a"], vb["b"], w, acc)
+
+    g = _capture(lambda: cycle(pa, out_a))
+    assert torch.equal(pa.state, pb.state) and torch.equal(pa.ring_count, pb.ring_count)
+    folded = False
+    for r in range(6):
+        tv = syn.draw_tokens(rng, s, (n, n_tok), io)
+        for m in vb:
+            vb[m].copy_(torch.from_numpy(tv[m]).to(vb[m].dtype))
+        acc.copy_(torch.from_numpy(rng.integers(1, n_tok + 1, size=n).astype(np.int32)))
+        torch.cuda.synchronize()
+        before = pa.ring_count.clone()
+        g.replay()
+        cycle(pb, out_b)
+        torch.cuda.synchronize()
+        folded |= bool(((pa.ring_count < before) & (before > 0)).any())
+        assert torch.equal(out_a, out_b), f"replay {r}: outputs differ"
+        assert torch.equal(pa.ring_count, pb.ring_count), f"replay {r}: ring counts differ"
+        assert torch.equal(pa.ring_records, pb.ring_records), f"replay {r}: ring records differ"
+        assert torch.equal(pa.state, pb.state), f"replay {r}: states differ"
+        assert torch.equal(pa.window, pb.window), f"replay {r}: windows differ"
+    assert folded, "no replay folded a ring"
+    assert pa.error() == 0
