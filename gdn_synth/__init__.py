@@ -29,7 +29,7 @@ __all__ = [
     "Shapes", "TINY", "QWEN3_NEXT", "bf16_round", "conv_channels",
     "draw_tokens", "draw_conv_weights", "draw_slot_state", "draw_slot_window",
     "draw_pool_contents", "tiny_layer_case", "decode_case", "prefill_case",
-    "varlen_case", "verify_case",
+    "varlen_case", "verify_case", "QWEN3_NEXT_HIDDEN", "draw_hidden", "draw_in_proj_weight",
 ]
 
 
@@ -110,6 +110,25 @@ def draw_tokens(rng: np.random.Generator, s: Shapes, lead: tuple, io: str) -> di
 def draw_conv_weights(rng: np.random.Generator, s: Shapes) -> np.ndarray:
     """[C_conv][conv_k] fp32; tap conv_k-1 multiplies the current token."""
     return (0.5 * rng.standard_normal((s.c_conv, s.conv_k))).astype(np.float32)
+
+
+# Hidden size of the layer's input for the Qwen3-Next-shaped workloads (the
+# model's width; the pages give the GDN head shapes only).
+QWEN3_NEXT_HIDDEN = 2048
+
+
+def draw_hidden(rng: np.random.Generator, lead: tuple, hidden: int) -> np.ndarray:
+    """Hidden states x ~ N(0, 1), rounded to bf16 (float32 values)."""
+    return bf16_round(rng.standard_normal(lead + (hidden,)))
+
+
+def draw_in_proj_weight(rng: np.random.Generator, s: Shapes, hidden: int) -> np.ndarray:
+    """Synthetic input-projection weights [C_conv + 2 h_v][hidden], entries
+    N(0, 1/hidden) rounded to bf16 (float32 values), so that with N(0,1) hidden states every
+    projected channel is about N(0,1), the distribution of the layer's raw
+    inputs and gate pre-activations."""
+    n_out = s.c_conv + 2 * s.h_v
+    return bf16_round(rng.standard_normal((n_out, hidden)) / np.sqrt(hidden))
 
 
 def draw_slot_state(seed: int, slot: int, s: Shapes, n_layers: int = 1) -> np.ndarray:

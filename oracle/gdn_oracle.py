@@ -41,6 +41,8 @@ is listed at the top of the design doc and repeated next to the code it affects:
       position's output and commits the copy taken after accept_len tokens
       (0 leaves the slot untouched).
   R7  a negative slot id marks a padding entry: skipped, its output unwritten.
+  R14 the input projection: y = x W^T; rows of W in the order q | k | v |
+      a logits | b logits; a = exp(-softplus(y_a)), b = sigmoid(y_b).
 
 Parity of these readings against an external implementation is unpinned (no
 implementation exists to compare against); the oracle itself is pinned by the
@@ -53,7 +55,7 @@ import numpy as np
 __all__ = [
     "silu", "conv_silu_token", "l2norm", "expand_groups", "delta_rule_step",
     "token_step", "OraclePool", "unit_lower_inverse", "chunked_sequence",
-    "split_channels",
+    "split_channels", "in_projection",
 ]
 
 
@@ -94,6 +96,28 @@ def split_channels(y: np.ndarray, dims):
     k = y[..., nq:2 * nq].reshape(y.shape[:-1] + (dims.h_k, dims.d_k))
     v = y[..., 2 * nq:].reshape(y.shape[:-1] + (dims.h_v, dims.d_v))
     return q, k, v
+
+
+def in_projection(x: np.ndarray, W: np.ndarray, dims):
+    """The input projection in front of the conv ([P1] "Why this looks
+    tractable": the layer's kernels include an input projection beside the
+    conv).  Reading R14: y = x W^T over the hidden size, W's rows being the
+    output channels in the order q heads | k heads | v heads | h_v gate
+    logits for a | h_v gate logits for b; the raw q, k, v are the first
+    C_conv channels of y, and the gates are activated as the layer's inputs
+    are distributed: a = exp(-softplus(y_a)), b = sigmoid(y_b).
+
+    x: [..., hidden]; W: [C_conv + 2 h_v, hidden].  Returns (q, k, v, a, b)
+    with q, k [..., h_k, d_k], v [..., h_v, d_v], a, b [..., h_v]."""
+    y = np.asarray(x, np.float64) @ np.asarray(W, np.float64).T
+    c_conv = 2 * dims.h_k * dims.d_k + dims.h_v * dims.d_v
+    q, k, v = split_channels(y[..., :c_conv], dims)
+    ya = y[..., c_conv:c_conv + dims.h_v]
+    yb = y[..., c_conv + dims.h_v:c_conv + 2 * dims.h_v]
+    a = np.exp(-np.logaddexp(0.0, ya))          # softplus(y) = log(1 + e^y)
+    with np.errstate(over="ignore"):
+        b = 1.0 / (1.0 + np.exp(-yb))
+    return q, k, v, a, b
 
 
 def expand_groups(x: np.ndarray, h_v: int) -> np.ndarray:

@@ -346,3 +346,61 @@ def test_verify_equals_sequential_decode(acc):
         snap = (seq.S.copy(), seq.X.copy())
     np.testing.assert_array_equal(pool.S, snap[0])
     np.testing.assert_array_equal(pool.X, snap[1])
+
+
+# ------------------------------------------------------- input projection
+
+def test_in_projection_brute_force_tiny():
+    """Every output of the projection recomputed with plain Python loops from
+    the definitions (dot products; softplus as log(1 + e^y); the logistic)."""
+    rng = np.random.default_rng(40)
+    dm = dims(h_k=1, h_v=2, d_k=2, d_v=2)
+    hidden, T = 5, 3
+    C = 2 * 2 + 2 * 2 + 2 * 2
+    x = rng.standard_normal((T, hidden))
+    W = rng.standard_normal((C, hidden))
+    q, k, v, a, b = O.in_projection(x, W, dm)
+    flat = [[sum(x[t][i] * W[c][i] for i in range(hidden)) for c in range(C)] for t in range(T)]
+    for t in range(T):
+        y = flat[t]
+        assert np.allclose(q[t].ravel(), y[0:2], rtol=0, atol=1e-14)
+        assert np.allclose(k[t].ravel(), y[2:4], rtol=0, atol=1e-14)
+        assert np.allclose(v[t].ravel(), y[4:8], rtol=0, atol=1e-14)
+        for h in range(2):
+            assert math.isclose(a[t][h], math.exp(-math.log(1.0 + math.exp(y[8 + h]))), rel_tol=1e-13)
+            assert math.isclose(b[t][h], 1.0 / (1.0 + math.exp(-y[10 + h])), rel_tol=1e-13)
+
+
+def test_in_projection_one_hot_rows_select_inputs():
+    """W rows that are unit vectors pick input features: the raw q, k, v are
+    exact copies of permuted inputs, and a = 1 / (1 + e^x) exactly."""
+    rng = np.random.default_rng(41)
+    dm = dims(h_k=2, h_v=4, d_k=4, d_v=4)
+    C = 2 * 2 * 4 + 4 * 4 + 2 * 4
+    hidden = C
+    perm = rng.permutation(hidden)
+    W = np.eye(hidden)[perm]                      # row c = e_perm[c]
+    x = rng.standard_normal((7, hidden))
+    q, k, v, a, b = O.in_projection(x, W, dm)
+    y = x[:, perm]
+    np.testing.assert_array_equal(q.reshape(7, -1), y[:, :8])
+    np.testing.assert_array_equal(k.reshape(7, -1), y[:, 8:16])
+    np.testing.assert_array_equal(v.reshape(7, -1), y[:, 16:32])
+    np.testing.assert_allclose(a, 1.0 / (1.0 + np.exp(y[:, 32:36])), rtol=1e-15)
+    np.testing.assert_allclose(b, 1.0 / (1.0 + np.exp(-y[:, 36:40])), rtol=1e-15)
+
+
+def test_in_projection_gate_symmetry_and_limits():
+    """exp(-softplus(-y)) and sigmoid(y) are the same function: with the a
+    rows the negated b rows, a == b; large logits saturate a -> 0, b -> 1."""
+    rng = np.random.default_rng(42)
+    dm = dims(h_k=1, h_v=3, d_k=2, d_v=2)
+    hidden = 6
+    Wb = rng.standard_normal((3, hidden))
+    W = np.concatenate([rng.standard_normal((2 + 2 + 6, hidden)), -Wb, Wb])
+    x = rng.standard_normal((5, hidden))
+    _, _, _, a, b = O.in_projection(x, W, dm)
+    np.testing.assert_allclose(a, b, rtol=1e-14)
+    _, _, _, a, b = O.in_projection(np.full((1, hidden), 100.0), np.concatenate(
+        [np.zeros((10, hidden)), np.ones((6, hidden))]), dm)
+    assert np.all(a < 1e-200) and np.all(b == 1.0)
