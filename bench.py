@@ -83,7 +83,9 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-verify", action="store_true")
     p.add_argument("--no-ring", action="store_true")
-    p.add_argument("--only", choices=["decode", "verify", "ring", "prefill", "copy", "gemm"],
+    p.add_argument("--no-in-proj", action="store_true")
+    p.add_argument("--only", choices=["decode", "verify", "ring", "in_proj", "prefill", "copy",
+                                      "gemm"],
                    default=None,
                    help="run one workload only (for profiling)")
     p.add_argument("--prefill-case", choices=["single", "split512", "varlen", "all"], default="all",
@@ -349,6 +351,37 @@ def bench_ring(args, torch, G, syn):
             "one_call_kernel_split_cycle_us": t_split * 1e6}
 
 
+def bench_in_proj(args, torch, G, syn):
+    """The input projection (hidden 2048 -> q|k|v|a|b, 8256 channels) at a
+    decode batch (64 tokens: streams the 33.8 MB weight) and at a prefill
+    length (8192 tokens: a 277 GFLOP bf16 GEMM)."""
+    s, H = syn.QWEN3_NEXT, syn.QWEN3_NEXT_HIDDEN
+    n_out = s.c_conv + 2 * s.h_v
+    pool = G.Pool(G.make_desc(1, 1, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k, G.GDN_BF16))
+    w = (torch.randn((n_out, H), device="cuda") / H ** 0.5).bfloat16()
+    res = {}
+    for n_tok, label in ((64, "decode_64"), (8192, "prefill_8192")):
+        x = torch.randn((n_tok, H), device="cuda").bfloat16()
+        q = torch.empty((n_tok, s.h_k, s.d_k), dtype=torch.bfloat16, device="cuda")
+        k = torch.empty_like(q)
+        v = torch.empty((n_tok, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+        a = torch.empty((n_tok, s.h_v), device="cuda")
+        b = torch.empty_like(a)
+        nb = pool.in_proj_workspace_bytes(n_tok, H)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda") if nb else None
+        reps = max(20, args.steps // 4) if n_tok <= 64 else 20
+        t = time_launches(lambda i: pool.in_proj(x, w, q, k, v, a, b, ws), reps, 5, torch)
+        flops = 2.0 * n_tok * H * n_out
+        bytes_ = n_out * H * 2 + n_tok * H * 2 + n_tok * (s.c_conv * 2 + 2 * s.h_v * 4)
+        res[label] = {"tokens": n_tok, "us": t * 1e6, "GBps": bytes_ / t / 1e9,
+                      "hbm_frac": bytes_ / t / 1e9 / HBM_PEAK_GBPS,
+                      "TFLOPs": flops / t / 1e12, "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS,
+                      "split_hidden": nb > 0}
+    assert pool.error() == 0
+    res["workload"] = f"hidden {H} -> {n_out} channels (q|k|v|a|b), bf16 x and W, synthetic"
+    return res
+
+
 def prefill_flops_per_token(s, C):
     """Algorithmic flops per token of the chunked form (2 per multiply-add,
     triangular products counted as triangles), per chunk divided by C:
@@ -512,6 +545,9 @@ def main():
     if args.only in (None, "ring") and not args.no_ring:
         res["ring"] = bench_ring(args, torch, G, syn)
         print(f"# ring done: {res['ring']['cycle_us']:.1f} us/cycle", file=sys.stderr, flush=True)
+    if args.only in (None, "in_proj") and not args.no_in_proj:
+        res["in_proj"] = bench_in_proj(args, torch, G, syn)
+        print("# in_proj done", file=sys.stderr, flush=True)
     if args.only in (None, "prefill") and not args.no_prefill:
         res["prefill"] = bench_prefill(args, torch, G, syn)
         print("# prefill done", file=sys.stderr, flush=True)
@@ -559,6 +595,8 @@ def main():
                           "hbm_frac": v["gbps"] / HBM_PEAK_GBPS}
     if res.get("ring"):
         line["verify_ring"] = res["ring"]
+    if res.get("in_proj"):
+        line["in_proj"] = res["in_proj"]
     if res.get("prefill"):
         line["prefill"] = res["prefill"]
     if res.get("copy"):

@@ -30,7 +30,8 @@ EXPORTED = (
     "gdn_pool_bytes", "gdn_pool_create", "gdn_pool_destroy", "gdn_slot_reset",
     "gdn_decode_step", "gdn_verify_step", "gdn_prefill_workspace_bytes",
     "gdn_prefill_chunked", "gdn_prefill_chunked_ckpt", "gdn_slot_copy", "gdn_ring_verify",
-    "gdn_ring_commit", "gdn_ring_flush", "gdn_pool_error", "gdn_status_string",
+    "gdn_ring_commit", "gdn_ring_flush", "gdn_in_proj_workspace_bytes", "gdn_in_proj",
+    "gdn_pool_error", "gdn_status_string",
 )
 
 
@@ -80,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_ring_verify": [P, I32, I32, P, I32, P, P, P, P, P, P, P, P],
         "gdn_ring_commit": [P, I32, I32, P, I32, P, P, P, P, P, P, P, P],
         "gdn_ring_flush": [P, I32, I32, P, P],
+        "gdn_in_proj_workspace_bytes": [P, I64, I32, PSZ],
+        "gdn_in_proj": [P, I64, I32, P, P, P, P, P, P, P, P, SZ, P],
         "gdn_pool_error": [P, P, ctypes.POINTER(I32)],
     }
     for name, args in sig.items():
@@ -238,6 +241,22 @@ class Pool:
         lib = load_library()
         _check(lib.gdn_ring_flush(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids),
                                   _stream(stream)), "gdn_ring_flush")
+
+    def in_proj_workspace_bytes(self, n_tok, hidden):
+        lib = load_library()
+        n = ctypes.c_size_t()
+        _check(lib.gdn_in_proj_workspace_bytes(self._h, n_tok, hidden, ctypes.byref(n)),
+               "gdn_in_proj_workspace_bytes")
+        return n.value
+
+    def in_proj(self, x, w, q, k, v, a, b, workspace=None, stream=None):
+        """x [n_tok][hidden] bf16, w [C_conv + 2 h_v][hidden] bf16 -> q, k, v, a, b."""
+        lib = load_library()
+        n_tok, hidden = int(x.shape[0]), int(x.shape[1])
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib.gdn_in_proj(self._h, n_tok, hidden, _ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(a), _ptr(b), _ptr(workspace), ws_bytes, _stream(stream)),
+               "gdn_in_proj")
 
     def prefill_workspace_bytes(self, n_seq, total_tokens, chunk):
         lib = load_library()

@@ -435,6 +435,42 @@ gdn_status gdn_ring_flush(gdn_pool* pool, int32_t layer, int32_t n, const int32_
                      nullptr, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
+static gdn_status in_proj_args(const gdn_pool* pool, int64_t n_tok, int32_t hidden) {
+    if (!pool || n_tok < 0 || hidden < 1) return GDN_ERR_INVALID_ARG;
+    if (hidden % 32 != 0) return GDN_ERR_UNSUPPORTED;
+    const int64_t n_out = pool->view.c_conv + 2 * pool->view.h_v;
+    // 32-bit byte offsets inside x and W (64 rows of slack for ragged tiles)
+    if ((n_tok + 64) * hidden * 2 >= INT32_MAX || (n_out + 64) * hidden * 2 >= INT32_MAX)
+        return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+gdn_status gdn_in_proj_workspace_bytes(const gdn_pool* pool, int64_t n_tok, int32_t hidden,
+                                       size_t* bytes) {
+    const gdn_status st = in_proj_args(pool, n_tok, hidden);
+    if (st != GDN_OK) return st;
+    if (!bytes) return GDN_ERR_INVALID_ARG;
+    *bytes = in_proj_workspace_bytes(pool, n_tok, hidden);
+    return GDN_OK;
+}
+
+gdn_status gdn_in_proj(gdn_pool* pool, int64_t n_tok, int32_t hidden, const void* x, const void* w,
+                       void* q, void* k, void* v, float* a, float* b, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    const gdn_status st = in_proj_args(pool, n_tok, hidden);
+    if (st != GDN_OK) return st;
+    if (n_tok == 0) return GDN_OK;
+    if (!x || !w || !q || !k || !v || !a || !b) return GDN_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w, 16)) return GDN_ERR_INVALID_ARG;
+    const size_t need = in_proj_workspace_bytes(pool, n_tok, hidden);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, kAlign)) return GDN_ERR_INVALID_ARG;
+    return launch_in_proj(pool, n_tok, hidden, x, w, q, k, v, a, b, workspace,
+                          as_stream(stream)) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
 gdn_status gdn_pool_error(gdn_pool* pool, void* stream, int32_t* device_error) {
     if (!pool || !device_error) return GDN_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);

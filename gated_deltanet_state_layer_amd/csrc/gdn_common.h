@@ -135,6 +135,11 @@ hipError_t launch_ring(const gdn_pool* pool, RingOp op, int32_t layer, int32_t n
                        const int32_t* slot_ids, int32_t n_tok, const void* q, const void* k,
                        const void* v, const float* a, const float* b, const float* conv_w,
                        const int32_t* accept_len, void* out, hipStream_t stream);
+// Input projection y = x W^T with the q | k | v | a | b epilogue.
+size_t in_proj_workspace_bytes(const gdn_pool* pool, int64_t n_tok, int32_t hidden);
+hipError_t launch_in_proj(const gdn_pool* pool, int64_t n_tok, int32_t hidden, const void* x,
+                          const void* w, void* q, void* k, void* v, float* a, float* b,
+                          void* workspace, hipStream_t stream);
 size_t prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
                                int32_t chunk);
 hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,

@@ -278,6 +278,29 @@ gdn_status gdn_ring_commit(gdn_pool* pool, int32_t layer, int32_t n, const int32
 gdn_status gdn_ring_flush(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
                           void* stream);
 
+/* Input projection, the step in front of the conv ("baseRT issue #31",
+ * section "Why this looks tractable": an input-projection kernel beside the
+ * conv).  For n_tok tokens, y = x W^T over the hidden size (bf16 inputs, fp32
+ * accumulation), written as the raw inputs of the other calls:
+ *   x          device bf16 [n_tok][hidden] (16-byte aligned; hidden % 32 == 0)
+ *   w          device bf16 [C_conv + 2*h_v][hidden] (16-byte aligned): rows
+ *              are the output channels, q heads | k heads | v heads | h_v a
+ *              logits | h_v b logits
+ *   q, k       device io dtype [n_tok][h_k][d_k]   raw (pre-conv) inputs
+ *   v          device io dtype [n_tok][h_v][d_v]
+ *   a, b       device fp32 [n_tok][h_v]: a = exp(-softplus(y_a)),
+ *              b = sigmoid(y_b)
+ *   workspace  device, >= gdn_in_proj_workspace_bytes (0 for large n_tok),
+ *              256-byte aligned; scratch only
+ * The pool supplies the shapes only; no slot is read or written.  Returns
+ * GDN_ERR_UNSUPPORTED when hidden is not a multiple of 32 or the operands
+ * exceed 2 GiB. */
+gdn_status gdn_in_proj_workspace_bytes(const gdn_pool* pool, int64_t n_tok, int32_t hidden,
+                                       size_t* bytes);
+gdn_status gdn_in_proj(gdn_pool* pool, int64_t n_tok, int32_t hidden, const void* x, const void* w,
+                       void* q, void* k, void* v, float* a, float* b, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Synchronise `stream`, then read and clear the sticky device error word
  * (0 = none; bit 0 = a slot id >= n_slots was skipped; bit 1 = a malformed
  * cu_seqlens was seen). */

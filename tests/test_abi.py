@@ -105,6 +105,8 @@ def test_null_arguments_are_rejected_before_any_device_work(lib):
     assert lib.gdn_ring_verify(nul, 0, 1, nul, 2, *([nul] * 8)) == -1
     assert lib.gdn_ring_commit(nul, 0, 1, nul, 2, *([nul] * 8)) == -1
     assert lib.gdn_ring_flush(nul, 0, 1, nul, nul) == -1
+    assert lib.gdn_in_proj(nul, 4, 64, *([nul] * 8), 0, nul) == -1
+    assert lib.gdn_in_proj_workspace_bytes(nul, 4, 64, ctypes.byref(ctypes.c_size_t())) == -1
     n = ctypes.c_size_t()
     assert lib.gdn_prefill_workspace_bytes(nul, 1, 8, 64, ctypes.byref(n)) == -1
     e = ctypes.c_int32()

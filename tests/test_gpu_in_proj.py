@@ -1,0 +1,113 @@
+"""GPU parity of the input projection (gdn_in_proj) against the fp64 oracle:
+the raw q, k, v and the activated gates, on the split-hidden path (few
+tokens) and the one-pass path, with ragged token and channel counts, and the
+projection feeding a decode step."""
+import numpy as np
+import pytest
+
+import gdn_synth as syn
+from gpu_util import check_f32, check_out, dev, host, load_slots, make_pool, oracle_pool, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from oracle import gdn_oracle as O  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_deltanet_state_layer_amd import binding
+    binding.load_library()
+
+
+def _project(pool, s, x_np, w_np, io):
+    n = x_np.shape[0]
+    t = torch.bfloat16 if io == "bf16" else torch.float32
+    x = dev(x_np, torch.bfloat16)
+    w = dev(w_np, torch.bfloat16)
+    q = torch.full((n, s.h_k, s.d_k), float("nan"), dtype=t, device="cuda")
+    k = torch.full_like(q, float("nan"))
+    v = torch.full((n, s.h_v, s.d_v), float("nan"), dtype=t, device="cuda")
+    a = torch.full((n, s.h_v), float("nan"), device="cuda")
+    b = torch.full_like(a, float("nan"))
+    nb = pool.in_proj_workspace_bytes(n, x_np.shape[1])
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda") if nb else None
+    pool.in_proj(x, w, q, k, v, a, b, ws)
+    torch.cuda.synchronize()
+    return q, k, v, a, b, nb
+
+
+@pytest.mark.parametrize("n_tok", [1, 64, 300, 1024])
+def test_in_proj_qwen3_next_vs_oracle(n_tok):
+    s, io, hidden = syn.QWEN3_NEXT, "bf16", syn.QWEN3_NEXT_HIDDEN
+    rng = np.random.default_rng(1100 + n_tok)
+    x = syn.draw_hidden(rng, (n_tok,), hidden)
+    w = syn.draw_in_proj_weight(rng, s, hidden)
+    pool = make_pool(s, 1, io)
+    q, k, v, a, b, nb = _project(pool, s, x, w, io)
+    say(f"in_proj: {n_tok} tokens, hidden {hidden}, workspace {nb} B "
+        f"({'split' if nb else 'one pass'})")
+    rq, rk, rv, ra, rb = O.in_projection(x, w, s)
+    check_out("q", host(q), rq, io)
+    check_out("k", host(k), rk, io)
+    check_out("v", host(v), rv, io)
+    check_f32("a", host(a), ra)
+    check_f32("b", host(b), rb)
+    assert pool.error() == 0
+
+
+@pytest.mark.parametrize("h_k,h_v,d,hidden,n_tok,io", [
+    (2, 2, 32, 96, 7, "f32"),        # 196 output channels: a ragged 16-channel tile
+    (1, 3, 64, 160, 70, "bf16"),     # 3 gates each: gate rows straddle a tile
+    (2, 4, 128, 4096, 5, "bf16"),    # long hidden, split 16 ways
+])
+def test_in_proj_other_shapes(h_k, h_v, d, hidden, n_tok, io):
+    s = syn.Shapes(h_k, h_v, d, d, 4)
+    rng = np.random.default_rng(1200 + hidden)
+    x = syn.draw_hidden(rng, (n_tok,), hidden)
+    w = syn.draw_in_proj_weight(rng, s, hidden)
+    pool = make_pool(s, 1, io)
+    q, k, v, a, b, nb = _project(pool, s, x, w, io)
+    say(f"in_proj: {s} hidden {hidden} tokens {n_tok} io {io} workspace {nb}")
+    rq, rk, rv, ra, rb = O.in_projection(x, w, s)
+    check_out("q", host(q), rq, io)
+    check_out("k", host(k), rk, io)
+    check_out("v", host(v), rv, io)
+    check_f32("a", host(a), ra)
+    check_f32("b", host(b), rb)
+
+
+def test_in_proj_feeds_decode():
+    """Hidden states -> projection -> decode step, on both sides."""
+    s, io, hidden = syn.QWEN3_NEXT, "bf16", syn.QWEN3_NEXT_HIDDEN
+    rng = np.random.default_rng(1300)
+    n, n_slots = 8, 12
+    ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
+    contents = syn.draw_pool_contents(1301, ids_np, s, io)
+    pool = make_pool(s, n_slots, io)
+    load_slots(pool, contents)
+    w_conv = syn.draw_conv_weights(rng, s)
+    x = syn.draw_hidden(rng, (n,), hidden)
+    w = syn.draw_in_proj_weight(rng, s, hidden)
+    q, k, v, a, b, _ = _project(pool, s, x, w, io)
+    out = torch.empty((n, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    pool.decode(0, dev(ids_np, torch.int32), q, k, v, a, b, dev(w_conv), out)
+    torch.cuda.synchronize()
+    rq, rk, rv, ra, rb = O.in_projection(x, w, s)
+    # the decode consumes the projection rounded to the io dtype, as stored
+    rq, rk, rv = (syn.bf16_round(t).astype(np.float64) for t in (rq, rk, rv))
+    op = oracle_pool(s, contents, ids_np)
+    ref = op.decode(0, np.arange(n), rq, rk, rv, ra, rb, w_conv)
+    check_out("decode outputs", host(out), ref, io)
+    check_f32("states", host(pool.state[torch.from_numpy(ids_np.astype(np.int64)).cuda()]), op.S)
+
+
+def test_in_proj_rejects_unsupported_hidden():
+    import gated_deltanet_state_layer_amd as G
+    s = syn.Shapes(2, 2, 32, 32, 4)
+    pool = make_pool(s, 1, "f32")
+    with pytest.raises(G.GdnError) as ei:
+        pool.in_proj_workspace_bytes(4, 100)
+    assert ei.value.status == -2
