@@ -439,8 +439,8 @@ static gdn_status in_proj_args(const gdn_pool* pool, int64_t n_tok, int32_t hidd
     if (!pool || n_tok < 0 || hidden < 1) return GDN_ERR_INVALID_ARG;
     if (hidden % 32 != 0) return GDN_ERR_UNSUPPORTED;
     const int64_t n_out = pool->view.c_conv + 2 * pool->view.h_v;
-    // 32-bit byte offsets inside x and W (64 rows of slack for ragged tiles)
-    if ((n_tok + 64) * hidden * 2 >= INT32_MAX || (n_out + 64) * hidden * 2 >= INT32_MAX)
+    // 32-bit byte offsets inside x and W (128 rows of slack for ragged tiles)
+    if ((n_tok + 128) * hidden * 2 >= INT32_MAX || (n_out + 128) * hidden * 2 >= INT32_MAX)
         return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }

@@ -7,15 +7,12 @@
 // | h_v a logits | h_v b logits; x and W are bf16, products are exact in fp32
 // and accumulate in fp32 on the bf16 matrix cores.
 //
-// gemm kernel: grid (N/64, M/64, ksplit), 4 waves; wave w owns 16 output
-// channels and the block's 64 tokens (4 MFMA tiles) over its share of the
-// hidden dimension.  Both operands come straight from memory into MFMA
-// registers: lane (m, q) of an operand reads the 16 bytes of row m at
-// k = 8q..8q+7 of the step, so no LDS staging is needed, and buffer
-// descriptors return zeros for rows past the ends (ragged token and channel
-// counts).  With few tokens the hidden dimension is split over ksplit
-// workgroups so that enough weight bytes are in flight; a second kernel adds
-// the partial sums.  Otherwise the gemm kernel writes the outputs itself.
+// gemm kernel: grid (N/128, M/128, ksplit), 4 waves, a 128 x 128 output tile
+// per workgroup; k-blocks of 32 go through LDS, double buffered, loaded with
+// 16-byte buffer loads whose descriptors return zeros past the ragged ends.
+// With few tokens the hidden dimension is split over ksplit workgroups so
+// that enough weight bytes are in flight; a second kernel adds the partial
+// sums.  Otherwise the gemm kernel writes the outputs itself.
 #include <algorithm>
 
 #include "gdn_common.h"
@@ -30,9 +27,6 @@ constexpr int kOffOOB = 0x7fff0000;   // an offset past every descriptor used he
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
-}
-__device__ __forceinline__ bf16x8 ld_frag(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 struct ProjOut {
@@ -51,57 +45,94 @@ __device__ __forceinline__ void put(const ProjOut& o, int64_t m, int n, float y)
     else o.b[m * o.h_v + n - o.c_conv - o.h_v] = 1.0f / (1.0f + __expf(-y));
 }
 
+// 128 x 128 output tile per workgroup (wave (wm, wn) owns a 64 x 64
+// quadrant: 4 x 4 MFMA tiles), k-blocks of 32 staged in LDS, double
+// buffered: each thread loads its share of block kb+1 (two 16-byte vectors
+// of x, two of W) while the waves multiply block kb, then stores it.
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int LDK = BK + 8;          // LDS row in bf16 (16-byte aligned, skewed banks)
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void in_proj_gemm_kernel(
+__global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
-    float* __restrict__ part, int steps_per_split) {
+    float* __restrict__ part, int blocks_per_split) {
+    __shared__ __align__(16) uint16_t sa[2][BM * LDK];
+    __shared__ __align__(16) uint16_t sb[2][BN * LDK];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;
     const int N = o.n_out;
-    const int n0 = (blockIdx.x * 4 + wave) * 16, m0 = blockIdx.y * 64;
-    const int nsteps = H / 32;
-    const int s_begin = blockIdx.z * steps_per_split;
-    const int s_end = min(nsteps, s_begin + steps_per_split);
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int nblk = H / BK;
+    const int kb_begin = blockIdx.z * blocks_per_split;
+    const int kb_end = min(nblk, kb_begin + blocks_per_split);
     const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
-    // byte offsets of this lane's 16 bytes at step 0 (rows past the ends read zeros)
-    const int w_off = (n0 + m16) * H * 2 + q4 * 16;
-    int x_off[4];
+    // staging: vector e = tid + 256 i (i < 2) of a tile is row e / 4, k 8 (e % 4)
+    int ga[2], gb[2], ls[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x_off[i] = (m0 + i * 16 + m16) * H * 2 + q4 * 16;
-    f32x4 acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // one step ahead: the next step's fragments load while this step multiplies
-    auto fetch = [&](int s, bf16x8* xf, bf16x8& wf) {
-        const bool ok = s < s_end;
-        wf = ld_frag(w_rs, ok ? w_off + s * 64 : kOffOOB);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xf[i] = ld_frag(x_rs, ok ? x_off[i] + s * 64 : kOffOOB);
-    };
-    bf16x8 xa[4], xb[4], wa, wb;
-    fetch(s_begin, xa, wa);
-    for (int s = s_begin; s < s_end; s += 2) {
-        fetch(s + 1, xb, wb);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], wa, acc[i], 0, 0, 0);
-        fetch(s + 2, xa, wa);
-        if (s + 1 < s_end) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[i], wb, acc[i], 0, 0, 0);
-        }
+    for (int i = 0; i < 2; ++i) {
+        const int e = tid + i * kThreads, r = e >> 2, kv = (e & 3) * 8;
+        ga[i] = ((m0 + r) * H + kv) * 2;     // rows past M / N read zeros
+        gb[i] = ((n0 + r) * H + kv) * 2;
+        ls[i] = r * LDK + kv;
     }
-    // lane holds y[m0 + 16 i + 4 q + j][n0 + m16]
-    const int n = n0 + m16;
-    if (n >= N) return;
+    uint4 va[2], vb[2];
+    auto fetch = [&](int kb) {
+        const bool ok = kb < kb_end;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + i * 16 + q4 * 4 + j;
-            if (m >= M) continue;
-            if (part) part[((int64_t)blockIdx.z * M + m) * N + n] = acc[i][j];
-            else put<T>(o, m, n, acc[i][j]);
+        for (int i = 0; i < 2; ++i) {
+            va[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, ok ? ga[i] + kb * BK * 2 : kOffOOB, 0, 0));
+            vb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, ok ? gb[i] + kb * BK * 2 : kOffOOB, 0, 0));
         }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<uint4*>(&sa[buf][ls[i]]) = va[i];
+            *reinterpret_cast<uint4*>(&sb[buf][ls[i]]) = vb[i];
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    fetch(kb_begin);
+    stage(0);
+    __syncthreads();
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+        const int buf = (kb - kb_begin) & 1;
+        fetch(kb + 1);
+        bf16x8 fa[4], fb[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            fa[mt] = *reinterpret_cast<const bf16x8*>(&sa[buf][(wm * 64 + mt * 16 + m16) * LDK + q4 * 8]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+            fb[nt] = *reinterpret_cast<const bf16x8*>(&sb[buf][(wn * 64 + nt * 16 + m16) * LDK + q4 * 8]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
+        stage(buf ^ 1);
+        __syncthreads();
+    }
+    // lane holds y[m0 + 64 wm + 16 mt + 4 q + j][n0 + 64 wn + 16 nt + m16]
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int n = n0 + wn * 64 + nt * 16 + m16;
+        if (n >= N) continue;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = m0 + wm * 64 + mt * 16 + q4 * 4 + j;
+                if (m >= M) continue;
+                if (part) part[((int64_t)blockIdx.z * M + m) * N + n] = acc[mt][nt][j];
+                else put<T>(o, m, n, acc[mt][nt][j]);
+            }
+    }
 }
 
 // Sum of the ksplit partial products, then the outputs.
@@ -120,12 +151,12 @@ __global__ __launch_bounds__(kThreads) void in_proj_epilogue_kernel(const float*
 }  // namespace
 
 // Split of the hidden dimension for M tokens: enough workgroups to keep the
-// weight stream busy, at least 4 steps of 32 per split.
+// weight stream busy, at least 4 k-blocks of 32 per split.
 int in_proj_ksplit(const gdn_pool* pool, int64_t M, int32_t H) {
     const int N = pool->view.c_conv + 2 * pool->view.h_v;
-    const int64_t tiles = (int64_t)((N + 63) / 64) * ((M + 63) / 64);
-    int ks = (int)std::min<int64_t>(16, std::max<int64_t>(1, 1024 / std::max<int64_t>(tiles, 1)));
-    ks = std::min(ks, std::max(1, H / 32 / 4));
+    const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+    int ks = (int)std::min<int64_t>(16, std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1)));
+    ks = std::min(ks, std::max(1, H / BK / 4));
     return ks;
 }
 
@@ -140,9 +171,9 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
     const PoolView& P = pool->view;
     ProjOut o{q, k, v, a, b, P.h_k * P.d, P.h_v * P.d, P.c_conv, P.h_v, P.c_conv + 2 * P.h_v};
     const int ks = in_proj_ksplit(pool, M, H);
-    const int nsteps = H / 32, per = (nsteps + ks - 1) / ks;
+    const int nblk = H / BK, per = (nblk + ks - 1) / ks;
     float* part = ks > 1 ? static_cast<float*>(workspace) : nullptr;
-    const dim3 grid((o.n_out + 63) / 64, (unsigned)((M + 63) / 64), ks);
+    const dim3 grid((o.n_out + BN - 1) / BN, (unsigned)((M + BM - 1) / BM), ks);
     const auto* xs = static_cast<const uint16_t*>(x);
     const auto* ws = static_cast<const uint16_t*>(w);
     if (pool->desc.io_dtype == GDN_BF16)
