@@ -522,7 +522,55 @@ def cpu_baseline(syn):
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": n_done / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
             "sample": f"{n_done} decode tokens (16-slot decode steps, Qwen3-Next shapes, fp64 "
-                      f"literal matrix form) in {dt:.1f} s on {platform.processor() or 'host'}"}
+                      f"literal matrix form) in {dt:.1f} s on {cpu_model()}"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "host"
+
+
+def cpu_other(syn):
+    """The fp64 oracle on bounded samples of the other workloads (context
+    beside cpu_baseline): the 8192-token prefill token by token and in its
+    chunked form (chunk 64), and the 4-token verify, each for a few seconds."""
+    from oracle import gdn_oracle as O
+    s = syn.QWEN3_NEXT
+    res = {}
+    case = syn.prefill_case()
+    tok = case["tokens"]
+    op = O.OraclePool(1, 1, s)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 4.0 and n < 8192:
+        op.prefill(0, np.array([0, 16]), np.array([0]), *(tok[m][n:n + 16] for m in "qkvab"),
+                   case["conv_w"])
+        n += 16
+    res["prefill_token_loop_tok_s"] = n / (time.perf_counter() - t0)
+    S0 = np.zeros((s.h_v, s.d_v, s.d_k))
+    X0 = np.zeros((s.conv_k - 1, s.c_conv))
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 4.0 and n < 8192:
+        _, S0, X0 = O.chunked_sequence(S0, X0, *(tok[m][n:n + 256] for m in "qkvab"),
+                                       case["conv_w"], s, 64)
+        n += 256
+    res["prefill_chunked_tok_s"] = n / (time.perf_counter() - t0)
+    vc = syn.verify_case()
+    vt = vc["tokens"]
+    op = O.OraclePool(16, 1, s)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 4.0:
+        op.verify(0, np.arange(16), 4, *(vt[m][:16] for m in "qkvab"), vc["conv_w"],
+                  vc["accept_len"][:16])
+        n += 64
+    res["verify_tok_s"] = n / (time.perf_counter() - t0)
+    res["sample"] = ("one 8192-token sequence (first tokens, fp64 token loop and chunked form), "
+                     "16 slots x 4-token verify; Qwen3-Next shapes; " + cpu_model())
+    return res
 
 
 def main():
@@ -557,9 +605,10 @@ def main():
     if args.only in (None, "gemm"):
         res["gemm"] = bench_gemm(args, torch)
         print("# gemm done", file=sys.stderr, flush=True)
-    cpu = None
+    cpu = cpu_more = None
     if not args.no_cpu and args.only is None:
         cpu = cpu_baseline(syn)
+        cpu_more = cpu_other(syn)
         print("# cpu baseline done", file=sys.stderr, flush=True)
     if "decode" not in res:
         print(json.dumps(res))
@@ -605,6 +654,7 @@ def main():
         line["mfma_reference"] = res["gemm"]
     if cpu:
         line["cpu_baseline"] = cpu
+        line["cpu_other"] = cpu_more
     print(json.dumps(line), flush=True)
 
 
