@@ -7,6 +7,7 @@
 // | h_v a logits | h_v b logits; x and W are bf16, products are exact in fp32
 // and accumulate in fp32 on the bf16 matrix cores.
 //
+// Up to 64 tokens: the skinny kernel below.  Otherwise the
 // gemm kernel: grid (N/128, M/128, ksplit), 4 waves, a 128 x 128 output tile
 // per workgroup; k-blocks of 32 go through LDS, double buffered, loaded with
 // 16-byte buffer loads whose descriptors return zeros past the ragged ends.
@@ -135,6 +136,82 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
     }
 }
 
+// Few tokens (M <= 64): the weight stream is the whole cost.  One workgroup
+// of 8 waves per 64 output channels; wave w multiplies the full 64 x 64 tile
+// over its eighth of the hidden dimension, operands straight from memory into
+// MFMA registers (16 bytes per lane, one step ahead), and the eight partial
+// tiles are added in LDS before the fused epilogue.  No partial sums leave
+// the chip and there is no second launch.
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
+constexpr size_t kSkinnyLds = (size_t)kSkinnyWaves * 64 * 64 * sizeof(float);
+
+template <typename T>
+__global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o) {
+    extern __shared__ __align__(16) float red[];     // [8 waves][64 tokens][64 channels]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m16 = lane & 15, q4 = lane >> 4;
+    const int N = o.n_out, n0 = blockIdx.x * 64;
+    const int nsteps = H / 32, per = (nsteps + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int s_begin = wave * per, s_end = min(nsteps, s_begin + per);
+    const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
+    int xo[4], wo[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        xo[t] = ((t * 16 + m16) * H) * 2 + q4 * 16;         // tokens past M read zeros
+        wo[t] = ((n0 + t * 16 + m16) * H) * 2 + q4 * 16;    // channels past N read zeros
+    }
+    auto fetch = [&](int st, bf16x8* xf, bf16x8* wf) {
+        const bool ok = st < s_end;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            xf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(x_rs, ok ? xo[t] + st * 64 : kOffOOB, 0, 0));
+            wf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(w_rs, ok ? wo[t] + st * 64 : kOffOOB, 0, 0));
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 xa[4], wa[4], xb[4], wb[4];
+    fetch(s_begin, xa, wa);
+    for (int st = s_begin; st < s_end; st += 2) {
+        fetch(st + 1, xb, wb);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], wa[nt], acc[mt][nt], 0, 0, 0);
+        fetch(st + 2, xa, wa);
+        if (st + 1 < s_end) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[mt], wb[nt], acc[mt][nt], 0, 0, 0);
+        }
+    }
+    // lane holds y[16 mt + 4 q + j][n0 + 16 nt + m16]
+    float* mine = red + wave * 64 * 64;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mine[(mt * 16 + q4 * 4 + j) * 64 + nt * 16 + m16] = acc[mt][nt][j];
+    __syncthreads();
+    for (int idx = tid; idx < 64 * 64; idx += kSkinnyThreads) {
+        const int m = idx >> 6, n = n0 + (idx & 63);
+        if (m >= M || n >= N) continue;
+        float y = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kSkinnyWaves; ++ww) y += red[ww * 64 * 64 + idx];
+        put<T>(o, m, n, y);
+    }
+}
+
 // Sum of the ksplit partial products, then the outputs.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void in_proj_epilogue_kernel(const float* __restrict__ part,
@@ -153,6 +230,7 @@ __global__ __launch_bounds__(kThreads) void in_proj_epilogue_kernel(const float*
 // Split of the hidden dimension for M tokens: enough workgroups to keep the
 // weight stream busy, at least 4 k-blocks of 32 per split.
 int in_proj_ksplit(const gdn_pool* pool, int64_t M, int32_t H) {
+    if (M <= 64) return 1;   // the skinny kernel
     const int N = pool->view.c_conv + 2 * pool->view.h_v;
     const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + BM - 1) / BM);
     int ks = (int)std::min<int64_t>(16, std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1)));
@@ -170,12 +248,34 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
                           hipStream_t stream) {
     const PoolView& P = pool->view;
     ProjOut o{q, k, v, a, b, P.h_k * P.d, P.h_v * P.d, P.c_conv, P.h_v, P.c_conv + 2 * P.h_v};
+    const auto* xs = static_cast<const uint16_t*>(x);
+    const auto* ws = static_cast<const uint16_t*>(w);
+    if (M <= 64) {
+        // more than 64 KiB of dynamic LDS: enabled once per kernel instance
+        static bool lds_bf = false, lds_f = false;
+        const bool bf = pool->desc.io_dtype == GDN_BF16;
+        bool& done = bf ? lds_bf : lds_f;
+        if (!done) {
+            const hipError_t e = bf ? hipFuncSetAttribute(reinterpret_cast<const void*>(&in_proj_skinny_kernel<uint16_t>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyLds)
+                                    : hipFuncSetAttribute(reinterpret_cast<const void*>(&in_proj_skinny_kernel<float>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyLds);
+            if (e != hipSuccess) return e;
+            done = true;
+        }
+        const dim3 grid((o.n_out + 63) / 64);
+        if (bf)
+            hipLaunchKernelGGL(in_proj_skinny_kernel<uint16_t>, grid, dim3(kSkinnyThreads), kSkinnyLds,
+                               stream, xs, ws, (int)M, H, o);
+        else
+            hipLaunchKernelGGL(in_proj_skinny_kernel<float>, grid, dim3(kSkinnyThreads), kSkinnyLds,
+                               stream, xs, ws, (int)M, H, o);
+        return hipGetLastError();
+    }
     const int ks = in_proj_ksplit(pool, M, H);
     const int nblk = H / BK, per = (nblk + ks - 1) / ks;
     float* part = ks > 1 ? static_cast<float*>(workspace) : nullptr;
     const dim3 grid((o.n_out + BN - 1) / BN, (unsigned)((M + BM - 1) / BM), ks);
-    const auto* xs = static_cast<const uint16_t*>(x);
-    const auto* ws = static_cast<const uint16_t*>(w);
     if (pool->desc.io_dtype == GDN_BF16)
         hipLaunchKernelGGL(in_proj_gemm_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, xs, ws,
                            (int)M, H, o, part, per);
