@@ -14,6 +14,8 @@ from gpu_util import (check_f32, check_out, dev, host, load_slots, make_pool, or
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
+from oracle import gdn_oracle as O  # noqa: E402
+
 
 @pytest.fixture(scope="module", autouse=True)
 def _need_gpu():
@@ -225,3 +227,50 @@ def test_one_call_path_requires_a_flushed_ring():
     with pytest.raises(G.GdnError) as ei:
         plain.ring_flush(0, ids)
     assert ei.value.status == -2
+
+
+def test_ring_layers_are_independent_and_accept_len_is_clamped():
+    """Two layers: ring calls on layer 1 leave layer 0 bitwise unchanged, ring
+    counts are per layer, and accept_len outside 0..n_tok is clamped (9 acts
+    as n_tok, -3 as 0), as the oracle's verify clamps nothing but is given
+    the clamped values."""
+    s, io, n_tok = syn.Shapes(2, 4, 64, 64, 4), "bf16", 3
+    say("ring: two layers, clamped accept_len")
+    rng = np.random.default_rng(900)
+    n_slots, ids_np = 6, np.array([4, 1], np.int32)
+    contents = syn.draw_pool_contents(901, ids_np, s, io, n_layers=2)
+    pool = make_pool(s, n_slots, io, n_layers=2, ring_len=8)
+    load_slots(pool, contents)
+    l0 = (pool.state[:, 0].clone(), pool.window[:, 0].clone(), pool.ring_count[:, 0].clone())
+    w_np = syn.draw_conv_weights(rng, s)
+    w = dev(w_np)
+    ids = dev(ids_np, torch.int32)
+    op = O.OraclePool(2, 1, s)
+    for j, sl in enumerate(ids_np):
+        op.S[j, 0], op.X[j, 0] = contents[int(sl)][0][1], contents[int(sl)][1][1]
+    outs, refs = [], []
+    for acc_raw in ([9, -3], [2, 9], [1, 1]):
+        tok = syn.draw_tokens(rng, s, (2, n_tok), io)
+        td = tokens_to_dev(tok, io)
+        out = torch.full((2, n_tok, s.h_v, s.d_v), float("nan"), dtype=pool.io_torch, device="cuda")
+        pool.ring_verify(1, ids, n_tok, td["q"], td["k"], td["v"], td["a"], td["b"], w, out)
+        refs.append(op.verify(0, np.arange(2), n_tok, tok["q"], tok["k"], tok["v"], tok["a"],
+                              tok["b"], w_np, np.zeros(2, np.int32)))
+        outs.append(host(out))
+        pool.ring_commit(1, ids, n_tok, td["q"], td["k"], td["v"], td["a"], td["b"], w,
+                         dev(np.array(acc_raw, np.int32), torch.int32))
+        op.verify(0, np.arange(2), n_tok, tok["q"], tok["k"], tok["v"], tok["a"], tok["b"], w_np,
+                  np.clip(np.array(acc_raw), 0, n_tok).astype(np.int32))
+    torch.cuda.synchronize()
+    # counts: 3 then 0 (slot 4: 3, then 3+2=5, then 6); slot 1: 0, then 3, then 4
+    assert pool.ring_count[4, 1].item() == 6 and pool.ring_count[1, 1].item() == 4
+    assert torch.equal(pool.ring_count[:, 0], l0[2]), "layer 0 ring counts changed"
+    check_out("draft outputs", np.array(outs), np.array(refs), io)
+    pool.ring_flush(1, ids)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(ids_np.astype(np.int64)).cuda()
+    check_f32("layer-1 states after flush", host(pool.state[idx, 1]), op.S[:, 0])
+    assert np.array_equal(host(pool.window[idx, 1]), op.X[:, 0])
+    assert torch.equal(pool.state[:, 0], l0[0]) and torch.equal(pool.window[:, 0], l0[1]), \
+        "layer 0 changed"
+    assert pool.error() == 0
