@@ -37,10 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 # same way (profiles/decode_hbm_traffic.txt).  Valid only for the kernel
 # source they were taken on: DECODE_SRC_SHA256 is checked at run time and the
 # traffic is reported as null when the source has changed since.
-DECODE_TRAFFIC = {"fetch_kib": 67794.5, "write_kib": 134768.0,
+DECODE_TRAFFIC = {"fetch_kib": 67809.96, "write_kib": 134768.33,
                   "copy_fetch_scale": 536870912 / (262155.95 * 1024),
                   "copy_write_scale": 536870912 / (524288.0 * 1024)}
-DECODE_SRC_SHA256 = "08e24e0af70fe899cf5a9f07220e50a66bc30351c4fd003e372642c811c0726b"
+DECODE_SRC_SHA256 = "1e4b87dcc30e5ae143f21cc3d2b9e3dc009d43daa6b5bba1386b3f65d859981a"
 
 
 # Executed bf16 MFMA flops of the prefill kernels per token, from rocprofv3

@@ -108,10 +108,6 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
             s[p][4] = x1.x; s[p][5] = x1.y; s[p][6] = x1.z; s[p][7] = x1.w;
         }
     };
-    // Issue the first round's state loads before the conv front end so the
-    // HBM stream overlaps it.
-    if (sub < G) load_tile(tile_rsrc(slot_state + (int64_t)(g * G + sub) * D * D, kTileBytes));
-
     // LDS: line [K-1+n_tok][nch] raw inputs (window rows, then tokens),
     //      act  [n_tok][nch]     conv+SiLU outputs,
     //      nrm  [n_tok][3]       q scale, k scale, k.q
@@ -121,11 +117,80 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
     float* act = line + L * nch;
     float* nrm = act + n_tok * nch;
     float* obuf = line;   // [n_tok][G][D] outputs; reuses `line` after the front end
-
-    // ---- front end: depthwise causal conv + SiLU over the group's channels.
     T* win = reinterpret_cast<T*>(P.window) +
              ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
-    for (int c = tid; c < nch; c += nthr) {
+    const auto first_tiles = [&]() {
+        if (sub < G) load_tile(tile_rsrc(slot_state + (int64_t)(g * G + sub) * D * D, kTileBytes));
+    };
+
+    // ---- front end: depthwise causal conv + SiLU over the group's channels.
+    // Verify in the common shape (conv_k = 4, one channel per thread, at most
+    // kFastTok tokens): the raw inputs are loaded into registers first and the
+    // state tiles after them, so the conv waits only for its own data while
+    // the state streams in (loads complete in order).  Otherwise, and for
+    // decode (measured slightly faster that way), the state loads go first
+    // and the conv follows from LDS.
+    constexpr int kFastTok = 4;
+    const bool fast = NTOK == 0 && K == 4 && nch <= nthr && n_tok <= kFastTok;   // uniform
+    if (fast) {
+        const int c = min(tid, nch - 1);
+        int gc;
+        const T* src;
+        int64_t tstride;
+        if (c < D) {
+            gc = g * D + c;
+            src = q + ((int64_t)i * n_tok * P.h_k + g) * D + c;
+            tstride = (int64_t)P.h_k * D;
+        } else if (c < 2 * D) {
+            gc = P.h_k * D + g * D + (c - D);
+            src = k + ((int64_t)i * n_tok * P.h_k + g) * D + (c - D);
+            tstride = (int64_t)P.h_k * D;
+        } else {
+            gc = 2 * P.h_k * D + g * G * D + (c - 2 * D);
+            src = v + ((int64_t)i * n_tok * P.h_v + g * G) * D + (c - 2 * D);
+            tstride = (int64_t)P.h_v * D;
+        }
+        constexpr int NX = 3 + kFastTok;
+        T rx[NX];
+        float wc[4];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) rx[r] = win[(int64_t)r * C + gc];
+#pragma unroll
+        for (int t = 0; t < kFastTok; ++t) rx[3 + t] = src[(t < n_tok ? t : 0) * tstride];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wc[j] = conv_w[(int64_t)gc * 4 + j];
+        first_tiles();
+        asm volatile("" ::: "memory");   // keep the state loads after the conv inputs
+        if (tid < nch) {
+            // Same accumulation order as the general loop below, so decode
+            // and verify positions stay bitwise equal.
+#pragma unroll
+            for (int t = 0; t < kFastTok; ++t) {
+                if (t < n_tok) {
+                    float z = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) z = fmaf(wc[j], Io<T>::load(rx, t + j), z);
+                    act[t * nch + c] = silu(z);
+                }
+            }
+            // Roll the window by `commit` tokens: row r takes input commit + r.
+            if (commit > 0) {
+#pragma unroll
+                for (int r = 0; r < 3; ++r) {
+                    T x = rx[r + 1];
+#pragma unroll
+                    for (int m = 2; m <= kFastTok; ++m)
+                        if (commit == m) x = rx[r + m];
+                    win[(int64_t)r * C + gc] = x;
+                }
+            }
+        }
+    } else {
+        // Issue the first round's state loads before the conv front end so the
+        // HBM stream overlaps it.
+        first_tiles();
+    }
+    for (int c = fast ? nch : tid; c < nch; c += nthr) {
         int gc;             // global channel
         const T* src;       // token 0 of this channel
         int64_t tstride;    // element stride between tokens
