@@ -37,10 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 # same way (profiles/decode_hbm_traffic.txt).  Valid only for the kernel
 # source they were taken on: DECODE_SRC_SHA256 is checked at run time and the
 # traffic is reported as null when the source has changed since.
-DECODE_TRAFFIC = {"fetch_kib": 67809.96, "write_kib": 134768.33,
+DECODE_TRAFFIC = {"fetch_kib": 67794.47, "write_kib": 134801.43,
                   "copy_fetch_scale": 536870912 / (262155.95 * 1024),
                   "copy_write_scale": 536870912 / (524288.0 * 1024)}
-DECODE_SRC_SHA256 = "1e4b87dcc30e5ae143f21cc3d2b9e3dc009d43daa6b5bba1386b3f65d859981a"
+DECODE_SRC_SHA256 = "a76ba518f4d11af4040c52d255ec6d01aae76f16550d4852a272ba6087cf6a98"
 
 
 # Executed bf16 MFMA flops of the prefill kernels per token, from rocprofv3

@@ -52,7 +52,9 @@ __global__ __launch_bounds__(kRowThreads * kRowHeads) void decode_rows_kernel(
     const int K = KC > 0 ? KC : P.conv_k, C = P.c_conv;
     constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
     const int nch = 2 * D + G * RB;   // q, k, then the v channels of this block's rows
-    const int sub = tid / kRowThreads, ht = tid % kRowThreads;
+    // Wave-uniform (kRowThreads is a multiple of 64); said so to the compiler,
+    // so the row descriptors live in scalar registers.
+    const int sub = __builtin_amdgcn_readfirstlane(tid / kRowThreads), ht = tid % kRowThreads;
     const int lr = ht % LPR, lrow0 = ht / LPR;
     const int c0 = 4 * lr, c1 = D / 2 + 4 * lr;
     const int voff = (lrow0 * D + c0) * (int)sizeof(float);

@@ -85,7 +85,9 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
     constexpr int LPR = D / 8;
     constexpr int RPP = kHeadThreads / LPR;
     constexpr int NP = (D + RPP - 1) / RPP;
-    const int sub = tid / kHeadThreads;
+    // Wave-uniform (a tile is a whole number of waves); said so to the
+    // compiler, so the tile descriptors live in scalar registers.
+    const int sub = __builtin_amdgcn_readfirstlane(tid / kHeadThreads);
     const int ht = tid % kHeadThreads;
     const int lr = ht % LPR;
     const int row0 = ht / LPR;
@@ -111,11 +113,19 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
     // LDS: line [K-1+n_tok][nch] raw inputs (window rows, then tokens),
     //      act  [n_tok][nch]     conv+SiLU outputs,
     //      nrm  [n_tok][3]       q scale, k scale, k.q
+    //      gate [2][n_tok][G]    a, then b, of the group's value heads
     //      obuf [n_tok][G][D]    outputs, over `line` once the front end is done
     const int L = K - 1 + n_tok;
     float* line = smem;
     float* act = line + L * nch;
     float* nrm = act + n_tok * nch;
+    float* gate = nrm + n_tok * 3;
+    const int ngate = 2 * n_tok * G;
+    // Gate e of the staged set: a (e < n_tok*G) or b, token t, group head hl.
+    const auto gate_src = [&](int e) {
+        const int which = e >= n_tok * G, rem = which ? e - n_tok * G : e;
+        return (which ? b : a) + ((int64_t)i * n_tok + rem / G) * P.h_v + g * G + rem % G;
+    };
     float* obuf = line;   // [n_tok][G][D] outputs; reuses `line` after the front end
     T* win = reinterpret_cast<T*>(P.window) +
              ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
@@ -131,6 +141,7 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
     // decode (measured slightly faster that way), the state loads go first
     // and the conv follows from LDS.
     constexpr int kFastTok = 4;
+    const float graw = *gate_src(min(tid, ngate - 1));   // issued ahead of the state
     const bool fast = NTOK == 0 && K == 4 && nch <= nthr && n_tok <= kFastTok;   // uniform
     if (fast) {
         const int c = min(tid, nch - 1);
@@ -220,6 +231,8 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
             for (int r = 0; r < K - 1; ++r)
                 Io<T>::store(win, (int64_t)r * C + gc, line[(commit + r) * nch + c]);
     }
+    if (tid < ngate) gate[tid] = graw;
+    for (int e = tid + nthr; e < ngate; e += nthr) gate[e] = *gate_src(e);
     __syncthreads();
 
     // ---- q/k normalisation factors and k.q per token (one wave per token).
@@ -265,9 +278,8 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
                 kc[e] = y[D + c0 + e] * rk;
                 kc[4 + e] = y[D + c1 + e] * rk;
             }
-            const int64_t tok = (int64_t)i * n_tok + t;
-            const float at = a[tok * P.h_v + hv];
-            const float bt = b[tok * P.h_v + hv];
+            const float at = gate[t * G + hl];
+            const float bt = gate[(n_tok + t) * G + hl];
             float* o_row = obuf + (t * G + hl) * D;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(kHeadThreads * kMaxHeadsPerBlock) void decode_verif
 size_t lds_bytes(const PoolView& P, int n_tok) {
     const int G = P.h_v / P.h_k;
     return (size_t)(P.conv_k - 1 + 2 * n_tok) * (2 + G) * P.d * sizeof(float) +
-           (size_t)n_tok * 3 * sizeof(float);
+           (size_t)n_tok * (3 + 2 * G) * sizeof(float);
 }
 
 template <int D, typename T>
