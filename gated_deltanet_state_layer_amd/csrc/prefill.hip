@@ -80,6 +80,7 @@ struct Ws {
     int32_t* hdr;        // [0]: number of chunks, or -1 if cu_seqlens is malformed
     int32_t* seq_coff;   // [n_seq+1] first global chunk of each sequence
     int4* crec;          // [max_chunks][2] per chunk: {sequence, slot, s0, len}, {position, 0, 0, 0}
+    int4* srec;          // [n_seq][2] sequences in scan order: {sequence, slot, s0, len}, {first chunk, chunks, 0, 0}
     bf16x8* qkf;         // [max_chunks][h_k][nqk fragments]
     bf16x8* tpf;         // [max_chunks][h_v][ntp fragments]; all-zero ones unwritten
     float* gl;           // [max_chunks][h_v][CP] cumulative log-decay in the chunk
@@ -112,6 +113,7 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
     const size_t o_hdr = take(256);
     const size_t o_coff = take((size_t)(n_seq + 1) * 4);
     const size_t o_cseq = take((size_t)mc * 2 * sizeof(int4));
+    const size_t o_srec = take((size_t)n_seq * 2 * sizeof(int4));
     const size_t o_qk = take((size_t)mc * P.h_k * gm.nqk() * fb);
     const size_t o_tp = take((size_t)mc * P.h_v * gm.ntp() * fb);
     const size_t o_g = take((size_t)mc * P.h_v * gm.CP * 4);
@@ -121,6 +123,7 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
     w.hdr = reinterpret_cast<int32_t*>(b + o_hdr);
     w.seq_coff = reinterpret_cast<int32_t*>(b + o_coff);
     w.crec = reinterpret_cast<int4*>(b + o_cseq);
+    w.srec = reinterpret_cast<int4*>(b + o_srec);
     w.qkf = reinterpret_cast<bf16x8*>(b + o_qk);
     w.tpf = reinterpret_cast<bf16x8*>(b + o_tp);
     w.gl = reinterpret_cast<float*>(b + o_g);
@@ -133,8 +136,13 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
 // and write each chunk's record (its sequence, slot, start, length and
 // position), so a factor workgroup finds all of it with one load.  A malformed cu_seqlens marks
 // the workspace invalid (the other kernels then do nothing) and sets the
-// sticky error bit.
+// sticky error bit.  It also writes one record per sequence in the order the
+// scan takes them: most chunks first (ties by index) when there are at most
+// kSortMax sequences, else in index order.  The scan's serial chain is
+// as long as its sequence, so starting the longest chains first keeps short
+// ones from leaving a long one alone at the end.
 constexpr int kPrepThreads = 1024;
+constexpr int kSortMax = 1024;
 
 __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     PoolView P, Ws W, const int32_t* __restrict__ cu, const int32_t* __restrict__ slot_ids, int n_seq,
@@ -186,6 +194,23 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
         W.hdr[0] = n_chunks;
     }
     __syncthreads();
+    // Sequence records in scan order: rank = number of sequences that come
+    // before j (more chunks, or as many and a lower index).
+    for (int j = tid; j < n_seq; j += kPrepThreads) {
+        const int c0 = in_lds ? s_coff[j] : W.seq_coff[j];
+        const int nj = (in_lds ? s_coff[j + 1] : W.seq_coff[j + 1]) - c0;
+        int rank = j;
+        if (n_seq <= kSortMax) {   // implies in_lds
+            rank = 0;
+            for (int i = 0; i < n_seq; ++i) {
+                const int ni = s_coff[i + 1] - s_coff[i];
+                rank += (ni > nj) | ((ni == nj) & (i < j));
+            }
+        }
+        const int s = cu[j];
+        W.srec[2 * rank] = make_int4(j, slot_ids[j], s, cu[j + 1] - s);
+        W.srec[2 * rank + 1] = make_int4(c0, nj, 0, 0);
+    }
     // Chunk records, one thread per chunk: the owning sequence is the j with
     // coff[j] <= chunk < coff[j+1] (binary search; empty sequences own none).
     for (int ch = tid; ch < n_chunks; ch += kPrepThreads) {
@@ -693,29 +718,42 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
-    // Work unit u = (seq * h_v + h) * (D/16) + rb.  Consecutive workgroup ids
-    // go to different XCDs (round robin over 8); when the unit count allows,
-    // give each XCD a contiguous range of units so the row blocks of one head
-    // (which read the same chunk operands) share that XCD's L2.
+    // Work units: sequence jj of the scan order, q/k head g, and the G * D/16
+    // (value head, row block) pairs of that group.  Consecutive workgroup ids
+    // go to different XCDs (round robin over 8).  When the (jj, g) count is a
+    // multiple of 8, (jj, g) goes to XCD (jj * h_k + g) % 8 with all of its
+    // workgroups, so the row blocks and value heads that read the same chunk
+    // operands share that XCD's L2, every sequence is spread over all XCDs,
+    // and each XCD starts its units in scan order (longest sequence first).
     constexpr int NRB = D / kRows;
-    const int n_units = gridDim.x;
+    const int G = P.h_v / P.h_k;
     const int bid = blockIdx.x;
-    const int u = (n_units % 8 == 0) ? (bid % 8) * (n_units / 8) + bid / 8 : bid;
-    const int rb = u % NRB, h = (u / NRB) % P.h_v, j = u / (NRB * P.h_v);
+    int jj, g, r;
+    if ((gridDim.x / (G * NRB)) % 8 == 0) {
+        const int i = bid / 8, ku = (i / (G * NRB)) * 8 + bid % 8;
+        jj = ku / P.h_k;
+        g = ku % P.h_k;
+        r = i % (G * NRB);
+    } else {
+        jj = bid / (NRB * P.h_v);
+        g = (bid / (G * NRB)) % P.h_k;
+        r = bid % (G * NRB);
+    }
+    const int h = g * G + r / NRB, rb = r % NRB;
     if (W.hdr[0] < 0) return;
-    const int slot = slot_ids[j];
+    const int4 sr0 = W.srec[2 * jj], sr1 = W.srec[2 * jj + 1];
+    const int j = sr0.x, slot = sr0.y;
     if (slot < 0) return;
     if (slot >= P.n_slots) {
         if (tid == 0 && rb == 0 && h == 0) atomicOr(P.err, kErrSlotRange);
         return;
     }
-    const int64_t s0 = cu[j];
-    const int len = cu[j + 1] - (int)s0;
+    const int64_t s0 = sr0.z;
+    const int len = sr0.w;
     if (len <= 0) return;
-    const int G = P.h_v / P.h_k, g = h / G;
     const int K = KC > 0 ? KC : P.conv_k, C = P.c_conv;
     constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
-    const int ci0 = W.seq_coff[j], n_ch = W.seq_coff[j + 1] - ci0;
+    const int ci0 = sr1.x, n_ch = sr1.y;
     const int row0 = rb * kRows;
     T* win = reinterpret_cast<T*>(P.window) + ((int64_t)slot * P.n_layers + layer) * (int64_t)(K - 1) * C;
     const int gc0 = 2 * P.h_k * D + h * D + row0;   // first v channel of the block
