@@ -7,7 +7,9 @@
 // | h_v a logits | h_v b logits; x and W are bf16, products are exact in fp32
 // and accumulate in fp32 on the bf16 matrix cores.
 //
-// Up to 64 tokens: the skinny kernel below.  Otherwise the
+// Up to 64 tokens: the skinny kernel below.  From 512 tokens (when the hidden
+// dimension is not split): the 256 x 128 tile kernel, plus the skinny kernel
+// for the channels past its last full 128-channel column.  Otherwise the
 // gemm kernel: grid (N/128, M/128, ksplit), 4 waves, a 128 x 128 output tile
 // per workgroup; k-blocks of 32 go through LDS, double buffered, loaded with
 // 16-byte buffer loads whose descriptors return zeros past the ragged ends.
@@ -136,8 +138,120 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
     }
 }
 
+// Many tokens: a 256 x 128 output tile per workgroup, wave (wm, wn) owning a
+// 128 x 64 block (8 x 4 MFMA tiles), so each wave reads 384 bytes of LDS
+// operands per MFMA instead of the 512 of a 64 x 64 block, and each k-block
+// of 32 runs 32 MFMAs per wave between barriers.  k-blocks go through LDS,
+// double buffered as above.  It covers the full 128-channel
+// columns only: the channels past the last of them (the gate logits when
+// the q|k|v channels are a multiple of 128) go to the skinny kernel below,
+// 64 tokens per workgroup, in a second short launch.  A partial column
+// would add a fifth round of tiles at 8192 tokens (2080 tiles over 512
+// workgroup slots) for 1/128 of the work.
+constexpr int BM2 = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
+    int n_tn) {
+    __shared__ __align__(16) uint16_t sa[2][BM2 * LDK];
+    __shared__ __align__(16) uint16_t sb[2][BN * LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m16 = lane & 15, q4 = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int N = o.n_out;
+    const int n_tm = (M + BM2 - 1) / BM2;
+    // Tile order: column-major (consecutive ids share their W rows).  A
+    // banded order that gives each XCD a compact 8 x 8 group of tiles was
+    // measured no faster (385 vs 379 us at 8192 tokens).
+    const int t = blockIdx.x;
+    if (t >= n_tm * n_tn) return;
+    const int tm = t % n_tm, tn = t / n_tm;
+    const int m0 = tm * BM2, n0 = tn * BN;
+    const int nblk = H / BK;
+    const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
+    // staging: vector e = tid + 256 i of a tile is row e / 4, k 8 (e % 4);
+    // x: 4 vectors per thread (256 rows), W: 2 (128 rows).  Rows past M or N
+    // read zeros (offset past the descriptor).
+    int ga[4], gb[2], la[4], lb[2];
+    bool va_ok[4], vb_ok[2];
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+        const int e = tid + i2 * kThreads, r = e >> 2, kv = (e & 3) * 8;
+        va_ok[i2] = m0 + r < M;
+        ga[i2] = va_ok[i2] ? ((m0 + r) * H + kv) * 2 : 0;
+        la[i2] = r * LDK + kv;
+    }
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+        const int e = tid + i2 * kThreads, r = e >> 2, kv = (e & 3) * 8;
+        vb_ok[i2] = n0 + r < N;
+        gb[i2] = vb_ok[i2] ? ((n0 + r) * H + kv) * 2 : 0;
+        lb[i2] = r * LDK + kv;
+    }
+    uint4 va[4], vb[2];
+    auto fetch = [&](int kb) {
+        const bool ok = kb < nblk;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2)
+            va[i2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                x_rs, ok && va_ok[i2] ? ga[i2] + kb * BK * 2 : kOffOOB, 0, 0));
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+            vb[i2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                w_rs, ok && vb_ok[i2] ? gb[i2] + kb * BK * 2 : kOffOOB, 0, 0));
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) *reinterpret_cast<uint4*>(&sa[buf][la[i2]]) = va[i2];
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) *reinterpret_cast<uint4*>(&sb[buf][lb[i2]]) = vb[i2];
+    };
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    fetch(0);
+    stage(0);
+    __syncthreads();
+    for (int kb = 0; kb < nblk; ++kb) {
+        const int buf = kb & 1;
+        fetch(kb + 1);
+        bf16x8 fa[8], fb[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+            fb[nt] = *reinterpret_cast<const bf16x8*>(&sb[buf][(wn * 64 + nt * 16 + m16) * LDK + q4 * 8]);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            fa[mt] = *reinterpret_cast<const bf16x8*>(&sa[buf][(wm * 128 + mt * 16 + m16) * LDK + q4 * 8]);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
+        stage(buf ^ 1);
+        __syncthreads();
+    }
+    // lane holds y[m0 + 128 wm + 16 mt + 4 q + j][n0 + 64 wn + 16 nt + m16]
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int n = n0 + wn * 64 + nt * 16 + m16;
+        if (n >= N) continue;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = m0 + wm * 128 + mt * 16 + q4 * 4 + j;
+                if (m < M) put<T>(o, m, n, acc[mt][nt][j]);
+            }
+    }
+}
+
 // Few tokens (M <= 64): the weight stream is the whole cost.  One workgroup
-// of 8 waves per 64 output channels; wave w multiplies the full 64 x 64 tile
+// of 8 waves per 64 output channels and 64 tokens (grid y; also used for the
+// channels past the last full column of the 256-token-tile kernel); wave w
+// multiplies the full 64 x 64 tile
 // over its eighth of the hidden dimension, operands straight from memory into
 // MFMA registers (16 bytes per lane, one step ahead), and the eight partial
 // tiles are added in LDS before the fused epilogue.  No partial sums leave
@@ -148,18 +262,19 @@ constexpr size_t kSkinnyLds = (size_t)kSkinnyWaves * 64 * 64 * sizeof(float);
 
 template <typename T>
 __global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
+    int c0) {
     extern __shared__ __align__(16) float red[];     // [8 waves][64 tokens][64 channels]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
-    const int N = o.n_out, n0 = blockIdx.x * 64;
+    const int N = o.n_out, n0 = c0 + blockIdx.x * 64, m0 = blockIdx.y * 64;
     const int nsteps = H / 32, per = (nsteps + kSkinnyWaves - 1) / kSkinnyWaves;
     const int s_begin = wave * per, s_end = min(nsteps, s_begin + per);
     const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
     int xo[4], wo[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        xo[t] = ((t * 16 + m16) * H) * 2 + q4 * 16;         // tokens past M read zeros
+        xo[t] = ((m0 + t * 16 + m16) * H) * 2 + q4 * 16;    // tokens past M read zeros
         wo[t] = ((n0 + t * 16 + m16) * H) * 2 + q4 * 16;    // channels past N read zeros
     }
     auto fetch = [&](int st, bf16x8* xf, bf16x8* wf) {
@@ -193,7 +308,7 @@ __global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[mt], wb[nt], acc[mt][nt], 0, 0, 0);
         }
     }
-    // lane holds y[16 mt + 4 q + j][n0 + 16 nt + m16]
+    // lane holds y[m0 + 16 mt + 4 q + j][n0 + 16 nt + m16]
     float* mine = red + wave * 64 * 64;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -203,7 +318,7 @@ __global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
             for (int j = 0; j < 4; ++j) mine[(mt * 16 + q4 * 4 + j) * 64 + nt * 16 + m16] = acc[mt][nt][j];
     __syncthreads();
     for (int idx = tid; idx < 64 * 64; idx += kSkinnyThreads) {
-        const int m = idx >> 6, n = n0 + (idx & 63);
+        const int m = m0 + (idx >> 6), n = n0 + (idx & 63);
         if (m >= M || n >= N) continue;
         float y = 0.f;
 #pragma unroll
@@ -226,6 +341,10 @@ __global__ __launch_bounds__(kThreads) void in_proj_epilogue_kernel(const float*
 }
 
 }  // namespace
+
+// From this many tokens (and no split of the hidden dimension) the 256 x 128
+// tile kernel runs.
+constexpr int64_t kWideMinTokens = 512;
 
 // Split of the hidden dimension for M tokens: enough workgroups to keep the
 // weight stream busy, at least 4 k-blocks of 32 per split.
@@ -250,10 +369,11 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
     ProjOut o{q, k, v, a, b, P.h_k * P.d, P.h_v * P.d, P.c_conv, P.h_v, P.c_conv + 2 * P.h_v};
     const auto* xs = static_cast<const uint16_t*>(x);
     const auto* ws = static_cast<const uint16_t*>(w);
-    if (M <= 64) {
+    const bool bf = pool->desc.io_dtype == GDN_BF16;
+    // Skinny kernel over channels [c0, n_out) and all M tokens, 64 x 64 per workgroup.
+    auto skinny = [&](int c0) -> hipError_t {
         // more than 64 KiB of dynamic LDS: enabled once per kernel instance
         static bool lds_bf = false, lds_f = false;
-        const bool bf = pool->desc.io_dtype == GDN_BF16;
         bool& done = bf ? lds_bf : lds_f;
         if (!done) {
             const hipError_t e = bf ? hipFuncSetAttribute(reinterpret_cast<const void*>(&in_proj_skinny_kernel<uint16_t>),
@@ -263,16 +383,31 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
             if (e != hipSuccess) return e;
             done = true;
         }
-        const dim3 grid((o.n_out + 63) / 64);
+        const dim3 grid((o.n_out - c0 + 63) / 64, (unsigned)((M + 63) / 64));
         if (bf)
             hipLaunchKernelGGL(in_proj_skinny_kernel<uint16_t>, grid, dim3(kSkinnyThreads), kSkinnyLds,
-                               stream, xs, ws, (int)M, H, o);
+                               stream, xs, ws, (int)M, H, o, c0);
         else
             hipLaunchKernelGGL(in_proj_skinny_kernel<float>, grid, dim3(kSkinnyThreads), kSkinnyLds,
-                               stream, xs, ws, (int)M, H, o);
+                               stream, xs, ws, (int)M, H, o, c0);
         return hipGetLastError();
-    }
+    };
+    if (M <= 64) return skinny(0);
     const int ks = in_proj_ksplit(pool, M, H);
+    const int n_full = o.n_out / BN;   // full 128-channel columns
+    if (ks == 1 && M >= kWideMinTokens && n_full > 0) {
+        const int tiles = (int)((M + BM2 - 1) / BM2) * n_full;
+        const dim3 grid((unsigned)tiles);
+        if (bf)
+            hipLaunchKernelGGL(in_proj_wide_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, xs, ws,
+                               (int)M, H, o, n_full);
+        else
+            hipLaunchKernelGGL(in_proj_wide_kernel<float>, grid, dim3(kThreads), 0, stream, xs, ws,
+                               (int)M, H, o, n_full);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess || n_full * BN == o.n_out) return e;
+        return skinny(n_full * BN);
+    }
     const int nblk = H / BK, per = (nblk + ks - 1) / ks;
     float* part = ks > 1 ? static_cast<float*>(workspace) : nullptr;
     const dim3 grid((o.n_out + BN - 1) / BN, (unsigned)((M + BM - 1) / BM), ks);

@@ -26,7 +26,7 @@ The recurrence itself (the gated delta rule) is the layer's definition:
     S_t = a_t * S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t
 with S a [d_v, d_k] matrix per value head ([P2] "[V,K]" state).  The pages
 name the rule but do not print it; every reading taken where they are silent
-is listed at the top of the design doc and repeated next to the code it affects:
+is listed below and repeated next to the code it affects:
 
   R1  conv: depthwise causal, all q, k and v channels, no bias; tap
       conv_k-1 multiplies the current token, tap 0 the oldest; the window

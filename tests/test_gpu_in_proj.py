@@ -1,7 +1,9 @@
 """GPU parity of the input projection (gdn_in_proj) against the fp64 oracle:
-the raw q, k, v and the activated gates, on the split-hidden path (few
-tokens) and the one-pass path, with ragged token and channel counts, and the
-projection feeding a decode step."""
+the raw q, k, v and the activated gates, on the skinny path (up to 64
+tokens), the split-hidden path, the 128-token-tile path and the 256-token-tile
+path (from 512 tokens; 1000 and 2100 tokens leave ragged row tiles and a
+partial band), with ragged token and channel counts, and the projection
+feeding a decode step."""
 import numpy as np
 import pytest
 
@@ -39,7 +41,7 @@ def _project(pool, s, x_np, w_np, io):
     return q, k, v, a, b, nb
 
 
-@pytest.mark.parametrize("n_tok", [1, 64, 300, 1024])
+@pytest.mark.parametrize("n_tok", [1, 64, 300, 1024, 1000, 2100])
 def test_in_proj_qwen3_next_vs_oracle(n_tok):
     s, io, hidden = syn.QWEN3_NEXT, "bf16", syn.QWEN3_NEXT_HIDDEN
     rng = np.random.default_rng(1100 + n_tok)
@@ -62,6 +64,7 @@ def test_in_proj_qwen3_next_vs_oracle(n_tok):
     (2, 2, 32, 96, 7, "f32"),        # 196 output channels: a ragged 16-channel tile
     (1, 3, 64, 160, 70, "bf16"),     # 3 gates each: gate rows straddle a tile
     (2, 4, 128, 4096, 5, "bf16"),    # long hidden, split 16 ways
+    (2, 4, 64, 96, 700, "f32"),      # 256-token tiles: ragged rows, an 8-channel last tile
 ])
 def test_in_proj_other_shapes(h_k, h_v, d, hidden, n_tok, io):
     s = syn.Shapes(h_k, h_v, d, d, 4)
