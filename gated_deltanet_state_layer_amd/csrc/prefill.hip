@@ -143,6 +143,7 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
 // ones from leaving a long one alone at the end.
 constexpr int kPrepThreads = 1024;
 constexpr int kSortMax = 1024;
+constexpr int kFusedPrepMax = 64;   // up to this many sequences the factor kernel does the prep
 
 __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(
     PoolView P, Ws W, const int32_t* __restrict__ cu, const int32_t* __restrict__ slot_ids, int n_seq,
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ q,
     const T* __restrict__ k, const float* __restrict__ a, const float* __restrict__ b,
-    const float* __restrict__ conv_w, Ckpt ck) {
+    const float* __restrict__ conv_w, Ckpt ck, int fused_n_seq, int total, int max_chunks) {
     constexpr int LD = 2 * D + 4;      // row of the staged q|k lines (floats)
     constexpr int LT = CP + 4;         // padded row of A, T, P (16-byte aligned)
     constexpr int NT = CP / 16;        // token tiles
@@ -290,14 +291,77 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
     const int ci = blockIdx.x, g = blockIdx.y;
-    const int4 rec0 = W.crec[2 * ci], rec1 = W.crec[2 * ci + 1];   // read with the count
-    const int n_chunks = W.hdr[0];
-    if (ci >= n_chunks) return;        // also when the workspace is invalid (-1)
-    const int j = rec0.x, slot = rec0.y;
+    int j, slot, len, cpos;   // sequence, its slot and length, chunk index inside it
+    int64_t s0;
+    if (fused_n_seq > 0) {
+        // At most 64 sequences: no prep launch.  Wave 0 of every workgroup
+        // checks cu_seqlens and prefix-sums the chunk counts (one lane per
+        // sequence) and finds the sequence owning chunk ci; workgroup (0, 0)
+        // also writes the header and the scan's sequence records (as the
+        // prep kernel does).
+        __shared__ int s_rec[6];
+        if (wave == 0) {
+            const int n = fused_n_seq;
+            const bool in = lane < n;
+            const int cs = in ? cu[lane] : 0, ce = in ? cu[lane + 1] : 0;
+            const int sl = in ? slot_ids[lane] : 0;
+            const bool bad_j = in && (cs < 0 || ce < cs || ce > total);
+            const int nj = in && !bad_j ? (ce - cs + chunk - 1) / chunk : 0;
+            int incl = nj;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {   // inclusive prefix sum over the wave
+                const int y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            const int excl = incl - nj, n_chunks = __shfl(incl, 63);
+            const bool bad = __any(bad_j) || __shfl(cs, 0) != 0 || __shfl(ce, n - 1) != total ||
+                             n_chunks > max_chunks;
+            const unsigned long long own = __ballot(in && ci >= excl && ci < incl);
+            const int jo = own ? __ffsll((unsigned long long)own) - 1 : 0;
+            const int o_cs = __shfl(cs, jo), o_ce = __shfl(ce, jo), o_sl = __shfl(sl, jo);
+            const int o_ex = __shfl(excl, jo);
+            if (ci == 0 && g == 0) {
+                int rank = 0;   // scan order: more chunks first, ties by index
+                for (int i = 0; i < n; ++i) {
+                    const int ni = __shfl(nj, i);
+                    rank += (ni > nj) | ((ni == nj) & (i < lane));
+                }
+                if (lane == 0) {
+                    W.hdr[0] = bad ? -1 : n_chunks;
+                    if (bad) atomicOr(P.err, kErrSeqlens);
+                }
+                if (in && !bad) {
+                    W.srec[2 * rank] = make_int4(lane, sl, cs, ce - cs);
+                    W.srec[2 * rank + 1] = make_int4(excl, nj, 0, 0);
+                }
+            }
+            if (lane == 0) {
+                s_rec[0] = bad || !own;
+                s_rec[1] = jo;
+                s_rec[2] = o_sl;
+                s_rec[3] = o_cs;
+                s_rec[4] = o_ce - o_cs;
+                s_rec[5] = ci - o_ex;
+            }
+        }
+        __syncthreads();
+        if (s_rec[0]) return;
+        j = s_rec[1];
+        slot = s_rec[2];
+        s0 = s_rec[3];
+        len = s_rec[4];
+        cpos = s_rec[5];
+    } else {
+        const int4 rec0 = W.crec[2 * ci], rec1 = W.crec[2 * ci + 1];   // read with the count
+        const int n_chunks = W.hdr[0];
+        if (ci >= n_chunks) return;        // also when the workspace is invalid (-1)
+        j = rec0.x;
+        slot = rec0.y;
+        s0 = rec0.z;
+        len = rec0.w;
+        cpos = rec1.x;
+    }
     if (slot < 0 || slot >= P.n_slots) return;
-    const int64_t s0 = rec0.z;
-    const int len = rec0.w;
-    const int cpos = rec1.x;                      // chunk index inside the sequence
     const int64_t t0 = s0 + (int64_t)cpos * chunk;
     const int L = min(chunk, len - cpos * chunk); // valid tokens in this chunk
     const int K = KC > 0 ? KC : P.conv_k, C = P.c_conv, G = P.h_v / P.h_k;
@@ -1160,13 +1224,17 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
     if (e != hipSuccess) return e;
     e = allow_lds(&prefill_scan_kernel<D, CP, KC, T>, ls, &scan_lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, P, W, cu,
-                       slot_ids, n_seq, total, chunk, mc);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // Up to 64 sequences the factor kernel builds the chunk records itself.
+    const int fused = n_seq <= kFusedPrepMax ? n_seq : 0;
+    if (!fused) {
+        hipLaunchKernelGGL(prefill_prep_kernel, dim3(1), dim3(kPrepThreads), 0, stream, P, W, cu,
+                           slot_ids, n_seq, total, chunk, mc);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
                        stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
-                       static_cast<const T*>(k), a, b, conv_w, ck);
+                       static_cast<const T*>(k), a, b, conv_w, ck, fused, total, mc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<D, CP, KC, T>), dim3((D / kRows) * P.h_v * n_seq),

@@ -291,6 +291,70 @@ def test_malformed_cu_seqlens_is_flagged_and_touches_nothing():
     assert torch.equal(pool.state, st0) and torch.equal(pool.window, wn0)
 
 
+def test_many_sequences_vs_oracle():
+    """More sequences (100) than the factor kernel books itself (64), so the
+    separate prep kernel builds the chunk map: short sequences, some empty,
+    two padding entries, slots continuing from pre-filled contents."""
+    s, io, chunk = syn.Shapes(1, 2, 32, 32, 4), "f32", 16
+    say(f"100 sequences: {s} chunk={chunk}")
+    rng = np.random.default_rng(77)
+    n, n_slots = 100, 128
+    lens = rng.integers(0, 41, n)
+    ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
+    ids_np[[5, 50]] = -1
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    w_np = syn.draw_conv_weights(rng, s)
+    tok = syn.draw_tokens(rng, s, (T,), io)
+    pool = make_pool(s, n_slots, io)
+    contents = syn.draw_pool_contents(8, ids_np[ids_np >= 0][:12], s, io)
+    load_slots(pool, contents)
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    out = run_prefill(pool, 0, cu, ids_np, tok, dev(w_np), chunk, io)
+    torch.cuda.synchronize()
+    assert pool.error() == 0
+    valid = ids_np >= 0
+    op = oracle_pool(s, contents, np.where(valid, ids_np, 0), form="rank1")
+    op.S[~valid] = 0.0
+    ref = op.prefill(0, cu, np.where(valid, np.arange(n), -1), tok["q"], tok["k"], tok["v"],
+                     tok["a"], tok["b"], w_np)
+    rows = np.concatenate([np.arange(cu[j], cu[j + 1]) for j in range(n) if valid[j]])
+    check_out("outputs", host(out)[rows], ref[rows], io)
+    for jj, sl in enumerate(ids_np):
+        if sl < 0:
+            continue
+        if lens[jj] == 0:   # a zero-length sequence leaves its slot bitwise unchanged
+            assert torch.equal(pool.state[int(sl)], st0[int(sl)]), f"state of slot {sl}"
+        else:
+            check_f32(f"state of slot {sl}", host(pool.state[int(sl)]), op.S[jj])
+        assert np.array_equal(host(pool.window[int(sl)]), op.X[jj]), f"window of slot {sl}"
+    untouched = np.setdiff1d(np.arange(n_slots), ids_np[valid])
+    idx = torch.from_numpy(untouched.astype(np.int64)).cuda()
+    assert torch.equal(pool.state[idx], st0[idx]) and torch.equal(pool.window[idx], wn0[idx])
+
+
+def test_malformed_cu_seqlens_many_sequences_is_flagged():
+    """The same check on the prep kernel's path (more than 64 sequences)."""
+    s, io = syn.Shapes(1, 2, 32, 32, 4), "f32"
+    say("malformed cu_seqlens, 70 sequences")
+    rng = np.random.default_rng(14)
+    w = dev(syn.draw_conv_weights(rng, s))
+    pool = make_pool(s, 80, io)
+    scramble_pool(pool, 15)
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    tok = syn.draw_tokens(rng, s, (140,), io)
+    good = np.arange(0, 141, 2, dtype=np.int32)   # 70 sequences of 2 tokens
+    bad_a = good.copy()
+    bad_a[40] = bad_a[38]                           # decreasing
+    bad_b = good.copy()
+    bad_b[0] = 1                                    # does not start at 0
+    for cu in (bad_a, bad_b):
+        out = run_prefill(pool, 0, cu, np.arange(70, dtype=np.int32), tok, w, 16, io)
+        assert pool.error() == 2
+        assert torch.isnan(out.float()).all()
+    assert torch.equal(pool.state, st0) and torch.equal(pool.window, wn0)
+
+
 def test_prefill_then_verify_and_decode_continue_the_sequence():
     """Prefill a prompt, then decode and verify steps continue from the
     prefilled state and window (Qwen3-Next shapes, one group checked)."""
