@@ -758,8 +758,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
 
 template <int D, int CP, int KC, typename T>
 __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
-    PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ v,
+    PoolView P, Ws W, int layer, int chunk, const T* __restrict__ v,
     const float* __restrict__ conv_w, T* __restrict__ out, Ckpt ck) {
     using S = ScanLds<D, CP>;
     constexpr int NKS = D / 32;       // 32-wide k-steps over d_k
@@ -1238,8 +1237,8 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<D, CP, KC, T>), dim3((D / kRows) * P.h_v * n_seq),
-                       dim3(kThreads), ls, stream, P, W, layer, cu, slot_ids, chunk,
-                       static_cast<const T*>(v), conv_w, static_cast<T*>(out), ck);
+                       dim3(kThreads), ls, stream, P, W, layer, chunk, static_cast<const T*>(v),
+                       conv_w, static_cast<T*>(out), ck);
     return hipGetLastError();
 }
 
