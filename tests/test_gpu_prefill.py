@@ -291,14 +291,16 @@ def test_malformed_cu_seqlens_is_flagged_and_touches_nothing():
     assert torch.equal(pool.state, st0) and torch.equal(pool.window, wn0)
 
 
-def test_many_sequences_vs_oracle():
-    """More sequences (100) than the factor kernel books itself (64), so the
-    separate prep kernel builds the chunk map: short sequences, some empty,
-    two padding entries, slots continuing from pre-filled contents."""
+@pytest.mark.parametrize("n", [64, 65, 100])
+def test_many_sequences_vs_oracle(n):
+    """Up to 64 sequences the factor kernel books the chunks itself; beyond,
+    the separate prep kernel builds the chunk map (64 and 65 sit on either
+    side of that boundary): short sequences, some empty, two padding
+    entries, slots continuing from pre-filled contents."""
     s, io, chunk = syn.Shapes(1, 2, 32, 32, 4), "f32", 16
-    say(f"100 sequences: {s} chunk={chunk}")
-    rng = np.random.default_rng(77)
-    n, n_slots = 100, 128
+    say(f"{n} sequences: {s} chunk={chunk}")
+    rng = np.random.default_rng(77 + n)
+    n_slots = 128
     lens = rng.integers(0, 41, n)
     ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
     ids_np[[5, 50]] = -1
