@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdn.h"
 
 namespace gdn {
@@ -109,6 +111,24 @@ hipError_t launch_slot_reset(const gdn_pool* pool, int32_t n, const int32_t* slo
                              hipStream_t stream);
 hipError_t launch_slot_copy(const gdn_pool* pool, int32_t n, const int32_t* src_ids,
                             const int32_t* dst_ids, hipStream_t stream);
+// More than 64 KiB of dynamic LDS has to be enabled per kernel (gfx950 has
+// 160 KiB per CU).  Done once per kernel and device: `done` holds one bit per
+// device id below 64 (set with release order once the attribute is in
+// place; devices from 64 on set it on every call), so concurrent first calls
+// from several host threads at worst set the same attribute twice.
+template <typename KFn>
+hipError_t allow_dynamic_lds(KFn* kernel, size_t bytes, std::atomic<uint64_t>* done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done->load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess && bit) done->fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 // Prefill checkpoints: after every `every_chunks` chunks of sequence j,
 // checkpoint m goes to slot slots[off[j] + m] (if m < off[j+1] - off[j]).
 struct Ckpt {

@@ -372,17 +372,11 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
     const bool bf = pool->desc.io_dtype == GDN_BF16;
     // Skinny kernel over channels [c0, n_out) and all M tokens, 64 x 64 per workgroup.
     auto skinny = [&](int c0) -> hipError_t {
-        // more than 64 KiB of dynamic LDS: enabled once per kernel instance
-        static bool lds_bf = false, lds_f = false;
-        bool& done = bf ? lds_bf : lds_f;
-        if (!done) {
-            const hipError_t e = bf ? hipFuncSetAttribute(reinterpret_cast<const void*>(&in_proj_skinny_kernel<uint16_t>),
-                                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyLds)
-                                    : hipFuncSetAttribute(reinterpret_cast<const void*>(&in_proj_skinny_kernel<float>),
-                                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkinnyLds);
-            if (e != hipSuccess) return e;
-            done = true;
-        }
+        // more than 64 KiB of dynamic LDS: enabled once per kernel and device
+        static std::atomic<uint64_t> lds_bf{0}, lds_f{0};
+        const hipError_t e = bf ? allow_dynamic_lds(&in_proj_skinny_kernel<uint16_t>, kSkinnyLds, &lds_bf)
+                                : allow_dynamic_lds(&in_proj_skinny_kernel<float>, kSkinnyLds, &lds_f);
+        if (e != hipSuccess) return e;
         const dim3 grid((o.n_out - c0 + 63) / 64, (unsigned)((M + 63) / 64));
         if (bf)
             hipLaunchKernelGGL(in_proj_skinny_kernel<uint16_t>, grid, dim3(kSkinnyThreads), kSkinnyLds,

@@ -1199,29 +1199,18 @@ size_t factor_lds_bytes() {
     return a > b ? a : b;
 }
 
-// More than 64 KiB of dynamic LDS has to be enabled per kernel (gfx950 has
-// 160 KiB per CU); done once per kernel instance.
-template <typename KFn>
-hipError_t allow_lds(KFn* kernel, size_t bytes, bool* done) {
-    if (*done) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) *done = true;
-    return e;
-}
-
 template <int D, int CP, int KC, typename T>
 hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
                       const int32_t* cu, const int32_t* slot_ids, int total, int chunk, int mc,
                       const void* q, const void* k, const void* v, const float* a, const float* b,
                       const float* conv_w, void* out, Ckpt ck, hipStream_t stream) {
     const PoolView& P = pool->view;
-    static bool factor_lds = false, scan_lds = false;
+    static std::atomic<uint64_t> factor_lds{0}, scan_lds{0};
     const size_t lf = factor_lds_bytes<D, CP>();
     const size_t ls = ScanLds<D, CP>::bytes;
-    hipError_t e = allow_lds(&prefill_factor_kernel<D, CP, KC, T>, lf, &factor_lds);
+    hipError_t e = allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, T>, lf, &factor_lds);
     if (e != hipSuccess) return e;
-    e = allow_lds(&prefill_scan_kernel<D, CP, KC, T>, ls, &scan_lds);
+    e = allow_dynamic_lds(&prefill_scan_kernel<D, CP, KC, T>, ls, &scan_lds);
     if (e != hipSuccess) return e;
     // Up to 64 sequences the factor kernel builds the chunk records itself.
     const int fused = n_seq <= kFusedPrepMax ? n_seq : 0;
