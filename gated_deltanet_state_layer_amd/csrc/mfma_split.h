@@ -20,13 +20,29 @@ struct Frag {
     bf16x8 hi, lo;
 };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Split of two floats: hi = their bf16 pair (one packed conversion), the
+// fp32 values of the two halves by a shift and a mask, lo = the packed bf16
+// of the two exact differences.  Bitwise the same as converting each value
+// on its own, in six instructions per pair instead of eight.
+__device__ __forceinline__ void split2(float a, float b, bf16x2& hi, bf16x2& lo) {
+    hi = bf16x2{(__bf16)a, (__bf16)b};
+    const uint32_t h = __builtin_bit_cast(uint32_t, hi);
+    const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xffff0000u);
+    lo = bf16x2{(__bf16)(a - ha), (__bf16)(b - hb)};
+}
+
 __device__ __forceinline__ Frag split8(const float* x) {
     Frag r;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const __bf16 h = (__bf16)x[j];
-        r.hi[j] = h;
-        r.lo[j] = (__bf16)(x[j] - (float)h);
+    for (int j = 0; j < 8; j += 2) {
+        bf16x2 h, l;
+        split2(x[j], x[j + 1], h, l);
+        r.hi[j] = h[0];
+        r.hi[j + 1] = h[1];
+        r.lo[j] = l[0];
+        r.lo[j + 1] = l[1];
     }
     return r;
 }

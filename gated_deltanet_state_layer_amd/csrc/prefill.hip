@@ -57,10 +57,13 @@ __device__ __forceinline__ Frag load_frag(const bf16x8* base, int f, int lane) {
 __device__ __forceinline__ void store_frag4(bf16x8* base, int f, int dl, int e0, const float* x) {
     bf16x4 h, l;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 hh = (__bf16)x[i];
-        h[i] = hh;
-        l[i] = (__bf16)(x[i] - (float)hh);
+    for (int i = 0; i < 4; i += 2) {
+        bf16x2 hh, ll;
+        split2(x[i], x[i + 1], hh, ll);
+        h[i] = hh[0];
+        h[i + 1] = hh[1];
+        l[i] = ll[0];
+        l[i + 1] = ll[1];
     }
     *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base + f * kFragVecs + dl) + e0) = h;
     *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base + f * kFragVecs + 64 + dl) + e0) = l;
