@@ -177,3 +177,38 @@ def test_graph_replayed_ring_cycle_equals_eager():
         assert torch.equal(pa.window, pb.window), f"replay {r}: windows differ"
     assert folded, "no replay folded a ring"
     assert pa.error() == 0
+
+
+@pytest.mark.parametrize("n_tok", [64, 300, 1000])
+def test_graph_replayed_in_proj_equals_eager(n_tok):
+    """The input projection on each of its paths (skinny; split hidden with
+    the partial-sum kernel; 256-token tiles plus the skinny gate strip),
+    recorded once and replayed with new hidden states, equals eager calls
+    bitwise at every replay."""
+    s, hidden = syn.QWEN3_NEXT, syn.QWEN3_NEXT_HIDDEN
+    say(f"graph in_proj: {n_tok} tokens")
+    rng = np.random.default_rng(970 + n_tok)
+    pool = make_pool(s, 1, "bf16")
+    w = dev(syn.draw_in_proj_weight(rng, s, hidden), torch.bfloat16)
+    x = torch.zeros((n_tok, hidden), dtype=torch.bfloat16, device="cuda")
+    nb = pool.in_proj_workspace_bytes(n_tok, hidden)
+
+    def outs():
+        return {"q": torch.zeros((n_tok, s.h_k, s.d_k), dtype=torch.bfloat16, device="cuda"),
+                "k": torch.zeros((n_tok, s.h_k, s.d_k), dtype=torch.bfloat16, device="cuda"),
+                "v": torch.zeros((n_tok, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda"),
+                "a": torch.zeros((n_tok, s.h_v), device="cuda"),
+                "b": torch.zeros((n_tok, s.h_v), device="cuda"),
+                "ws": torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda") if nb else None}
+
+    oa, ob = outs(), outs()
+    g = _capture(lambda: pool.in_proj(x, w, oa["q"], oa["k"], oa["v"], oa["a"], oa["b"], oa["ws"]))
+    for r in range(3):
+        x.copy_(torch.from_numpy(syn.draw_hidden(rng, (n_tok,), hidden)).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        pool.in_proj(x, w, ob["q"], ob["k"], ob["v"], ob["a"], ob["b"], ob["ws"])
+        torch.cuda.synchronize()
+        for m in "qkvab":
+            assert torch.equal(oa[m], ob[m]), f"replay {r}: {m} differs"
+    assert pool.error() == 0
