@@ -50,7 +50,7 @@ DECODE_SRC_SHA256 = "a76ba518f4d11af4040c52d255ec6d01aae76f16550d4852a272ba6087c
 # source they were taken on (PREFILL_SRC_SHA256), else reported as null.
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
-PREFILL_SRC_SHA256 = "b8903032ab9e0476a0a62c31d327efa59d1525ade0b686dd6268ced039d9a5fe"
+PREFILL_SRC_SHA256 = "db39f8bb118bd015e7cc9065d346fdbb72fa57b8ec9d718f9d0703312b0db3dd"
 
 
 def prefill_exec_flop_per_token(case):

@@ -13,12 +13,17 @@
 //     O       = diag(gamma) Q S0^T + P U,  P[t][s] = exp(g_t - g_s) q_t.k_s (s <= t)
 //     S       = exp(g_last) S0 + U^T diag(exp(g_last - g)) K
 //
-// Three kernels, stream-ordered, no host synchronisation:
-//   prep   (1 workgroup)             chunk map from the device cu_seqlens;
+// Kernels, stream-ordered, no host synchronisation:
+//   prep   (1 workgroup)             chunk map and scan order from the device
+//                                    cu_seqlens (only with more than 64
+//                                    sequences; otherwise the factor kernel
+//                                    builds them itself);
 //   factor (chunk x q/k head)        conv+SiLU, q/k normalisation, KK^T and QK^T
 //                                    on bf16 MFMA, T' and P per value head;
 //   scan   (seq x v head x 16 rows)  the serial chunk carry on bf16 MFMA, the
-//                                    state block kept in registers.
+//                                    state block kept in registers; sequences
+//                                    taken longest first, each spread over
+//                                    all XCDs.
 // Every MFMA operand that is not an exact bf16 value is split as hi + lo bf16
 // and multiplied as hi*hi + hi*lo + lo*hi (fp32 accumulate), which keeps the
 // chunked result within fp32-recurrence accuracy.  The factor kernel writes
@@ -261,7 +266,9 @@ template <> struct Vec<float> {
 
 // ------------------------------------------------------------------ factor
 
-// grid (max_chunks, h_k), 256 threads.  Dynamic LDS: the chunk's raw q|k rows
+// grid (max_chunks, h_k), 256 threads; with fused_n_seq > 0 (at most 64
+// sequences) each workgroup finds its chunk from cu_seqlens itself, else it
+// reads the prep kernel's chunk record.  Dynamic LDS: the chunk's raw q|k rows
 // (conv_k-1 rows of left context, then CP tokens), overwritten in place by
 // the conv+SiLU outputs and normalised; later reused for A, T and P.
 // KC > 0: conv taps fixed at compile time (must equal conv_k); 0: runtime.
