@@ -257,10 +257,13 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
 // tiles are added in LDS before the fused epilogue.  No partial sums leave
 // the chip and there is no second launch.
 constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyStages = 4;   // k-steps of operand loads in flight per wave
 constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
 constexpr size_t kSkinnyLds = (size_t)kSkinnyWaves * 64 * 64 * sizeof(float);
 
-template <typename T>
+// NS > 0: each wave's k-step count fixed at compile time (the loop below is
+// then straight-line code with exact waits); 0: any count.
+template <typename T, int NS>
 __global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
     int c0) {
@@ -290,22 +293,40 @@ __global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 xa[4], wa[4], xb[4], wb[4];
-    fetch(s_begin, xa, wa);
-    for (int st = s_begin; st < s_end; st += 2) {
-        fetch(st + 1, xb, wb);
+    // Up to kSkinnyStages k-steps of loads in flight per wave: a step's MFMAs
+    // take ~0.1 us, the loads ~1-2 us, so one step of prefetch would leave
+    // every step waiting a whole memory latency.  Each stage's registers are
+    // refilled right after its MFMAs.  Steps past the wave's range load zeros
+    // (no memory access).
+    bf16x8 xs[kSkinnyStages][4], ws[kSkinnyStages][4];
+    auto mma_stage = [&](int i) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], wa[nt], acc[mt][nt], 0, 0, 0);
-        fetch(st + 2, xa, wa);
-        if (st + 1 < s_end) {
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xs[i][mt], ws[i][nt], acc[mt][nt], 0, 0, 0);
+    };
+    if constexpr (NS > 0) {
+        // Straight-line pipeline.  The scheduling barriers keep each stage's
+        // loads where they are written: left alone, the scheduler sinks them
+        // next to their MFMAs to save registers, and every step waits again.
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+        for (int i = 0; i < kSkinnyStages && i < NS; ++i) fetch(s_begin + i, xs[i], ws[i]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[mt], wb[nt], acc[mt][nt], 0, 0, 0);
+        for (int j = 0; j < NS; ++j) {
+            mma_stage(j % kSkinnyStages);
+            if (j + kSkinnyStages < NS) fetch(s_begin + j + kSkinnyStages, xs[j % kSkinnyStages], ws[j % kSkinnyStages]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        // Any step count: two stages, one step ahead.
+        fetch(s_begin, xs[0], ws[0]);
+        for (int st = s_begin; st < s_end; st += 2) {
+            fetch(st + 1, xs[1], ws[1]);
+            mma_stage(0);
+            fetch(st + 2, xs[0], ws[0]);
+            mma_stage(1);   // zeros past the range
         }
     }
     // lane holds y[m0 + 16 mt + 4 q + j][n0 + 16 nt + m16]
@@ -374,15 +395,26 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
     auto skinny = [&](int c0) -> hipError_t {
         // more than 64 KiB of dynamic LDS: enabled once per kernel and device
         static std::atomic<uint64_t> lds_bf{0}, lds_f{0};
-        const hipError_t e = bf ? allow_dynamic_lds(&in_proj_skinny_kernel<uint16_t>, kSkinnyLds, &lds_bf)
-                                : allow_dynamic_lds(&in_proj_skinny_kernel<float>, kSkinnyLds, &lds_f);
+        static std::atomic<uint64_t> lds_bf8{0}, lds_f8{0};
+        const bool ns8 = (H / 32 + kSkinnyWaves - 1) / kSkinnyWaves == 8;   // e.g. hidden 2048
+        const hipError_t e =
+            bf ? (ns8 ? allow_dynamic_lds(&in_proj_skinny_kernel<uint16_t, 8>, kSkinnyLds, &lds_bf8)
+                      : allow_dynamic_lds(&in_proj_skinny_kernel<uint16_t, 0>, kSkinnyLds, &lds_bf))
+               : (ns8 ? allow_dynamic_lds(&in_proj_skinny_kernel<float, 8>, kSkinnyLds, &lds_f8)
+                      : allow_dynamic_lds(&in_proj_skinny_kernel<float, 0>, kSkinnyLds, &lds_f));
         if (e != hipSuccess) return e;
         const dim3 grid((o.n_out - c0 + 63) / 64, (unsigned)((M + 63) / 64));
-        if (bf)
-            hipLaunchKernelGGL(in_proj_skinny_kernel<uint16_t>, grid, dim3(kSkinnyThreads), kSkinnyLds,
+        if (bf && ns8)
+            hipLaunchKernelGGL((in_proj_skinny_kernel<uint16_t, 8>), grid, dim3(kSkinnyThreads), kSkinnyLds,
+                               stream, xs, ws, (int)M, H, o, c0);
+        else if (bf)
+            hipLaunchKernelGGL((in_proj_skinny_kernel<uint16_t, 0>), grid, dim3(kSkinnyThreads), kSkinnyLds,
+                               stream, xs, ws, (int)M, H, o, c0);
+        else if (ns8)
+            hipLaunchKernelGGL((in_proj_skinny_kernel<float, 8>), grid, dim3(kSkinnyThreads), kSkinnyLds,
                                stream, xs, ws, (int)M, H, o, c0);
         else
-            hipLaunchKernelGGL(in_proj_skinny_kernel<float>, grid, dim3(kSkinnyThreads), kSkinnyLds,
+            hipLaunchKernelGGL((in_proj_skinny_kernel<float, 0>), grid, dim3(kSkinnyThreads), kSkinnyLds,
                                stream, xs, ws, (int)M, H, o, c0);
         return hipGetLastError();
     };
