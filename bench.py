@@ -50,7 +50,7 @@ DECODE_SRC_SHA256 = "a76ba518f4d11af4040c52d255ec6d01aae76f16550d4852a272ba6087c
 # source they were taken on (PREFILL_SRC_SHA256), else reported as null.
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
-PREFILL_SRC_SHA256 = "db39f8bb118bd015e7cc9065d346fdbb72fa57b8ec9d718f9d0703312b0db3dd"
+PREFILL_SRC_SHA256 = "900a1ca1b0eb155a1fa9c45e61a31d87ec63d6f4e64fc682b5738aa576f3f629"
 
 
 def prefill_exec_flop_per_token(case):

@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         for (int m = 0; m < KM; ++m) w[m] = m < K ? conv_w[(int64_t)gc * K + m] : 0.f;
 #pragma unroll
         for (int m = 0; m < KM - 1; ++m) line[m] = m < K - 1 ? xr[m * LD + c] : 0.f;
-#pragma unroll 4
+#pragma unroll 16
         for (int t = 0; t < CP; ++t) {
             const float x = xr[(t + K - 1) * LD + c];
             float z = 0.f;
