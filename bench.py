@@ -576,7 +576,7 @@ def cpu_other(syn):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the GDN state layer benchmark runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
     import gated_deltanet_state_layer_amd as G

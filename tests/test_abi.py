@@ -120,3 +120,15 @@ def test_status_strings(lib):
     for s in (-1, -2, -3, -4, -5, -6):
         assert B.status_string(s) != "unknown status"
     assert B.status_string(42) == "unknown status"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it prints a JSON error line
+    and exits with status 2 before touching a device."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "--gpus must be 1" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
