@@ -110,6 +110,25 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, numel, dtype):
+    """Host-side check of a tensor argument before it becomes a raw pointer:
+    a contiguous device tensor of `dtype` with at least `numel` elements, so
+    that no kernel reads or writes past it.  A call that touches no element
+    of it (numel 0) accepts anything, None included."""
+    if numel <= 0:
+        return
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: not a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the call needs {numel}")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -198,19 +217,39 @@ class Pool:
         except Exception:
             pass
 
+    # -- argument checks (shapes follow include/gdn.h) ----------------------
+    def _tokens(self, rows, q, k, v, a, b, conv_w):
+        d, io = self.desc, self.io_torch
+        _need(q, "q", rows * d.h_k * d.d_k, io)
+        _need(k, "k", rows * d.h_k * d.d_k, io)
+        _need(v, "v", rows * d.h_v * d.d_v, io)
+        _need(a, "a", rows * d.h_v, torch.float32)
+        _need(b, "b", rows * d.h_v, torch.float32)
+        _need(conv_w, "conv_w", self.c_conv * d.conv_k if rows else 0, torch.float32)
+
+    def _out(self, rows, out):
+        _need(out, "out", rows * self.desc.h_v * self.desc.d_v, self.io_torch)
+
     # -- calls -------------------------------------------------------------
     def reset(self, slot_ids, stream=None):
         lib = load_library()
+        _need(slot_ids, "slot_ids", slot_ids.numel(), torch.int32)
         _check(lib.gdn_slot_reset(self._h, int(slot_ids.numel()), _ptr(slot_ids), _stream(stream)),
                "gdn_slot_reset")
 
     def copy(self, src_ids, dst_ids, stream=None):
         lib = load_library()
+        _need(src_ids, "src_ids", src_ids.numel(), torch.int32)
+        _need(dst_ids, "dst_ids", src_ids.numel(), torch.int32)
         _check(lib.gdn_slot_copy(self._h, int(src_ids.numel()), _ptr(src_ids), _ptr(dst_ids),
                                  _stream(stream)), "gdn_slot_copy")
 
     def decode(self, layer, slot_ids, q, k, v, a, b, conv_w, out, stream=None):
         lib = load_library()
+        n = int(slot_ids.numel())
+        _need(slot_ids, "slot_ids", n, torch.int32)
+        self._tokens(n, q, k, v, a, b, conv_w)
+        self._out(n, out)
         _check(lib.gdn_decode_step(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), _ptr(q),
                                    _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w), _ptr(out),
                                    _stream(stream)), "gdn_decode_step")
@@ -218,6 +257,13 @@ class Pool:
 
     def verify(self, layer, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len, out, stream=None):
         lib = load_library()
+        n = int(slot_ids.numel())
+        _need(slot_ids, "slot_ids", n, torch.int32)
+        self._tokens(n * n_tok, q, k, v, a, b, conv_w)
+        if accept_len is not None:
+            _need(accept_len, "accept_len", n, torch.int32)
+        if out is not None:   # None: commit only
+            self._out(n * n_tok, out)
         _check(lib.gdn_verify_step(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), n_tok,
                                    _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
                                    _ptr(accept_len), _ptr(out), _stream(stream)),
@@ -226,6 +272,10 @@ class Pool:
 
     def ring_verify(self, layer, slot_ids, n_tok, q, k, v, a, b, conv_w, out, stream=None):
         lib = load_library()
+        n = int(slot_ids.numel())
+        _need(slot_ids, "slot_ids", n, torch.int32)
+        self._tokens(n * n_tok, q, k, v, a, b, conv_w)
+        self._out(n * n_tok, out)
         _check(lib.gdn_ring_verify(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), n_tok,
                                    _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
                                    _ptr(out), _stream(stream)), "gdn_ring_verify")
@@ -233,12 +283,17 @@ class Pool:
 
     def ring_commit(self, layer, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len, stream=None):
         lib = load_library()
+        n = int(slot_ids.numel())
+        _need(slot_ids, "slot_ids", n, torch.int32)
+        self._tokens(n * n_tok, q, k, v, a, b, conv_w)
+        _need(accept_len, "accept_len", n, torch.int32)
         _check(lib.gdn_ring_commit(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids), n_tok,
                                    _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
                                    _ptr(accept_len), _stream(stream)), "gdn_ring_commit")
 
     def ring_flush(self, layer, slot_ids, stream=None):
         lib = load_library()
+        _need(slot_ids, "slot_ids", slot_ids.numel(), torch.int32)
         _check(lib.gdn_ring_flush(self._h, layer, int(slot_ids.numel()), _ptr(slot_ids),
                                   _stream(stream)), "gdn_ring_flush")
 
@@ -253,6 +308,14 @@ class Pool:
         """x [n_tok][hidden] bf16, w [C_conv + 2 h_v][hidden] bf16 -> q, k, v, a, b."""
         lib = load_library()
         n_tok, hidden = int(x.shape[0]), int(x.shape[1])
+        d = self.desc
+        _need(x, "x", n_tok * hidden, torch.bfloat16)
+        _need(w, "w", (self.c_conv + 2 * d.h_v) * hidden if n_tok else 0, torch.bfloat16)
+        _need(q, "q", n_tok * d.h_k * d.d_k, self.io_torch)
+        _need(k, "k", n_tok * d.h_k * d.d_k, self.io_torch)
+        _need(v, "v", n_tok * d.h_v * d.d_v, self.io_torch)
+        _need(a, "a", n_tok * d.h_v, torch.float32)
+        _need(b, "b", n_tok * d.h_v, torch.float32)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib.gdn_in_proj(self._h, n_tok, hidden, _ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(a), _ptr(b), _ptr(workspace), ws_bytes, _stream(stream)),
@@ -269,6 +332,7 @@ class Pool:
                 out, workspace=None, stream=None):
         lib = load_library()
         n_seq = int(slot_ids.numel())
+        self._prefill_args(n_seq, cu_seqlens, slot_ids, total_tokens, q, k, v, a, b, conv_w, out)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib.gdn_prefill_chunked(self._h, layer, n_seq, _ptr(cu_seqlens), _ptr(slot_ids),
                                        total_tokens, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
@@ -281,6 +345,11 @@ class Pool:
                      stream=None):
         lib = load_library()
         n_seq = int(slot_ids.numel())
+        self._prefill_args(n_seq, cu_seqlens, slot_ids, total_tokens, q, k, v, a, b, conv_w, out)
+        if ckpt_every > 0:
+            _need(ckpt_offsets, "ckpt_offsets", n_seq + 1, torch.int32)
+            _need(ckpt_slots, "ckpt_slots", 0 if ckpt_slots is None else ckpt_slots.numel(),
+                  torch.int32)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib.gdn_prefill_chunked_ckpt(self._h, layer, n_seq, _ptr(cu_seqlens),
                                             _ptr(slot_ids), total_tokens, chunk, _ptr(q), _ptr(k),
@@ -289,6 +358,13 @@ class Pool:
                                             _ptr(workspace), ws_bytes, _stream(stream)),
                "gdn_prefill_chunked_ckpt")
         return out
+
+    def _prefill_args(self, n_seq, cu_seqlens, slot_ids, total_tokens, q, k, v, a, b, conv_w,
+                      out):
+        _need(slot_ids, "slot_ids", n_seq, torch.int32)
+        _need(cu_seqlens, "cu_seqlens", n_seq + 1 if n_seq else 0, torch.int32)
+        self._tokens(int(total_tokens), q, k, v, a, b, conv_w)
+        self._out(int(total_tokens), out)
 
     def error(self, stream=None) -> int:
         lib = load_library()

@@ -81,3 +81,41 @@ def test_empty_calls_are_no_ops(io):
     pool.in_proj(x, wp, q, k, v, a, b)
     assert _unchanged(pool, snap)
     assert pool.error() == 0
+
+
+def test_binding_rejects_undersized_or_mistyped_tensors():
+    """The binding checks each tensor argument on the host (device,
+    contiguity, dtype, element count against the call's shapes) before it
+    becomes a raw pointer; a bad one raises ValueError and nothing runs."""
+    s, io = syn.Shapes(2, 4, 64, 64, 4), "bf16"
+    say("binding argument checks")
+    pool = make_pool(s, 4, io)
+    scramble_pool(pool, 6)
+    snap = _snapshot(pool)
+    n = 2
+    ids = dev(np.array([0, 1], np.int32), torch.int32)
+    w = dev(syn.draw_conv_weights(np.random.default_rng(4), s))
+    good = {"q": torch.zeros((n, s.h_k, s.d_k), dtype=torch.bfloat16, device="cuda"),
+            "k": torch.zeros((n, s.h_k, s.d_k), dtype=torch.bfloat16, device="cuda"),
+            "v": torch.zeros((n, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda"),
+            "a": torch.ones((n, s.h_v), device="cuda"),
+            "b": torch.zeros((n, s.h_v), device="cuda")}
+    out = torch.zeros((n, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
+    bad_cases = {
+        "v": good["v"][:1],                                   # too few elements
+        "q": good["q"].float(),                               # wrong dtype
+        "a": torch.ones((s.h_v, n), device="cuda").t(),       # not contiguous
+        "b": good["b"].cpu(),                                 # not on the device
+    }
+    for name, bad in bad_cases.items():
+        args = dict(good)
+        args[name] = bad
+        with pytest.raises(ValueError):
+            pool.decode(0, ids, args["q"], args["k"], args["v"], args["a"], args["b"], w, out)
+    with pytest.raises(ValueError):
+        pool.decode(0, ids.long(), good["q"], good["k"], good["v"], good["a"], good["b"], w, out)
+    with pytest.raises(ValueError):
+        pool.decode(0, ids, good["q"], good["k"], good["v"], good["a"], good["b"], w, out[:1])
+    assert _unchanged(pool, snap)
+    pool.decode(0, ids, good["q"], good["k"], good["v"], good["a"], good["b"], w, out)
+    assert pool.error() == 0
