@@ -36,6 +36,7 @@ struct ProjOut {
     void *q, *k, *v;
     float *a, *b;
     int hkd, hvd, c_conv, h_v, n_out;
+    int vec8;   // q, k, v 16-byte aligned and hkd, hvd, c_conv multiples of 8
 };
 
 // Output channel n of token m: a raw q/k/v value or an activated gate.
@@ -46,6 +47,43 @@ __device__ __forceinline__ void put(const ProjOut& o, int64_t m, int n, float y)
     else if (n < o.c_conv) Io<T>::store(static_cast<T*>(o.v), m * o.hvd + n - 2 * o.hkd, y);
     else if (n < o.c_conv + o.h_v) o.a[m * o.h_v + n - o.c_conv] = 1.0f / (1.0f + __expf(y));
     else o.b[m * o.h_v + n - o.c_conv - o.h_v] = 1.0f / (1.0f + __expf(-y));
+}
+
+// Outputs n .. n+7 of token m (n a multiple of 8).  With vec8, eight
+// channels below c_conv lie in one of q, k, v and go out as one 16-byte
+// (bf16) or two 16-byte (fp32) stores; otherwise (and for the gates) one by
+// one, skipping channels past n_out.
+template <typename T>
+__device__ __forceinline__ void put8(const ProjOut& o, int64_t m, int n, const float* y) {
+    if (o.vec8 && n < o.c_conv) {
+        T* dst;
+        int64_t off;
+        if (n < o.hkd) {
+            dst = static_cast<T*>(o.q);
+            off = m * o.hkd + n;
+        } else if (n < 2 * o.hkd) {
+            dst = static_cast<T*>(o.k);
+            off = m * o.hkd + n - o.hkd;
+        } else {
+            dst = static_cast<T*>(o.v);
+            off = m * o.hvd + n - 2 * o.hkd;
+        }
+        if constexpr (sizeof(T) == 2) {
+            uint4 pk;
+            pk.x = f32_to_bf16(y[0]) | (uint32_t)f32_to_bf16(y[1]) << 16;
+            pk.y = f32_to_bf16(y[2]) | (uint32_t)f32_to_bf16(y[3]) << 16;
+            pk.z = f32_to_bf16(y[4]) | (uint32_t)f32_to_bf16(y[5]) << 16;
+            pk.w = f32_to_bf16(y[6]) | (uint32_t)f32_to_bf16(y[7]) << 16;
+            *reinterpret_cast<uint4*>(dst + off) = pk;
+        } else {
+            *reinterpret_cast<float4*>(dst + off) = make_float4(y[0], y[1], y[2], y[3]);
+            *reinterpret_cast<float4*>(dst + off + 4) = make_float4(y[4], y[5], y[6], y[7]);
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (n + i < o.n_out) put<T>(o, m, n + i, y[i]);
 }
 
 // 128 x 128 output tile per workgroup (wave (wm, wn) owns a 64 x 64
@@ -233,18 +271,36 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
         stage(buf ^ 1);
         __syncthreads();
     }
+    // Epilogue through LDS: lane (m16, q4) holds rows 16 mt + 4 q4 + j of
+    // column 16 nt + m16 of the wave's 128 x 64 block, so stores straight from
+    // the accumulators write 2- or 4-byte pieces.  Each wave instead writes 32
+    // of its rows at a time to a private fp32 buffer in the (now free) operand
+    // LDS and reads them back as eight consecutive channels per lane for
+    // put8.  The last k-block's barrier has passed, so no wave still reads
+    // sa/sb; each wave touches only its own buffer, so no barrier is needed.
     // lane holds y[m0 + 128 wm + 16 mt + 4 q + j][n0 + 64 wn + 16 nt + m16]
+    constexpr int ER = 32, ELD = 64 + 4;   // rows per pass; padded row (floats)
+    static_assert(4 * ER * ELD * sizeof(float) <= sizeof(sa), "epilogue buffer fits in sa");
+    float* eb = reinterpret_cast<float*>(&sa[0][0]) + wave * ER * ELD;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int n = n0 + wn * 64 + nt * 16 + m16;
-        if (n >= N) continue;
+    for (int pass = 0; pass < 128 / ER; ++pass) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int mh = 0; mh < ER / 16; ++mh)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int m = m0 + wm * 128 + mt * 16 + q4 * 4 + j;
-                if (m < M) put<T>(o, m, n, acc[mt][nt][j]);
-            }
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    eb[(mh * 16 + q4 * 4 + j) * ELD + nt * 16 + m16] = acc[pass * (ER / 16) + mh][nt][j];
+        // read back: 32 rows x 8 groups of 8 channels = 4 groups per lane
+#pragma unroll
+        for (int it = 0; it < ER * 8 / 64; ++it) {
+            const int gidx = lane + it * 64, r = gidx >> 3, c8 = (gidx & 7) * 8;
+            const float4 p0 = *reinterpret_cast<const float4*>(eb + r * ELD + c8);
+            const float4 p1 = *reinterpret_cast<const float4*>(eb + r * ELD + c8 + 4);
+            const float y[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            const int m = m0 + wm * 128 + pass * ER + r, n = n0 + wn * 64 + c8;
+            if (m < M && n < N) put8<T>(o, m, n, y);
+        }
     }
 }
 
@@ -387,7 +443,10 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
                           void* q, void* k, void* v, float* a, float* b, void* workspace,
                           hipStream_t stream) {
     const PoolView& P = pool->view;
-    ProjOut o{q, k, v, a, b, P.h_k * P.d, P.h_v * P.d, P.c_conv, P.h_v, P.c_conv + 2 * P.h_v};
+    const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const int hkd = P.h_k * P.d, hvd = P.h_v * P.d;
+    ProjOut o{q, k, v, a, b, hkd, hvd, P.c_conv, P.h_v, P.c_conv + 2 * P.h_v,
+              al16(q) && al16(k) && al16(v) && hkd % 8 == 0 && hvd % 8 == 0 && P.c_conv % 8 == 0};
     const auto* xs = static_cast<const uint16_t*>(x);
     const auto* ws = static_cast<const uint16_t*>(w);
     const bool bf = pool->desc.io_dtype == GDN_BF16;
