@@ -82,6 +82,38 @@ def test_in_proj_other_shapes(h_k, h_v, d, hidden, n_tok, io):
     check_f32("b", host(b), rb)
 
 
+@pytest.mark.parametrize("h_k,h_v,d,hidden,n_tok,io", [
+    (16, 32, 128, 2048, 17, "f32"),   # 8256 channels, fp32 io, ragged tokens
+    (2, 4, 64, 1024, 64, "bf16"),     # 520 channels: an 8-channel last tile of gates
+    (4, 8, 64, 2048, 33, "bf16"),     # 1040 channels
+    (4, 20, 64, 1024, 9, "f32"),      # 1832 channels: 40 gate channels across a tile edge
+])
+def test_in_proj_few_tokens_repeated_calls(h_k, h_v, d, hidden, n_tok, io):
+    """Decode-sized batches (up to 64 tokens) at hidden 1024 and 2048, the
+    two step counts of the few-token kernel, with ragged last tiles: three
+    calls in a row, each matching the oracle, and a repeated input giving
+    bitwise the same outputs."""
+    s = syn.Shapes(h_k, h_v, d, d, 4)
+    rng = np.random.default_rng(1250 + hidden + n_tok)
+    w = syn.draw_in_proj_weight(rng, s, hidden)
+    pool = make_pool(s, 1, io)
+    xs = [syn.draw_hidden(rng, (n_tok,), hidden) for _ in range(2)]
+    outs = []
+    for call, x in enumerate(xs + xs[:1]):
+        q, k, v, a, b, nb = _project(pool, s, x, w, io)
+        say(f"in_proj few tokens: {s} hidden {hidden} tokens {n_tok} io {io} call {call} workspace {nb}")
+        rq, rk, rv, ra, rb = O.in_projection(x, w, s)
+        check_out("q", host(q), rq, io)
+        check_out("k", host(k), rk, io)
+        check_out("v", host(v), rv, io)
+        check_f32("a", host(a), ra)
+        check_f32("b", host(b), rb)
+        outs.append((q, k, v, a, b))
+    for t0, t2 in zip(outs[0], outs[2]):
+        assert torch.equal(t0, t2), "the same input gave different outputs"
+    assert pool.error() == 0
+
+
 def test_in_proj_feeds_decode():
     """Hidden states -> projection -> decode step, on both sides."""
     s, io, hidden = syn.QWEN3_NEXT, "bf16", syn.QWEN3_NEXT_HIDDEN
