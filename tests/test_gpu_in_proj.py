@@ -114,6 +114,41 @@ def test_in_proj_few_tokens_repeated_calls(h_k, h_v, d, hidden, n_tok, io):
     assert pool.error() == 0
 
 
+@pytest.mark.parametrize("n_tok,io", [(64, "bf16"), (1000, "bf16"), (300, "f32")])
+def test_in_proj_unaligned_outputs_equal_aligned(n_tok, io):
+    """q, k, v starting one element into their buffers (not 16-byte aligned)
+    go out element by element instead of as 16-byte vectors; the values are
+    bitwise those of the aligned call, on the few-token, 128-token-tile and
+    256-token-tile paths."""
+    s, hidden = syn.QWEN3_NEXT, syn.QWEN3_NEXT_HIDDEN
+    say(f"in_proj unaligned outputs: {n_tok} tokens io {io}")
+    rng = np.random.default_rng(1400 + n_tok)
+    x = dev(syn.draw_hidden(rng, (n_tok,), hidden), torch.bfloat16)
+    w = dev(syn.draw_in_proj_weight(rng, s, hidden), torch.bfloat16)
+    pool = make_pool(s, 1, io)
+    t = torch.bfloat16 if io == "bf16" else torch.float32
+
+    def outs(off):
+        def view(shape):
+            n = int(np.prod(shape))
+            return torch.full((n + off,), float("nan"), dtype=t, device="cuda")[off:].view(shape)
+        return (view((n_tok, s.h_k, s.d_k)), view((n_tok, s.h_k, s.d_k)), view((n_tok, s.h_v, s.d_v)),
+                torch.full((n_tok, s.h_v), float("nan"), device="cuda"),
+                torch.full((n_tok, s.h_v), float("nan"), device="cuda"))
+
+    nb = pool.in_proj_workspace_bytes(n_tok, hidden)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda") if nb else None
+    al, un = outs(0), outs(1)
+    assert all(o.data_ptr() % 16 != 0 for o in un[:3])
+    pool.in_proj(x, w, *al, ws)
+    pool.in_proj(x, w, *un, ws)
+    torch.cuda.synchronize()
+    for name, u, v_ in zip("qkvab", al, un):
+        assert torch.equal(u, v_), f"{name} differs between aligned and unaligned outputs"
+    assert not torch.isnan(al[0].float()).any()
+    assert pool.error() == 0
+
+
 def test_in_proj_feeds_decode():
     """Hidden states -> projection -> decode step, on both sides."""
     s, io, hidden = syn.QWEN3_NEXT, "bf16", syn.QWEN3_NEXT_HIDDEN
