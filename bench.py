@@ -37,10 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 # same way (profiles/decode_hbm_traffic.txt).  Valid only for the kernel
 # source they were taken on: DECODE_SRC_SHA256 is checked at run time and the
 # traffic is reported as null when the source has changed since.
-DECODE_TRAFFIC = {"fetch_kib": 67794.47, "write_kib": 134801.43,
-                  "copy_fetch_scale": 536870912 / (262155.95 * 1024),
+DECODE_TRAFFIC = {"fetch_kib": 67857.33, "write_kib": 134740.77,
+                  "copy_fetch_scale": 536870912 / (262155.93 * 1024),
                   "copy_write_scale": 536870912 / (524288.0 * 1024)}
-DECODE_SRC_SHA256 = "a76ba518f4d11af4040c52d255ec6d01aae76f16550d4852a272ba6087cf6a98"
+DECODE_SRC_SHA256 = "4d5ce4cc06c97678c5f999c3c12b391658c7d9fe160415c63ef74b914d4982f7"
 
 
 # Executed bf16 MFMA flops of the prefill kernels per token, from rocprofv3

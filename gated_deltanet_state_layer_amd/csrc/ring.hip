@@ -57,7 +57,10 @@ __device__ __forceinline__ int tok_slot(int q, int e) { return e < 4 ? 4 * q + e
 // returns zero without a memory access.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kOffOOB = 0x7fff0000;     // an offset past every descriptor used here
-constexpr int kStreamPolicy = 2;        // non-temporal: the state is streamed once
+// State tile loads with the default cache policy (the fold's stores are
+// non-temporal): measured at 128 slots x 4 drafts, a verify + commit cycle
+// took 146 us, against 163 us with non-temporal loads.
+constexpr int kStreamPolicy = 0;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
 }
