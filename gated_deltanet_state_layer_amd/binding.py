@@ -22,6 +22,7 @@ GDN_ERR_BAD_INDEX = -3
 GDN_ERR_WORKSPACE = -4
 GDN_ERR_HIP = -5
 GDN_ERR_RING = -6
+GDN_ERR_HOST = -7
 GDN_F32 = 0
 GDN_BF16 = 1
 GDN_VALIDATE = 1

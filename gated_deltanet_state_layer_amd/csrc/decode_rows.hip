@@ -2,8 +2,9 @@
 //
 // With few entries the one-workgroup-per-(entry, q/k group) decode runs on
 // only n * h_k CUs and is bound by one workgroup's latency (the pages put
-// batch-1 GDN decode at about 2 % of HBM: "Project: Intel Arc Pro B70",
-// speculative-verify measurements).  Here workgroup (entry, group, rb) owns
+// batch-1 GDN decode at about 2 % of HBM: "Plan (research-based):
+// Qwen3.6-35B-A3B -- parity fix + path to >150 tok/s", section "Honest
+// caveat on speed").  Here workgroup (entry, group, rb) owns
 // rows [rb*D/NRB, (rb+1)*D/NRB) of the group's G value-head tiles and the v
 // conv channels of those rows, so NRB times more CUs stream the state.  The
 // arithmetic per row is that of the one-workgroup kernel (same row split over

@@ -78,6 +78,18 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Host-side C++ failures (a host array that cannot be allocated in
+// GDN_VALIDATE mode) never cross the C ABI: they become GDN_ERR_HOST, and
+// nothing has been enqueued by then.
+template <typename F>
+gdn_status guarded(F&& f) noexcept {
+    try {
+        return f();
+    } catch (...) {
+        return GDN_ERR_HOST;
+    }
+}
+
 // GDN_VALIDATE: copy a device index array to the host and check it.
 gdn_status host_check_ids(const int32_t* ids, int32_t n, int32_t n_slots, hipStream_t s) {
     std::vector<int32_t> h(n);
@@ -109,8 +121,12 @@ gdn_status host_check_seqlens(const int32_t* cu, int32_t n_seq, int64_t total, h
 
 // Host check of the checkpoint lists (GDN_VALIDATE): offsets from 0,
 // non-decreasing; every sequence and checkpoint slot in range and distinct.
+// The row count is bounded before anything is sized from it: no sequence can
+// use more than len_j / ckpt_every rows, so more than
+// total_tokens / ckpt_every + n_seq rows in all is rejected.
 gdn_status host_check_ckpt(const int32_t* slot_ids, int32_t n_seq, const int32_t* off,
-                           const int32_t* slots, int32_t n_slots, hipStream_t s) {
+                           const int32_t* slots, int32_t n_slots, int64_t total_tokens,
+                           int32_t ckpt_every, hipStream_t s) {
     std::vector<int32_t> ho(n_seq + 1), hs(n_seq);
     if (hipMemcpyAsync(ho.data(), off, (n_seq + 1) * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipMemcpyAsync(hs.data(), slot_ids, n_seq * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
@@ -119,6 +135,7 @@ gdn_status host_check_ckpt(const int32_t* slot_ids, int32_t n_seq, const int32_t
     if (ho[0] != 0) return GDN_ERR_BAD_INDEX;
     for (int j = 0; j < n_seq; ++j)
         if (ho[j + 1] < ho[j]) return GDN_ERR_BAD_INDEX;
+    if ((int64_t)ho[n_seq] > total_tokens / ckpt_every + n_seq) return GDN_ERR_BAD_INDEX;
     std::vector<int32_t> hc(ho[n_seq]);
     if (!hc.empty() &&
         (hipMemcpyAsync(hc.data(), slots, hc.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
@@ -174,7 +191,7 @@ gdn_status prefill_common(gdn_pool* pool, int32_t layer, int32_t n_seq, const in
     if (pool->desc.flags & GDN_VALIDATE) {
         gdn_status st = ckpt_every > 0
                             ? host_check_ckpt(slot_ids, n_seq, ckpt_offsets, ckpt_slots,
-                                              pool->desc.n_slots, s)
+                                              pool->desc.n_slots, total_tokens, ckpt_every, s)
                             : host_check_ids(slot_ids, n_seq, pool->desc.n_slots, s);
         if (st != GDN_OK) return st;
         st = host_check_seqlens(cu_seqlens, n_seq, total_tokens, s);
@@ -263,15 +280,17 @@ gdn_status gdn_pool_destroy(gdn_pool* pool) {
 }
 
 gdn_status gdn_slot_reset(gdn_pool* pool, int32_t n, const int32_t* slot_ids, void* stream) {
-    if (!pool || n < 0 || (n > 0 && !slot_ids)) return GDN_ERR_INVALID_ARG;
-    if (n == 0) return GDN_OK;
-    if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
-    hipStream_t s = as_stream(stream);
-    if (pool->desc.flags & GDN_VALIDATE) {
-        gdn_status st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
-        if (st != GDN_OK) return st;
-    }
-    return launch_slot_reset(pool, n, slot_ids, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return guarded([&]() -> gdn_status {
+        if (!pool || n < 0 || (n > 0 && !slot_ids)) return GDN_ERR_INVALID_ARG;
+        if (n == 0) return GDN_OK;
+        if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
+        hipStream_t s = as_stream(stream);
+        if (pool->desc.flags & GDN_VALIDATE) {
+            gdn_status st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+            if (st != GDN_OK) return st;
+        }
+        return launch_slot_reset(pool, n, slot_ids, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    });
 }
 
 static gdn_status check_step_args(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
@@ -292,42 +311,46 @@ static gdn_status check_step_args(gdn_pool* pool, int32_t layer, int32_t n, cons
 gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
                            const void* q, const void* k, const void* v, const float* a,
                            const float* b, const float* conv_w, void* out, void* stream) {
-    gdn_status st = check_step_args(pool, layer, n, slot_ids, 1, q, k, v, a, b, conv_w, out);
-    if (st != GDN_OK || n == 0) return st;
-    hipStream_t s = as_stream(stream);
-    if (pool->desc.flags & GDN_VALIDATE) {
-        st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
-        if (st == GDN_OK) st = host_check_rings_empty(pool, layer, slot_ids, n, s);
-        if (st != GDN_OK) return st;
-    }
-    // Few entries: split each head's rows over several workgroups so that
-    // more CUs stream the state (same arithmetic, bitwise equal results).
-    const int nrb = decode_rows_split(pool, n);
-    const hipError_t e = nrb > 1 ? launch_decode_rows(pool, nrb, layer, n, slot_ids, q, k, v, a, b,
-                                                      conv_w, out, s)
-                                 : launch_decode_verify(pool, layer, n, slot_ids, 1, q, k, v, a, b,
-                                                        conv_w, nullptr, out, s);
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return guarded([&]() -> gdn_status {
+        gdn_status st = check_step_args(pool, layer, n, slot_ids, 1, q, k, v, a, b, conv_w, out);
+        if (st != GDN_OK || n == 0) return st;
+        hipStream_t s = as_stream(stream);
+        if (pool->desc.flags & GDN_VALIDATE) {
+            st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+            if (st == GDN_OK) st = host_check_rings_empty(pool, layer, slot_ids, n, s);
+            if (st != GDN_OK) return st;
+        }
+        // Few entries: split each head's rows over several workgroups so that
+        // more CUs stream the state (same arithmetic, bitwise equal results).
+        const int nrb = decode_rows_split(pool, n);
+        const hipError_t e = nrb > 1 ? launch_decode_rows(pool, nrb, layer, n, slot_ids, q, k, v, a, b,
+                                                          conv_w, out, s)
+                                     : launch_decode_verify(pool, layer, n, slot_ids, 1, q, k, v, a, b,
+                                                            conv_w, nullptr, out, s);
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    });
 }
 
 gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
                            int32_t n_tok, const void* q, const void* k, const void* v,
                            const float* a, const float* b, const float* conv_w,
                            const int32_t* accept_len, void* out, void* stream) {
-    gdn_status st = check_step_args(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, out, true);
-    if (st != GDN_OK) return st;
-    if (n > 0 && !accept_len) return GDN_ERR_INVALID_ARG;
-    if (n == 0) return GDN_OK;
-    hipStream_t s = as_stream(stream);
-    if (pool->desc.flags & GDN_VALIDATE) {
-        st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
-        if (st == GDN_OK) st = host_check_rings_empty(pool, layer, slot_ids, n, s);
+    return guarded([&]() -> gdn_status {
+        gdn_status st = check_step_args(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, out, true);
         if (st != GDN_OK) return st;
-    }
-    return launch_decode_verify(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len,
-                                out, s) == hipSuccess
-               ? GDN_OK
-               : GDN_ERR_HIP;
+        if (n > 0 && !accept_len) return GDN_ERR_INVALID_ARG;
+        if (n == 0) return GDN_OK;
+        hipStream_t s = as_stream(stream);
+        if (pool->desc.flags & GDN_VALIDATE) {
+            st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+            if (st == GDN_OK) st = host_check_rings_empty(pool, layer, slot_ids, n, s);
+            if (st != GDN_OK) return st;
+        }
+        return launch_decode_verify(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len,
+                                    out, s) == hipSuccess
+                   ? GDN_OK
+                   : GDN_ERR_HIP;
+    });
 }
 
 gdn_status gdn_prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
@@ -343,9 +366,11 @@ gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
                                int64_t total_tokens, int32_t chunk, const void* q, const void* k,
                                const void* v, const float* a, const float* b, const float* conv_w,
                                void* out, void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_common(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v,
-                          a, b, conv_w, out, 0, nullptr, nullptr, workspace, workspace_bytes,
-                          stream);
+    return guarded([&]() -> gdn_status {
+        return prefill_common(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v,
+                              a, b, conv_w, out, 0, nullptr, nullptr, workspace, workspace_bytes,
+                              stream);
+    });
 }
 
 gdn_status gdn_prefill_chunked_ckpt(gdn_pool* pool, int32_t layer, int32_t n_seq,
@@ -355,62 +380,68 @@ gdn_status gdn_prefill_chunked_ckpt(gdn_pool* pool, int32_t layer, int32_t n_seq
                                     const float* conv_w, void* out, int32_t ckpt_every,
                                     const int32_t* ckpt_offsets, const int32_t* ckpt_slots,
                                     void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_common(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v,
-                          a, b, conv_w, out, ckpt_every, ckpt_offsets, ckpt_slots, workspace,
-                          workspace_bytes, stream);
+    return guarded([&]() -> gdn_status {
+        return prefill_common(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v,
+                              a, b, conv_w, out, ckpt_every, ckpt_offsets, ckpt_slots, workspace,
+                              workspace_bytes, stream);
+    });
 }
 
 gdn_status gdn_slot_copy(gdn_pool* pool, int32_t n, const int32_t* src_ids,
                          const int32_t* dst_ids, void* stream) {
-    if (!pool || n < 0 || (n > 0 && (!src_ids || !dst_ids))) return GDN_ERR_INVALID_ARG;
-    if (n == 0) return GDN_OK;
-    if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
-    hipStream_t s = as_stream(stream);
-    if (pool->desc.flags & GDN_VALIDATE) {
-        // sources in range; destinations in range, distinct and not sources
-        std::vector<int32_t> hs(n), hd(n);
-        if (hipMemcpyAsync(hs.data(), src_ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
-            hipMemcpyAsync(hd.data(), dst_ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
-            hipStreamSynchronize(s) != hipSuccess)
-            return GDN_ERR_HIP;
-        std::vector<int32_t> dst;
-        for (int i = 0; i < n; ++i) {
-            if (hs[i] >= pool->desc.n_slots || hd[i] >= pool->desc.n_slots) return GDN_ERR_BAD_INDEX;
-            if (hs[i] >= 0 && hd[i] >= 0) dst.push_back(hd[i]);
+    return guarded([&]() -> gdn_status {
+        if (!pool || n < 0 || (n > 0 && (!src_ids || !dst_ids))) return GDN_ERR_INVALID_ARG;
+        if (n == 0) return GDN_OK;
+        if (n > 65535) return GDN_ERR_UNSUPPORTED;  // grid.y limit
+        hipStream_t s = as_stream(stream);
+        if (pool->desc.flags & GDN_VALIDATE) {
+            // sources in range; destinations in range, distinct and not sources
+            std::vector<int32_t> hs(n), hd(n);
+            if (hipMemcpyAsync(hs.data(), src_ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+                hipMemcpyAsync(hd.data(), dst_ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+                hipStreamSynchronize(s) != hipSuccess)
+                return GDN_ERR_HIP;
+            std::vector<int32_t> dst;
+            for (int i = 0; i < n; ++i) {
+                if (hs[i] >= pool->desc.n_slots || hd[i] >= pool->desc.n_slots) return GDN_ERR_BAD_INDEX;
+                if (hs[i] >= 0 && hd[i] >= 0) dst.push_back(hd[i]);
+            }
+            std::sort(dst.begin(), dst.end());
+            if (std::adjacent_find(dst.begin(), dst.end()) != dst.end()) return GDN_ERR_BAD_INDEX;
+            for (int i = 0; i < n; ++i)
+                if (hs[i] >= 0 && hd[i] >= 0 && std::binary_search(dst.begin(), dst.end(), hs[i]))
+                    return GDN_ERR_BAD_INDEX;
         }
-        std::sort(dst.begin(), dst.end());
-        if (std::adjacent_find(dst.begin(), dst.end()) != dst.end()) return GDN_ERR_BAD_INDEX;
-        for (int i = 0; i < n; ++i)
-            if (hs[i] >= 0 && hd[i] >= 0 && std::binary_search(dst.begin(), dst.end(), hs[i]))
-                return GDN_ERR_BAD_INDEX;
-    }
-    return launch_slot_copy(pool, n, src_ids, dst_ids, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+        return launch_slot_copy(pool, n, src_ids, dst_ids, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    });
 }
 
 static gdn_status ring_call(gdn_pool* pool, RingOp op, int32_t layer, int32_t n,
                             const int32_t* slot_ids, int32_t n_tok, const void* q, const void* k,
                             const void* v, const float* a, const float* b, const float* conv_w,
                             const int32_t* accept_len, void* out, void* stream) {
-    if (!pool || layer < 0 || layer >= pool->desc.n_layers || n < 0) return GDN_ERR_INVALID_ARG;
-    if (pool->desc.ring_len == 0) return GDN_ERR_UNSUPPORTED;
-    if (op != RingOp::kFlush) {
-        if (n_tok < 1 || n_tok > kMaxVerifyTokens) return GDN_ERR_INVALID_ARG;
-        if (pool->desc.ring_len + n_tok > kMaxRingSolve) return GDN_ERR_UNSUPPORTED;
-        if (n > 0 && (!q || !k || !v || !a || !b || !conv_w)) return GDN_ERR_INVALID_ARG;
-        if (n > 0 && op == RingOp::kVerify && !out) return GDN_ERR_INVALID_ARG;
-        if (n > 0 && op == RingOp::kCommit && !accept_len) return GDN_ERR_INVALID_ARG;
-    }
-    if (n > 0 && !slot_ids) return GDN_ERR_INVALID_ARG;
-    if (n == 0) return GDN_OK;
-    hipStream_t s = as_stream(stream);
-    if (pool->desc.flags & GDN_VALIDATE) {
-        const gdn_status st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
-        if (st != GDN_OK) return st;
-    }
-    const hipError_t e = launch_ring(pool, op, layer, n, slot_ids, op == RingOp::kFlush ? 0 : n_tok,
-                                     q, k, v, a, b, conv_w, accept_len, out, s);
-    if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return guarded([&]() -> gdn_status {
+        if (!pool || layer < 0 || layer >= pool->desc.n_layers || n < 0) return GDN_ERR_INVALID_ARG;
+        if (pool->desc.ring_len == 0) return GDN_ERR_UNSUPPORTED;
+        if (op != RingOp::kFlush) {
+            if (n_tok < 1 || n_tok > kMaxVerifyTokens) return GDN_ERR_INVALID_ARG;
+            if (pool->desc.ring_len + n_tok > kMaxRingSolve) return GDN_ERR_UNSUPPORTED;
+            if (n > 0 && (!q || !k || !v || !a || !b || !conv_w)) return GDN_ERR_INVALID_ARG;
+            if (n > 0 && op == RingOp::kVerify && !out) return GDN_ERR_INVALID_ARG;
+            if (n > 0 && op == RingOp::kCommit && !accept_len) return GDN_ERR_INVALID_ARG;
+        }
+        if (n > 0 && !slot_ids) return GDN_ERR_INVALID_ARG;
+        if (n == 0) return GDN_OK;
+        hipStream_t s = as_stream(stream);
+        if (pool->desc.flags & GDN_VALIDATE) {
+            const gdn_status st = host_check_ids(slot_ids, n, pool->desc.n_slots, s);
+            if (st != GDN_OK) return st;
+        }
+        const hipError_t e = launch_ring(pool, op, layer, n, slot_ids, op == RingOp::kFlush ? 0 : n_tok,
+                                         q, k, v, a, b, conv_w, accept_len, out, s);
+        if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    });
 }
 
 gdn_status gdn_ring_verify(gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
@@ -495,6 +526,7 @@ const char* gdn_status_string(gdn_status status) {
         case GDN_ERR_WORKSPACE: return "prefill workspace too small";
         case GDN_ERR_HIP: return "HIP runtime error";
         case GDN_ERR_RING: return "a listed slot's verify ring is not empty (flush it first)";
+        case GDN_ERR_HOST: return "host-side failure (host memory)";
         default: return "unknown status";
     }
 }

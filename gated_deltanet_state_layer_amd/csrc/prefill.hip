@@ -91,7 +91,8 @@ struct Ws {
     int4* srec;          // [n_seq][2] sequences in scan order: {sequence, slot, s0, len}, {first chunk, chunks, 0, 0}
     bf16x8* qkf;         // [max_chunks][h_k][nqk fragments]
     bf16x8* tpf;         // [max_chunks][h_v][ntp fragments]; all-zero ones unwritten
-    float* gl;           // [max_chunks][h_v][CP] cumulative log-decay in the chunk
+    float* gl;           // [max_chunks][h_v][2][CP] per token: gamma = exp(g), then
+                         // eta = exp(g_last - g) (g: cumulative log-decay in the chunk)
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -124,7 +125,7 @@ Ws carve(void* base, const PoolView& P, int32_t n_seq, int64_t total, int32_t ch
     const size_t o_srec = take((size_t)n_seq * 2 * sizeof(int4));
     const size_t o_qk = take((size_t)mc * P.h_k * gm.nqk() * fb);
     const size_t o_tp = take((size_t)mc * P.h_v * gm.ntp() * fb);
-    const size_t o_g = take((size_t)mc * P.h_v * gm.CP * 4);
+    const size_t o_g = take((size_t)mc * P.h_v * 2 * gm.CP * 4);
     *bytes = off;
     char* b = static_cast<char*>(base);
     Ws w;
@@ -294,7 +295,10 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     float* sP = sT + CP * LT;          // [CP][LT]
     constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
     constexpr int kMaxGroup = 4;                   // value heads per group kept in LDS
-    __shared__ __align__(16) float s_g[CP];
+    // Cumulative log-decay in fp64: with a -> 0 (log a down to the clamp)
+    // |g| reaches hundreds within a chunk, where fp32 would keep only ~1e-5
+    // of the differences g_t - g_s that the decays are made of.
+    __shared__ __align__(16) double s_g[CP];
     __shared__ __align__(16) float s_b[CP];
     __shared__ float s_la[kMaxGroup][CP], s_bb[kMaxGroup][CP];
 
@@ -572,11 +576,11 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         const int hv = g * G + hl;
         // cumulative log-decay and b for the chunk's tokens (zero past L)
         if (wave == 0) {
-            float la = lane < CP ? s_la[hl][lane] : 0.f;
+            double la = lane < CP ? (double)s_la[hl][lane] : 0.0;
             const float bt = lane < CP ? s_bb[hl][lane] : 0.f;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {   // inclusive prefix sum (CP <= 64)
-                const float y = __shfl_up(la, o);
+                const double y = __shfl_up(la, o);
                 if (lane >= o) la += y;
             }
             if (lane < CP) {
@@ -589,19 +593,21 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         // four rows share their g and b (one vector read each); blocks above
         // the diagonal are plain zeros.
         if (ti < NT) {
-            const float4 gt4 = *reinterpret_cast<const float4*>(s_g + ti * 16 + q4 * 4);
+            const double2 ga = *reinterpret_cast<const double2*>(s_g + ti * 16 + q4 * 4);
+            const double2 gb = *reinterpret_cast<const double2*>(s_g + ti * 16 + q4 * 4 + 2);
             const float4 bt4 = *reinterpret_cast<const float4*>(s_b + ti * 16 + q4 * 4);
-            const float gt[4] = {gt4.x, gt4.y, gt4.z, gt4.w}, bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+            const double gt[4] = {ga.x, ga.y, gb.x, gb.y};
+            const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) {
                 const int s = jt * 16 + m16;          // column
-                const float gs = s_g[s];
+                const double gs = s_g[s];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = ti * 16 + q4 * 4 + r;   // row (later token)
                     float av = 0.f, pv = 0.f;
                     if (jt <= ti) {
-                        const float dec = __expf(fminf(gt[r] - gs, 0.f));
+                        const float dec = __expf(fminf((float)(gt[r] - gs), 0.f));
                         av = s < t ? bt[r] * dec * kk[jt][r] : 0.f;
                         pv = s <= t ? qk[jt][r] * dec : 0.f;
                     }
@@ -702,7 +708,11 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             }
             store_frag(gtp, f, lane, split8(x));
         }
-        if (tid < CP) W.gl[((int64_t)ci * P.h_v + hv) * CP + tid] = s_g[tid];
+        if (tid < 2 * CP) {   // gamma_t, then eta_t = exp(g_last - g_t), from fp64 g
+            const int t = tid % CP;
+            const float e = tid < CP ? (float)s_g[t] : (float)(s_g[CP - 1] - s_g[t]);
+            W.gl[((int64_t)ci * P.h_v + hv) * 2 * CP + tid] = __expf(e);
+        }
         __syncthreads();
     }
 }
@@ -737,8 +747,8 @@ struct ScanLds {
     // floats, after the fragments
     static constexpr int vv = vec_end * 4;                     // [2][CP][16] conv+SiLU of v
     static constexpr int raw = vv + 2 * CP * kRows;            // [2][NRAW][16] raw v rows
-    static constexpr int gg = raw + 2 * NRAW * kRows;          // [2][CP] cumulative log-decay
-    static constexpr int win = gg + 2 * CP;                    // [kMaxConvK-1][16] old window
+    static constexpr int gg = raw + 2 * NRAW * kRows;          // [2][2][CP] gamma, eta per token
+    static constexpr int win = gg + 4 * CP;                    // [kMaxConvK-1][16] old window
     // K^ of the chunk, bf16 planes hi and lo, [CP][D] with the 16-element
     // column groups of each row XOR-swizzled (kswz), so the rows read
     // together by a transpose read fall in disjoint banks.
@@ -904,7 +914,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             const int64_t pc = p < s0 ? s0 : (p >= s0 + len ? s0 + len - 1 : p);
             rv[it] = *reinterpret_cast<const uint4*>(vsrc + pc * vstride + cv);
         }
-        rg = W.gl[((int64_t)(ci0 + cc) * P.h_v + h) * CP + (tid % CP)];
+        rg = W.gl[((int64_t)(ci0 + cc) * P.h_v + h) * 2 * CP + (tid % (2 * CP))];
     };
     // Store chunk cc's raw rows: zero past its valid tokens, window rows
     // before the sequence start (only the first chunk reaches back there).
@@ -931,7 +941,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                     *reinterpret_cast<float4*>(dst + r * kRows + cv + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
             }
         }
-        if (tid < CP) s_g[buf * CP + tid] = rg;
+        if (tid < 2 * CP) s_g[buf * 2 * CP + tid] = rg;
     };
     // conv+SiLU of the block's v channels for chunk cc from s_raw[buf].  All
     // KM taps are applied (weights past conv_k are zero, and raw rows past the
@@ -981,11 +991,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     // B fragments over tokens (k-step kc = tw/2).
     const int dst_lane = (2 * (tw & 1) + (q4 >> 1)) * 16 + m16;
     const int dst_e0 = 4 * (q4 & 1);
-    // Outputs go through a buffer descriptor bounded at the sequence's last
-    // token, so rows past it are dropped without a branch.
+    // Outputs go through a buffer descriptor per chunk, based at the chunk's
+    // first row (64-bit address) and bounded at its last valid token, so rows
+    // past the sequence end are dropped without a branch and the 32-bit
+    // offsets stay inside one chunk however long the sequence is.
     T* out_base = out + (s0 * P.h_v + h) * D + row0;
-    const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
-        out_base, 0, (int)(((int64_t)(len - 1) * P.h_v * D + kRows) * sizeof(T)), 0x00020000);
+    const int64_t out_tok = (int64_t)P.h_v * D;       // elements between output rows
 
     // ---- prologue: state block, old v window, new v window, chunk 0 operands.
     {
@@ -1027,9 +1038,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         const bool nxt = cc + 1 < n_ch;
         const int cn = ci0 + min(cc + 1, n_ch - 1);   // next chunk (clamped)
         const int64_t trel = (int64_t)cc * chunk;      // chunk start relative to s0
-        const float* gb = s_g + buf * CP;
-        const float glast = gb[CP - 1];
-        const float4 g4 = *reinterpret_cast<const float4*>(gb + tw * 16 + q4 * 4);   // this lane's 4 tokens
+        // this lane's 4 tokens: gamma = exp(g) and eta = exp(g_last - g)
+        const float* gb = s_g + buf * 2 * CP;
+        const float4 g4 = *reinterpret_cast<const float4*>(gb + tw * 16 + q4 * 4);
+        const float4 e4 = *reinterpret_cast<const float4*>(gb + CP + tw * 16 + q4 * 4);
 
         // (1) X_K for token tile tw; R = V - diag(gamma) X_K to LDS.  (X_Q
         // only feeds the output: it is computed in phase 2, where it fills
@@ -1064,8 +1076,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
 #pragma unroll
             for (int ks = 1; ks < NKS; ++ks) ak += acc[ks];
             const float4 v4 = *reinterpret_cast<const float4*>(s_v + buf * CP * kRows + m16 * CP + tw * 16 + q4 * 4);
-            const float r4[4] = {v4.x - __expf(g4.x) * ak[0], v4.y - __expf(g4.y) * ak[1],
-                                 v4.z - __expf(g4.z) * ak[2], v4.w - __expf(g4.w) * ak[3]};
+            const float r4[4] = {v4.x - g4.x * ak[0], v4.y - g4.y * ak[1],
+                                 v4.z - g4.z * ak[2], v4.w - g4.w * ak[3]};
             store_frag4(s_rf, tw >> 1, dst_lane, dst_e0, r4);
             load_qk(cn, 1);
         }
@@ -1096,12 +1108,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
 #pragma unroll
             for (int ks = 1; ks < NKS; ++ks) aq += acc[NKC + ks];
             float u4[4], uu4[4];
-            const float gl4[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float gl4[4] = {g4.x, g4.y, g4.z, g4.w}, el4[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 u4[i] = uv[i];
-                uu4[i] = uv[i] * __expf(glast - gl4[i]);
-                xq[i] = __expf(gl4[i]) * aq[i];
+                uu4[i] = uv[i] * el4[i];
+                xq[i] = gl4[i] * aq[i];
             }
             store_frag4(s_uf, tw >> 1, dst_lane, dst_e0, u4);
             store_frag4(s_uuf, tw >> 1, dst_lane, dst_e0, uu4);
@@ -1117,7 +1129,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             constexpr int NJ = 3 * NKC;
             Frag fa[NJ], fb[NJ];
             f32x4 acc[NJ];
-            const float dlast = __expf(glast);
+            const float dlast = gb[CP - 1];   // gamma of the last token
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
                 const Frag ub = load_frag(s_uf, kc, lane);
@@ -1153,10 +1165,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
 #pragma unroll
                 for (int kc = 1; kc < NKC; ++kc) st[uu] += acc[NKC + uu * NKC + kc];
             }
+            const int lc = (int)min((int64_t)chunk, len - trel);   // valid rows of the chunk
+            const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
+                out_base + trel * out_tok, 0, (int)(((lc - 1) * out_tok + kRows) * sizeof(T)),
+                0x00020000);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = tw * 16 + q4 * 4 + i;
-                const int off = (int)(((trel + t) * P.h_v * D + m16) * (int64_t)sizeof(T));
+                const int off = (int)((t * out_tok + m16) * (int64_t)sizeof(T));
                 if constexpr (sizeof(T) == 2)
                     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(o[i]), out_rs, off, 0, 0);
                 else
@@ -1287,6 +1303,8 @@ hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,
     const int64_t mc = max_chunks(n_seq, total_tokens, chunk);
     if (mc > INT32_MAX || n_seq > 65535) return hipErrorNotSupported;
     if (P.h_v / P.h_k > 4) return hipErrorNotSupported;   // value heads per group kept in LDS
+    // One chunk of output rows is addressed with 32-bit offsets.
+    if ((int64_t)64 * P.h_v * P.d * pool->io_size >= INT32_MAX) return hipErrorNotSupported;
     const bool bf = pool->desc.io_dtype == GDN_BF16;
     const int total = (int)total_tokens, m = (int)mc;
     switch (P.d) {

@@ -121,6 +121,11 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
     __shared__ __align__(16) float mT[NTOK * MP];          // T = (I+A)^-1
     __shared__ __align__(16) float mP[VERIFY ? 16 * MP : 4];   // P rows of the drafts
     __shared__ __align__(16) float sg[NTOK], sb[NTOK], sla[NTOK];
+    // The cumulative log-decay also in fp64, and exp(g_last - g) from it: with
+    // a -> 0 (log a down to the clamp) |g| reaches hundreds, where fp32 keeps
+    // only ~1e-5 of the differences that the decays are made of.
+    __shared__ __align__(16) double sgd[NTOK];
+    __shared__ __align__(16) float sge[NTOK];
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -330,17 +335,22 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
         }
     }
     if (wave == 0 && solve) {
-        float la = 0.f;
+        double la = 0.0;
         if (lane < NTOK) {
             const float av = sla[lane];
-            la = lane < Lc ? fmaxf(__logf(av), kLogDecayMin) : 0.f;   // a <= 0 gives -inf -> clamp
+            la = lane < Lc ? (double)fmaxf(__logf(av), kLogDecayMin) : 0.0;   // a <= 0 gives -inf -> clamp
         }
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
-            const float y = __shfl_up(la, o);
+            const double y = __shfl_up(la, o);
             if (lane >= o) la += y;
         }
-        if (lane < NTOK) sg[lane] = la;
+        const double gl = __shfl(la, NTOK - 1);   // g is constant past Lc
+        if (lane < NTOK) {
+            sg[lane] = (float)la;
+            sgd[lane] = la;
+            sge[lane] = __expf((float)(gl - la));
+        }
     }
     __syncthreads();
 
@@ -379,19 +389,19 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
                 acc = mma3(acc, split8(x), split8(y));
             }
             const int s = tj * 16 + m16;             // column token
-            const float gs = sg[s];
+            const double gs = sgd[s];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = ti * 16 + q4 * 4 + i;  // row: token (KK) or draft (QK)
                 if (!isq) {
-                    const float av = s < r ? sb[r] * __expf(fminf(sg[r] - gs, 0.f)) * acc[i] : 0.f;
+                    const float av = s < r ? sb[r] * __expf(fminf((float)(sgd[r] - gs), 0.f)) * acc[i] : 0.f;
                     mA[r * MP + s] = av;
                     if (ti != tj) mA[(tj * 16 + q4 * 4 + i) * MP + ti * 16 + m16] = 0.f;   // upper block
                 } else if constexpr (VERIFY) {
                     float pv = 0.f;
                     if (r < n_new) {
                         const int tr2 = c + r;       // the draft's position in the solve
-                        pv = s <= tr2 ? __expf(fminf(sg[tr2] - gs, 0.f)) * acc[i] : 0.f;
+                        pv = s <= tr2 ? __expf(fminf((float)(sgd[tr2] - gs), 0.f)) * acc[i] : 0.f;
                     }
                     mP[r * MP + s] = pv;
                 }
@@ -546,11 +556,12 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
             for (int tt = 0; tt < 2; ++tt) {
                 const int ts = min(tt, NT - 1);
                 const f32x4 u = uacc[i * NT + ts];
-                const float gg[4] = {gq4[ts].x, gq4[ts].y, gq4[ts].z, gq4[ts].w};
+                const float4 e4 = *reinterpret_cast<const float4*>(sge + ts * 16 + q4 * 4);
+                const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     float x = tt < NT ? u[j] : 0.f;
-                    if constexpr (!VERIFY) x *= __expf(glast - gg[j]);   // decayed U for the state update
+                    if constexpr (!VERIFY) x *= ee[j];   // decayed U for the state update
                     uu[tt * 4 + j] = x;
                 }
             }

@@ -86,6 +86,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_WORKSPACE (-4)   /* prefill workspace too small */
 #define GDN_ERR_HIP (-5)         /* a HIP runtime call failed */
 #define GDN_ERR_RING (-6)        /* GDN_VALIDATE: a listed slot's verify ring is not empty */
+#define GDN_ERR_HOST (-7)        /* host-side failure (e.g. GDN_VALIDATE cannot allocate its host copies) */
 
 typedef int32_t gdn_dtype;
 #define GDN_F32 0
@@ -111,12 +112,19 @@ typedef struct {
 
 /* Bytes the caller must allocate for a pool with this descriptor: the fp32
  * state buffer and the aux buffer (conv windows + meta).  Both buffers must be
- * 256-byte aligned.  Returns INVALID_ARG / UNSUPPORTED for a bad descriptor. */
+ * 256-byte aligned.  Returns INVALID_ARG / UNSUPPORTED for a bad descriptor.
+ * The size is fixed by the slot count and the layer shapes alone, not by any
+ * context length: a recurrent state does not grow with the sequence, and the
+ * slot dimension is an outer dimension on it (baseRT issue #31, "Why this
+ * looks tractable"). */
 gdn_status gdn_pool_bytes(const gdn_pool_desc* desc, size_t* state_bytes, size_t* aux_bytes);
 
 /* Create a pool over caller-owned device buffers sized by gdn_pool_bytes and
- * zero them on `stream` (every slot starts from zero state and window).  The
- * buffers must outlive the pool.  *out receives a host handle. */
+ * zero them on `stream`: every slot starts from zero state and window, as a
+ * new request does ("Project: adding the hybrid model Qwen3.5", table "What
+ * to do", row "State").  The buffers must outlive the pool.  *out receives a
+ * host handle.  Returns INVALID_ARG for a null or misaligned buffer, HIP if
+ * the zero fill cannot be enqueued (then no handle is returned). */
 gdn_status gdn_pool_create(const gdn_pool_desc* desc, void* state_buf, void* aux_buf,
                            void* stream, gdn_pool** out);
 
@@ -202,8 +210,10 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int6
  *              written in 16-byte vectors)
  *   workspace  device, >= gdn_prefill_workspace_bytes, 256-byte aligned;
  *              scratch only, contents undefined afterwards
- * Zero-length sequences are no-ops.  Returns GDN_ERR_UNSUPPORTED for more
- * than 4 value heads per q/k head (h_v/h_k > 4). */
+ * Zero-length sequences are no-ops.  A single sequence may be as long as
+ * total_tokens allows (up to 2^31 - 1 tokens; output rows are addressed per
+ * chunk with 64-bit bases).  Returns GDN_ERR_UNSUPPORTED for more than 4
+ * value heads per q/k head (h_v/h_k > 4) or total_tokens >= 2^31. */
 gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
                                const int32_t* cu_seqlens, const int32_t* slot_ids,
                                int64_t total_tokens, int32_t chunk, const void* q, const void* k,
@@ -225,7 +235,9 @@ gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
  * tokens, exactly what the sequence's own slot would hold had the sequence
  * ended there (within the prefill's tolerance).  A negative checkpoint slot
  * is skipped.  Checkpoint slots must differ from each other and from
- * slot_ids (GDN_VALIDATE checks). */
+ * slot_ids (GDN_VALIDATE checks).  GDN_VALIDATE also returns BAD_INDEX,
+ * before reading ckpt_slots, when ckpt_offsets[n_seq] exceeds
+ * total_tokens / ckpt_every + n_seq (more rows than any call can fill). */
 gdn_status gdn_prefill_chunked_ckpt(gdn_pool* pool, int32_t layer, int32_t n_seq,
                                     const int32_t* cu_seqlens, const int32_t* slot_ids,
                                     int64_t total_tokens, int32_t chunk, const void* q,

@@ -29,10 +29,10 @@ def io_torch(io):
     return torch.bfloat16 if io == "bf16" else torch.float32
 
 
-def make_pool(s: syn.Shapes, n_slots, io, n_layers=1, flags=0, ring_len=0):
+def make_pool(s: syn.Shapes, n_slots, io, n_layers=1, flags=0, ring_len=0, eps=0.0):
     import gated_deltanet_state_layer_amd as G
     d = G.make_desc(n_slots, n_layers, s.h_k, s.h_v, s.d_k, s.d_v, s.conv_k,
-                    G.GDN_BF16 if io == "bf16" else G.GDN_F32, 0.0, 0.0, flags, ring_len)
+                    G.GDN_BF16 if io == "bf16" else G.GDN_F32, 0.0, eps, flags, ring_len)
     return G.Pool(d)
 
 
@@ -52,9 +52,9 @@ def load_slots(pool, contents: dict):
     torch.cuda.synchronize()
 
 
-def oracle_pool(s, contents: dict, slot_order, n_layers=1, form="matrix"):
+def oracle_pool(s, contents: dict, slot_order, n_layers=1, form="matrix", eps=1e-6):
     """An oracle pool whose slot j holds contents[slot_order[j]]."""
-    op = O.OraclePool(len(slot_order), n_layers, s, form=form)
+    op = O.OraclePool(len(slot_order), n_layers, s, eps=eps, form=form)
     for j, slot in enumerate(slot_order):
         if contents is not None and int(slot) in contents:
             st, wn = contents[int(slot)]
@@ -73,6 +73,15 @@ def rel_err(x, ref):
     ref = np.asarray(ref, np.float64)
     rms = np.sqrt(np.mean(ref * ref))
     return float(np.max(np.abs(x - ref)) / rms) if ref.size else 0.0
+
+
+def check_f32_dev(name, x, ref, tol=TOL_F32):
+    """check_f32 computed on the device, for tensors too large to copy."""
+    x, ref = x.double(), ref.double()
+    assert bool(torch.isfinite(x).all()), f"{name}: non-finite values"
+    e = float((x - ref).abs().max() / ref.square().mean().sqrt())
+    say(f"  {name}: max|err|/rms = {e:.3e} (tol {tol:g})")
+    assert e <= tol, f"{name}: {e:.3e} > {tol:g}"
 
 
 def check_f32(name, x, ref, tol=TOL_F32):

@@ -160,6 +160,12 @@ def test_validate_mode_rejects_overlapping_checkpoint_slots():
         with pytest.raises(G.GdnError) as e:
             pool.prefill_ckpt(*args, every, _i32([0, len(ck)]), _i32(ck), ws)
         assert e.value.status == status
+    # more checkpoint rows than any call can fill (64 / 32 + 1 = 3): rejected
+    # before the row list is sized from the device value or read
+    for last in (4, 1 << 30):
+        with pytest.raises(G.GdnError) as e:
+            pool.prefill_ckpt(*args, 32, _i32([0, last]), _i32([2]), ws)
+        assert e.value.status == -3
     with pytest.raises(G.GdnError) as e:
         pool.copy(_i32([1, 2]), _i32([2, 3]))   # destination 2 is also a source
     assert e.value.status == -3

@@ -2,7 +2,7 @@
 the raw q, k, v and the activated gates, on the skinny path (up to 64
 tokens), the split-hidden path, the 128-token-tile path and the 256-token-tile
 path (from 512 tokens; 1000 and 2100 tokens leave ragged row tiles and a
-partial band), with ragged token and channel counts, and the projection
+partial band; 8192 tokens is the prefill workload's length), with ragged token and channel counts, and the projection
 feeding a decode step."""
 import numpy as np
 import pytest
@@ -41,7 +41,7 @@ def _project(pool, s, x_np, w_np, io):
     return q, k, v, a, b, nb
 
 
-@pytest.mark.parametrize("n_tok", [1, 64, 300, 1024, 1000, 2100])
+@pytest.mark.parametrize("n_tok", [1, 64, 300, 1024, 1000, 2100, 8192])
 def test_in_proj_qwen3_next_vs_oracle(n_tok):
     s, io, hidden = syn.QWEN3_NEXT, "bf16", syn.QWEN3_NEXT_HIDDEN
     rng = np.random.default_rng(1100 + n_tok)

@@ -7,8 +7,8 @@ import pytest
 
 import gdn_synth as syn
 from oracle import gdn_oracle as O
-from gpu_util import (check_f32, check_out, dev, group_slice, host, load_slots, make_pool,
-                      oracle_pool, say, scramble_pool, slice_tokens, tokens_to_dev)
+from gpu_util import (check_f32, check_f32_dev, check_out, dev, group_slice, host, load_slots, make_pool,
+                      oracle_pool, rel_err, say, scramble_pool, slice_tokens, tokens_to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -94,13 +94,47 @@ def _check_groups(pool, res, out, ids_np, io, cu=None):
         assert np.array_equal(host(pool.window[idx][..., ch]), op.X), f"group {g} windows"
 
 
-def test_prefill_8192_tokens_sampled_groups():
-    """One 8192-token sequence, chunk 64, Qwen3-Next shapes (the benchmark's
-    launch), checked on q/k head groups 0 and 11 against the oracle."""
+def _check_layer(pool, out, ids_np, ref, io, rows=None, what=""):
+    """Whole-layer comparison with the oracle: every output row of the
+    listed rows (all by default), every final state and every window of the
+    sequences' slots; the worst q/k group is printed too."""
+    out_ref, S_ref, X_ref = ref
+    s = pool.desc
+    o = host(out)
+    if rows is not None:
+        o, out_ref = o[rows], out_ref[rows]
+    check_out(f"{what}outputs, all {s.h_k} groups", o, out_ref, io)
+    G = s.h_v // s.h_k
+    worst = max(range(s.h_k), key=lambda g: rel_err(o[:, g * G:(g + 1) * G],
+                                                    out_ref[:, g * G:(g + 1) * G]))
+    say(f"  worst group {worst}: {rel_err(o[:, worst * G:(worst + 1) * G], out_ref[:, worst * G:(worst + 1) * G]):.3e}")
+    idx = torch.from_numpy(ids_np.astype(np.int64)).cuda()
+    check_f32(f"{what}final states, all {s.h_v} heads", host(pool.state[idx]), S_ref)
+    assert np.array_equal(host(pool.window[idx]), X_ref), f"{what}windows"
+
+
+_REF_8192 = {}
+
+
+def _oracle_8192(workers, case):
+    """Oracle over the whole layer for the 8192-token sequence (computed
+    once, shared by the one-call and the split test)."""
+    if "ref" not in _REF_8192:
+        tok = case["tokens"]
+        T = tok["q"].shape[0]
+        _REF_8192["ref"] = workers.prefill_all_groups(case["shapes"], tok, case["conv_w"],
+                                                      np.array([0, T]), np.array([0]))
+    return _REF_8192["ref"]
+
+
+def test_prefill_8192_tokens_all_groups(oracle_pool_workers):
+    """One 8192-token sequence, chunk 64, Qwen3-Next shapes, in the launch the
+    benchmark times: outputs, final state and window compared with the
+    oracle on every q/k group and value head of the layer."""
     case = syn.prefill_case()
     s, io, tok = case["shapes"], case["io"], case["tokens"]
     T = tok["q"].shape[0]
-    say(f"prefill T={T} chunk 64")
+    say(f"prefill T={T} chunk 64, all groups")
     pool = make_pool(s, 4, io)
     scramble_pool(pool, 21)
     pool.reset(dev(np.array([2], np.int32), torch.int32))
@@ -109,20 +143,19 @@ def test_prefill_8192_tokens_sampled_groups():
                       dev(case["conv_w"]), 64, io)
     torch.cuda.synchronize()
     assert pool.error() == 0
-    res = _oracle_groups(s, [0, 11], tok, case["conv_w"], [0, T], np.array([2]))
-    _check_groups(pool, res, out, np.array([2], np.int32), io)
+    _check_layer(pool, out, np.array([2], np.int32), _oracle_8192(oracle_pool_workers, case), io)
     keep = [0, 1, 3]
     assert torch.equal(pool.state[keep], st0[keep]) and torch.equal(pool.window[keep], wn0[keep])
-    assert torch.isfinite(out.float()).all()
 
 
-def test_prefill_scheduler_split_matches_unsplit():
+def test_prefill_scheduler_split_matches_unsplit(oracle_pool_workers):
     """The same 8192 tokens as 16 calls of 512 tokens carrying state and
-    window match the single call (within tolerance) and the oracle."""
+    window: equal to the single call (within tolerance) and to the oracle on
+    every group of the layer."""
     case = syn.prefill_case()
     s, io, tok = case["shapes"], case["io"], case["tokens"]
     T = tok["q"].shape[0]
-    say("prefill split 16 x 512")
+    say("prefill split 16 x 512, all groups")
     w = dev(case["conv_w"])
     p1 = make_pool(s, 2, io)
     o1 = run_prefill(p1, 0, np.array([0, T], np.int32), np.array([1], np.int32), tok, w, 64, io)
@@ -134,36 +167,145 @@ def test_prefill_scheduler_split_matches_unsplit():
                                  w, 64, io))
     o2 = torch.cat(parts)
     torch.cuda.synchronize()
+    assert p2.error() == 0
     check_out("split vs unsplit outputs", host(o2), host(o1), io)
     check_f32("split vs unsplit state", host(p2.state[1]), host(p1.state[1]))
     assert torch.equal(p2.window[1], p1.window[1])
-    res = _oracle_groups(s, [5], tok, case["conv_w"], [0, T], np.array([1]))
-    _check_groups(p2, res, o2, np.array([1], np.int32), io)
+    _check_layer(p2, o2, np.array([1], np.int32), _oracle_8192(oracle_pool_workers, case), io,
+                 what="split: ")
 
 
-def test_varlen_batched_prefill_into_slots():
+def _varlen_setup(case, contents):
+    """Pool for the varlen workload: every slot scrambled, the continuing
+    sequences' slots holding `contents`, the others reset."""
+    s, io, ids_np, cont = case["shapes"], case["io"], case["slot_ids"], case["continuing"]
+    pool = make_pool(s, case["n_slots"], io)
+    scramble_pool(pool, 31)
+    load_slots(pool, contents)
+    pool.reset(dev(ids_np[~cont], torch.int32))
+    return pool
+
+
+def _start_contents(case, contents):
+    """Oracle starting states/windows per sequence (zero for reset slots)."""
+    s, ids_np = case["shapes"], case["slot_ids"]
+    n = len(ids_np)
+    st = np.zeros((n, 1, s.h_v, s.d_v, s.d_k))
+    wn = np.zeros((n, 1, s.conv_k - 1, s.c_conv))
+    for j, sl in enumerate(ids_np):
+        if int(sl) in contents:
+            st[j], wn[j] = contents[int(sl)]
+    return st, wn
+
+
+def test_varlen_batched_prefill_into_slots(oracle_pool_workers):
     """16 packed sequences of 128..4096 tokens; 12 into reset slots, 4
-    continuing from pre-filled states and windows."""
+    continuing from pre-filled states and windows; every group, state and
+    window of the layer against the oracle, other slots bitwise untouched."""
     case = syn.varlen_case()
     s, io, tok = case["shapes"], case["io"], case["tokens"]
     cu, ids_np, cont = case["cu_seqlens"], case["slot_ids"], case["continuing"]
-    say(f"varlen: {len(ids_np)} seqs, {int(cu[-1])} tokens")
-    pool = make_pool(s, case["n_slots"], io)
-    scramble_pool(pool, 31)
+    say(f"varlen: {len(ids_np)} seqs, {int(cu[-1])} tokens, all groups")
     contents = syn.draw_pool_contents(case["pool_seed"], ids_np[cont], s, io)
-    load_slots(pool, contents)
-    fresh = ids_np[~cont]
-    pool.reset(dev(fresh, torch.int32))
+    pool = _varlen_setup(case, contents)
     st0, wn0 = pool.state.clone(), pool.window.clone()
     out = run_prefill(pool, 0, cu, ids_np, tok, dev(case["conv_w"]), 64, io)
     torch.cuda.synchronize()
     assert pool.error() == 0
-    res = _oracle_groups(s, [3], tok, case["conv_w"], cu, ids_np,
-                         contents={int(k): v for k, v in contents.items()})
-    _check_groups(pool, res, out, ids_np, io)
+    st, wn = _start_contents(case, contents)
+    ref = oracle_pool_workers.prefill_all_groups(s, tok, case["conv_w"], cu, np.arange(len(ids_np)),
+                                                 st, wn)
+    _check_layer(pool, out, ids_np, ref, io)
     mask = torch.ones(case["n_slots"], dtype=torch.bool, device="cuda")
     mask[torch.from_numpy(ids_np.astype(np.int64)).cuda()] = False
     assert torch.equal(pool.state[mask], st0[mask]) and torch.equal(pool.window[mask], wn0[mask])
+
+
+def test_varlen_continuing_slots_from_a_prefix_prefill(oracle_pool_workers):
+    """The varlen workload whose 4 continuing slots got their state and
+    window from an earlier prefill (prefixes of 64..512 tokens, one call),
+    as a scheduler's earlier chunk would leave them: the prefix and the
+    varlen call are both run by the oracle, every group compared."""
+    case = syn.varlen_case()
+    s, io, tok = case["shapes"], case["io"], case["tokens"]
+    cu, ids_np, cont = case["cu_seqlens"], case["slot_ids"], case["continuing"]
+    rng = np.random.default_rng(1013)
+    plen = rng.integers(64, 513, size=int(cont.sum()))
+    pcu = np.concatenate([[0], np.cumsum(plen)]).astype(np.int32)
+    ptok = syn.draw_tokens(rng, s, (int(pcu[-1]),), io)
+    pids = ids_np[cont]
+    say(f"varlen after prefixes {plen.tolist()} into slots {pids.tolist()}")
+    pool = make_pool(s, case["n_slots"], io)
+    scramble_pool(pool, 33)
+    pool.reset(dev(ids_np, torch.int32))
+    w = dev(case["conv_w"])
+    run_prefill(pool, 0, pcu, pids, ptok, w, 64, io)
+    out = run_prefill(pool, 0, cu, ids_np, tok, w, 64, io)
+    torch.cuda.synchronize()
+    assert pool.error() == 0
+    _, S1, X1 = oracle_pool_workers.prefill_all_groups(s, ptok, case["conv_w"], pcu,
+                                                       np.arange(len(pids)))
+    n = len(ids_np)
+    st = np.zeros((n, 1, s.h_v, s.d_v, s.d_k))
+    wn = np.zeros((n, 1, s.conv_k - 1, s.c_conv))
+    st[cont], wn[cont] = S1, X1
+    ref = oracle_pool_workers.prefill_all_groups(s, tok, case["conv_w"], cu, np.arange(n), st, wn)
+    _check_layer(pool, out, ids_np, ref, io)
+
+
+def test_one_sequence_with_outputs_beyond_2gib(oracle_pool_workers):
+    """One fp32 sequence whose output rows run past 2^31 bytes (h_v = 64,
+    d = 128: 32 KiB per token, 66,236 tokens) in one call: equal to the
+    same tokens as 512-token calls, and the last q/k group against the
+    oracle over the whole sequence."""
+    s, io = syn.Shapes(16, 64, 128, 128, 4), "f32"
+    T = 65536 + 700
+    say(f"one sequence of {T} tokens, {s}, outputs {T * s.h_v * s.d_v * 4 / 2**30:.2f} GiB")
+    g = torch.Generator(device="cuda").manual_seed(2024)
+    qk = torch.randn((T, 2, s.h_k, s.d_k), generator=g, device="cuda")
+    qk = qk / qk.norm(dim=-1, keepdim=True)
+    td = {"q": qk[:, 0].contiguous(), "k": qk[:, 1].contiguous()}
+    del qk
+    td["v"] = torch.randn((T, s.h_v, s.d_v), generator=g, device="cuda")
+    td["b"] = torch.sigmoid(torch.randn((T, s.h_v), generator=g, device="cuda"))
+    td["a"] = torch.exp(-torch.nn.functional.softplus(torch.randn((T, s.h_v), generator=g,
+                                                                   device="cuda")))
+    w_np = syn.draw_conv_weights(np.random.default_rng(2025), s)
+    w = dev(w_np)
+    p1 = make_pool(s, 2, io)
+    o1 = torch.full((T, s.h_v, s.d_v), float("nan"), device="cuda")
+    ws = torch.empty(p1.prefill_workspace_bytes(1, T, 64), dtype=torch.uint8, device="cuda")
+    one = dev(np.array([1], np.int32), torch.int32)
+    p1.prefill(0, dev(np.array([0, T], np.int32), torch.int32), one, T, 64, td["q"], td["k"],
+               td["v"], td["a"], td["b"], w, o1, ws)
+    del ws
+    p2 = make_pool(s, 2, io)
+    o2 = torch.full_like(o1, float("nan"))
+    ws = torch.empty(p2.prefill_workspace_bytes(1, 512, 64), dtype=torch.uint8, device="cuda")
+    for c0 in range(0, T, 512):
+        c1 = min(c0 + 512, T)
+        p2.prefill(0, dev(np.array([0, c1 - c0], np.int32), torch.int32), one, c1 - c0, 64,
+                   *(td[n][c0:c1] for n in "qkvab"), w, o2[c0:c1], ws)
+    torch.cuda.synchronize()
+    assert p1.error() == 0 and p2.error() == 0
+    assert torch.isfinite(o1).all(), "rows of the one-call run were not written"
+    past = 2 ** 31 // (s.h_v * s.d_v * 4)     # first token whose row starts at 2 GiB
+    check_f32_dev("rows past 2 GiB: one call vs 512-token calls", o1[past:], o2[past:])
+    check_f32_dev("all rows: one call vs 512-token calls", o1, o2)
+    check_f32_dev("state: one call vs 512-token calls", p1.state[1], p2.state[1])
+    gq = s.h_k - 1
+    G = s.group
+    hs = slice(gq * G, (gq + 1) * G)
+    tok = {"q": host(td["q"][:, gq:gq + 1]).astype(np.float32),
+           "k": host(td["k"][:, gq:gq + 1]).astype(np.float32),
+           "v": host(td["v"][:, hs]).astype(np.float32),
+           "a": host(td["a"][:, hs]).astype(np.float32), "b": host(td["b"][:, hs]).astype(np.float32)}
+    sub = syn.Shapes(1, G, s.d_k, s.d_v, s.conv_k)
+    ch = oracle_pool_workers.group_channels(s, gq)
+    ref, S, X = oracle_pool_workers.prefill_all_groups(sub, tok, w_np[ch], np.array([0, T]),
+                                                       np.array([0]))
+    check_out(f"group {gq} outputs vs oracle", host(o1[:, hs]), ref, io)
+    check_f32(f"group {gq} state vs oracle", host(p1.state[1][:, hs]), S[0])
 
 
 @pytest.mark.parametrize("d,chunk,lens,io", [

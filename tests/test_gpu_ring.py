@@ -42,8 +42,10 @@ def _same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-def _run_cycles(s, io, ring_len, n_tok, n_cycles, n_slots, ids_np, seed, acc_fn=None):
-    """Verify -> compare with the oracle -> commit, n_cycles times, then flush."""
+def _run_cycles(s, io, ring_len, n_tok, n_cycles, n_slots, ids_np, seed, acc_fn=None,
+                tok_fn=None):
+    """Verify -> compare with the oracle -> commit, n_cycles times, then flush.
+    tok_fn(tok, rng), if given, edits each cycle's drawn tokens in place."""
     rng = np.random.default_rng(seed)
     n = len(ids_np)
     w_np = syn.draw_conv_weights(rng, s)
@@ -67,6 +69,8 @@ def _run_cycles(s, io, ring_len, n_tok, n_cycles, n_slots, ids_np, seed, acc_fn=
     folds = 0
     for cyc in range(n_cycles):
         tok = syn.draw_tokens(rng, s, (n, n_tok), io)
+        if tok_fn is not None:
+            tok_fn(tok, rng)
         td = tokens_to_dev(tok, io)
         acc = (acc_fn(rng, cyc, n) if acc_fn else rng.integers(0, n_tok + 1, size=n)).astype(np.int32)
         before = _snapshot(pool)
@@ -102,6 +106,27 @@ def _run_cycles(s, io, ring_len, n_tok, n_cycles, n_slots, ids_np, seed, acc_fn=
     assert _same(untouched, [x[mask] for x in _snapshot(pool)]), "an untouched slot changed"
     assert pool.error() == 0
     return folds
+
+
+def _vanishing_decay(tok, rng):
+    """a = 1e-30 or 1e-45 (below the kernels' clamp of log a at -87) on a
+    fifth of the tokens, a = 1 on another fifth."""
+    u = rng.random(tok["a"].shape)
+    tok["a"][u < 0.1] = np.float32(1e-30)
+    tok["a"][(u >= 0.1) & (u < 0.2)] = np.float32(1e-45)
+    tok["a"][(u >= 0.2) & (u < 0.4)] = 1.0
+
+
+@pytest.mark.parametrize("io,ring_len,n_tok", [("bf16", 8, 4), ("f32", 24, 8)])
+def test_ring_cycles_vanishing_decay_vs_oracle(io, ring_len, n_tok):
+    """Ring verify/commit/flush with decays that make the state forget
+    (down to below the clamp) and with no decay, against the oracle."""
+    s = syn.Shapes(2, 4, 128, 128, 4)
+    say(f"ring cycles, vanishing decay: io={io} L={ring_len} n_tok={n_tok}")
+    ids_np = np.array([2, 6, 0, 3], np.int32)
+    folds = _run_cycles(s, io, ring_len, n_tok, 10, 8, ids_np, 700 + ring_len,
+                        tok_fn=_vanishing_decay)
+    assert folds > 0, "no cycle reached a fold"
 
 
 @pytest.mark.parametrize("h_k,h_v,d,io,ring_len,n_tok", [
