@@ -26,11 +26,13 @@ GDN_ERR_HOST = -7
 GDN_F32 = 0
 GDN_BF16 = 1
 GDN_VALIDATE = 1
+GDN_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = (
     "gdn_pool_bytes", "gdn_pool_create", "gdn_pool_destroy", "gdn_slot_reset",
     "gdn_decode_step", "gdn_verify_step", "gdn_prefill_workspace_bytes",
-    "gdn_prefill_chunked", "gdn_prefill_chunked_ckpt", "gdn_slot_copy", "gdn_ring_verify",
+    "gdn_prefill_chunked", "gdn_prefill_chunked_static", "gdn_prefill_chunked_ckpt",
+    "gdn_slot_copy", "gdn_ring_verify",
     "gdn_ring_commit", "gdn_ring_flush", "gdn_in_proj_workspace_bytes", "gdn_in_proj",
     "gdn_pool_error", "gdn_status_string",
 )
@@ -77,6 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_verify_step": [P, I32, I32, P, I32, P, P, P, P, P, P, P, P, P],
         "gdn_prefill_workspace_bytes": [P, I32, I64, I32, PSZ],
         "gdn_prefill_chunked": [P, I32, I32, P, P, I64, I32, P, P, P, P, P, P, P, P, SZ, P],
+        "gdn_prefill_chunked_static": [P, I32, I32, P, P, I64, I32, P, P, P, P, P, P, P, P],
         "gdn_prefill_chunked_ckpt": [P, I32, I32, P, P, I64, I32, P, P, P, P, P, P, P, I32, P, P,
                                      P, SZ, P],
         "gdn_ring_verify": [P, I32, I32, P, I32, P, P, P, P, P, P, P, P],
@@ -339,6 +342,20 @@ class Pool:
                                        total_tokens, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                        _ptr(b), _ptr(conv_w), _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream(stream)), "gdn_prefill_chunked")
+        return out
+
+    def prefill_static(self, layer, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v, a, b,
+                       conv_w, out, stream=None):
+        """gdn_prefill_chunked_static: the workspace is the library's own
+        device array (no allocation)."""
+        lib = load_library()
+        n_seq = int(slot_ids.numel())
+        self._prefill_args(n_seq, cu_seqlens, slot_ids, total_tokens, q, k, v, a, b, conv_w, out)
+        _check(lib.gdn_prefill_chunked_static(self._h, layer, n_seq, _ptr(cu_seqlens),
+                                              _ptr(slot_ids), total_tokens, chunk, _ptr(q),
+                                              _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(conv_w),
+                                              _ptr(out), _stream(stream)),
+               "gdn_prefill_chunked_static")
         return out
 
     def prefill_ckpt(self, layer, cu_seqlens, slot_ids, total_tokens, chunk, q, k, v, a, b,

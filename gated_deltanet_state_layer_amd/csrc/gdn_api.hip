@@ -373,6 +373,25 @@ gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
     });
 }
 
+gdn_status gdn_prefill_chunked_static(gdn_pool* pool, int32_t layer, int32_t n_seq,
+                                      const int32_t* cu_seqlens, const int32_t* slot_ids,
+                                      int64_t total_tokens, int32_t chunk, const void* q,
+                                      const void* k, const void* v, const float* a,
+                                      const float* b, const float* conv_w, void* out,
+                                      void* stream) {
+    return guarded([&]() -> gdn_status {
+        if (!pool || n_seq < 0 || total_tokens < 0) return GDN_ERR_INVALID_ARG;
+        if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
+        if (prefill_workspace_bytes(pool, n_seq, total_tokens, chunk) > kStaticScratchBytes)
+            return GDN_ERR_WORKSPACE;
+        void* ws = nullptr;
+        if (prefill_static_scratch(&ws) != hipSuccess) return GDN_ERR_HIP;
+        return prefill_common(pool, layer, n_seq, cu_seqlens, slot_ids, total_tokens, chunk, q, k,
+                              v, a, b, conv_w, out, 0, nullptr, nullptr, ws, kStaticScratchBytes,
+                              stream);
+    });
+}
+
 gdn_status gdn_prefill_chunked_ckpt(gdn_pool* pool, int32_t layer, int32_t n_seq,
                                     const int32_t* cu_seqlens, const int32_t* slot_ids,
                                     int64_t total_tokens, int32_t chunk, const void* q,

@@ -162,6 +162,10 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t n_tok, int32_t hidden, c
                           void* workspace, hipStream_t stream);
 size_t prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
                                int32_t chunk);
+// The static prefill scratch (kStaticScratchBytes on every device): its
+// address on the current device, resolved on the first call there.
+constexpr size_t kStaticScratchBytes = GDN_STATIC_SCRATCH_BYTES;
+hipError_t prefill_static_scratch(void** ptr);
 hipError_t launch_prefill(const gdn_pool* pool, int32_t layer, int32_t n_seq,
                           const int32_t* cu_seqlens, const int32_t* slot_ids,
                           int64_t total_tokens, int32_t chunk, const void* q, const void* k,

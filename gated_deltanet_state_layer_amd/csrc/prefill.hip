@@ -31,6 +31,8 @@
 // order, so the scan's serial loop only splits what it produces itself; the
 // transposed K^ of the state update is read from LDS with the gfx950
 // transposing load instead of being stored twice.
+#include <mutex>
+
 #include "gdn_common.h"
 #include "mfma_split.h"
 
@@ -1283,7 +1285,39 @@ hipError_t launch_d(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq, co
                               conv_w, out, ck, stream);
 }
 
+// Device-resident prefill workspace for callers that cannot allocate
+// (gdn_prefill_chunked_static).  Every device the library runs on holds one
+// until the process ends.  Its name is only a host-side handle: the kernels
+// get the per-device address that hipGetSymbolAddress returns.
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
 }  // namespace
+
+hipError_t prefill_static_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // first call on this device (the device is current): resolve the
+        // array's address on it once
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 size_t prefill_workspace_bytes(const gdn_pool* pool, int32_t n_seq, int64_t total_tokens,
                                int32_t chunk) {

@@ -221,6 +221,28 @@ gdn_status gdn_prefill_chunked(gdn_pool* pool, int32_t layer, int32_t n_seq,
                                const float* conv_w, void* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gdn_prefill_chunked with its workspace taken from a device array that the
+ * library holds on every device it runs on, GDN_STATIC_SCRATCH_BYTES (64 MiB)
+ * each, until the process ends.  The call itself allocates no device memory
+ * (in GDN_VALIDATE mode the host-side index checks copy the index arrays to
+ * host memory, as for every call).  Same arguments, layout and results as
+ * gdn_prefill_chunked; returns GDN_ERR_WORKSPACE, enqueuing nothing, when
+ * gdn_prefill_workspace_bytes(n_seq, total_tokens, chunk) exceeds
+ * GDN_STATIC_SCRATCH_BYTES (e.g. about 1,900 tokens of one sequence with
+ * h_k = 16, h_v = 32, d = 128, chunk 64).  All calls on one device share the
+ * array, which keeps the last call's contents: calls that may overlap on one
+ * device (different streams, no ordering between them) race and must be
+ * serialised by the caller. */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_prefill_chunked_static(gdn_pool* pool, int32_t layer, int32_t n_seq,
+                                      const int32_t* cu_seqlens, const int32_t* slot_ids,
+                                      int64_t total_tokens, int32_t chunk, const void* q,
+                                      const void* k, const void* v, const float* a,
+                                      const float* b, const float* conv_w, void* out,
+                                      void* stream);
+
 /* gdn_prefill_chunked that also stores state checkpoints inside the
  * sequences, for prefix caching (the pages: a cache hit is only possible
  * where a state checkpoint was stored, and a state is copied whole).
