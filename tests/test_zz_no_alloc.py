@@ -54,8 +54,11 @@ def test_static_prefill_equals_workspace_prefill_twice():
     contents = syn.draw_pool_contents(5, [1, 4, 6], s, io)
     for p in _POOLS:
         load_slots(p, contents)
-    # first call: 3 sequences, 1,180 tokens (about 3/4 of the array)
-    lens, ids = np.array([700, 33, 447]), np.array([1, 4, 6], np.int32)
+    # first call: 3 sequences filling about 3/4 of the array
+    cap = G.GDN_STATIC_SCRATCH_BYTES
+    per_tok = _POOLS[1].prefill_workspace_bytes(1, 6400, 64) / 6400
+    n1 = int(0.75 * cap / per_tok)
+    lens, ids = np.array([n1 * 6 // 10, 33, n1 - n1 * 6 // 10 - 33]), np.array([1, 4, 6], np.int32)
     need = _POOLS[1].prefill_workspace_bytes(3, int(lens.sum()), 64)
     say(f"call 1: {lens.tolist()} tokens, workspace {need} of {G.GDN_STATIC_SCRATCH_BYTES} B")
     assert need <= G.GDN_STATIC_SCRATCH_BYTES
@@ -78,8 +81,9 @@ def test_static_prefill_rejects_a_call_beyond_the_array():
     from gated_deltanet_state_layer_amd import binding as G
     s, io = syn.QWEN3_NEXT, "bf16"
     pool = make_pool(s, 2, io)
-    T = 4096
-    assert pool.prefill_workspace_bytes(1, T, 64) > G.GDN_STATIC_SCRATCH_BYTES
+    T = 64
+    while pool.prefill_workspace_bytes(1, T, 64) <= G.GDN_STATIC_SCRATCH_BYTES:
+        T += 64
     st0 = pool.state.clone()
     td = tokens_to_dev(syn.draw_tokens(np.random.default_rng(3), s, (T,), io), io)
     w = dev(syn.draw_conv_weights(np.random.default_rng(4), s))
