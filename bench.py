@@ -50,7 +50,8 @@ DECODE_SRC_SHA256 = "4d5ce4cc06c97678c5f999c3c12b391658c7d9fe160415c63ef74b914d4
 # source they were taken on (PREFILL_SRC_SHA256), else reported as null.
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
-PREFILL_SRC_SHA256 = "900a1ca1b0eb155a1fa9c45e61a31d87ec63d6f4e64fc682b5738aa576f3f629"
+# (profiles/prefill_mfma_counters.txt; profiles/prefill_hbm_traffic.txt has the bytes)
+PREFILL_SRC_SHA256 = "370a22a57d504a00f7e611caa085d9527c22a8e9707fd2e0fec375d166ceaa32"
 
 
 def prefill_exec_flop_per_token(case):
@@ -85,7 +86,7 @@ def parse():
     p.add_argument("--no-ring", action="store_true")
     p.add_argument("--no-in-proj", action="store_true")
     p.add_argument("--only", choices=["decode", "verify", "ring", "in_proj", "prefill", "copy",
-                                      "gemm"],
+                                      "gemm", "stream"],
                    default=None,
                    help="run one workload only (for profiling)")
     p.add_argument("--prefill-case", choices=["single", "split512", "varlen", "all"], default="all",
@@ -382,18 +383,24 @@ def bench_in_proj(args, torch, G, syn):
     return res
 
 
-def prefill_flops_per_token(s, C):
+def prefill_flops_per_token(s, C, kernel_form=False):
     """Algorithmic flops per token of the chunked form (2 per multiply-add,
-    triangular products counted as triangles), per chunk divided by C:
-      per q/k head: K K^T and Q K^T lower triangles      2 * C * d_k
-      per value head: (I+A)^-1 by substitution            C^2 / 3
-                      K S0^T, Q S0^T, U^T K               3 * 2 * d_k * d_v
-                      T' R and P U (lower triangles)      2 * C * d_v
-    """
+    triangular products counted as triangles, incl. the diagonal), per chunk
+    divided by C, in the WY form of the chunked delta rule:
+      per q/k head:   K K^T and Q K^T (lower triangles)         2 * C(C+1)/2 * d_k * 2
+      per value head: (I+A)^-1 by substitution                    C^3 / 3
+                      W = T diag(b gamma) K, U_v = T diag(b) V,
+                      P U (triangles)                             3 * C(C+1)/2 * d * 2
+                      W S0^T, Q S0^T, U^T K' (dense)              3 * C * d_k * d_v * 2
+    (4.254 MFLOP per token at the Qwen3-Next shapes, chunk 64).  The kernels
+    form U = T'(V - diag(gamma) K S0^T) instead of W and U_v, one triangular
+    product fewer per value head (3.988 MFLOP per token: kernel_form=True)."""
     dk, dv = s.d_k, s.d_v
-    per_k = 2 * C * dk
-    per_v = C * C / 3.0 + 6 * dk * dv + 2 * C * dv
-    return s.h_k * per_k + s.h_v * per_v
+    tri = C * (C + 1) / 2
+    per_k = 2 * tri * dk * 2
+    n_tri = 2 if kernel_form else 3
+    per_v = C ** 3 / 3.0 + n_tri * tri * dv * 2 + 3 * C * dk * dv * 2
+    return (s.h_k * per_k + s.h_v * per_v) / C
 
 
 def _prefill_inputs(torch, tok):
@@ -427,7 +434,8 @@ def bench_prefill(args, torch, G, syn):
     res = {}
     io = 2
     tok_bytes = (2 * s.h_k * s.d_k + s.h_v * s.d_v) * io + 2 * s.h_v * 4 + s.h_v * s.d_v * io
-    state_rw = 2 * s.h_v * s.d_v * s.d_k * 4
+    # per sequence: state read + write, conv window read + write
+    state_rw = 2 * s.h_v * s.d_v * s.d_k * 4 + 2 * (s.conv_k - 1) * s.c_conv * io
     fl_tok = prefill_flops_per_token(s, C)
     # One 8192-token sequence: one call, and 16 scheduler chunks of 512.
     case = syn.prefill_case()
@@ -443,7 +451,8 @@ def bench_prefill(args, torch, G, syn):
         t1 = _time_prefill(args, torch, pool, [(0, T, [0, T])], ids, d, w, out, C, reps)
         b = T * tok_bytes + state_rw
         res["single"] = {"workload": "one 8192-token sequence, chunk 64", "us": t1 * 1e6,
-                         "tok_s": T / t1, "GBps": b / t1 / 1e9, "alg_TFLOPs": fl_tok * T / t1 / 1e12,
+                         "tok_s": T / t1, "GBps": b / t1 / 1e9, "hbm_frac": b / t1 / 1e9 / HBM_PEAK_GBPS,
+                         "alg_TFLOPs": fl_tok * T / t1 / 1e12,
                          "mfma_frac_alg": fl_tok * T / t1 / 1e12 / BF16_PEAK_TFLOPS}
         ex = prefill_exec_flop_per_token("single")
         res["single"]["mfma_frac_exec"] = None if ex is None else ex * T / t1 / 1e12 / BF16_PEAK_TFLOPS
@@ -466,15 +475,59 @@ def bench_prefill(args, torch, G, syn):
     out = torch.empty((Tv, s.h_v, s.d_v), dtype=torch.bfloat16, device="cuda")
     ids = torch.from_numpy(case["slot_ids"]).cuda()
     tv = _time_prefill(args, torch, pool, [(0, Tv, [int(x) for x in cu])], ids, d, w, out, C, reps)
-    bv = Tv * tok_bytes + len(cu) * state_rw
+    bv = Tv * tok_bytes + (len(cu) - 1) * state_rw
     res["varlen"] = {"workload": f"16 packed sequences, {Tv} tokens (lengths U[128,4096])",
                      "us": tv * 1e6, "tok_s": Tv / tv, "GBps": bv / tv / 1e9,
+                     "hbm_frac": bv / tv / 1e9 / HBM_PEAK_GBPS,
                      "alg_TFLOPs": fl_tok * Tv / tv / 1e12,
                      "mfma_frac_alg": fl_tok * Tv / tv / 1e12 / BF16_PEAK_TFLOPS}
     ex = prefill_exec_flop_per_token("varlen")
     res["varlen"]["mfma_frac_exec"] = None if ex is None else ex * Tv / tv / 1e12 / BF16_PEAK_TFLOPS
     assert pool.error() == 0
     return res
+
+
+def bench_stream_ceiling(args, torch):
+    """The state stream of the decode step with nothing else, through the
+    bandwidth probe (libgdn_probe.so, not part of the libgdn ABI): the same
+    256-slot fp32 pool, the same four rotating sets of 64 slot ids in random
+    order, each slot's 2 MiB read once and written once in place with the
+    decode kernel's access pattern.  Its rate is the ceiling the decode state
+    traffic can reach on this machine; decode, verify and the ring are reported
+    against it beside the published 8 TB/s."""
+    import ctypes
+    from gated_deltanet_state_layer_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        raise RuntimeError(f"{B.PROBE_LIB} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.gdn_probe_stream_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                           ctypes.c_void_p]
+    lib.gdn_probe_stream_tiles.restype = ctypes.c_int
+    n_slots, heads, N = 256, 32, 64
+    state = torch.empty(n_slots * heads * 128 * 128, dtype=torch.float32, device="cuda")
+    state.normal_(generator=torch.Generator(device="cuda").manual_seed(99))
+    perm = np.random.default_rng(1001).permutation(n_slots).astype(np.int32)
+    sets = [torch.from_numpy(perm[j * N:(j + 1) * N].copy()).cuda() for j in range(4)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    names = ["2 tiles/workgroup, default loads", "2 tiles/workgroup, non-temporal loads",
+             "1 tile/workgroup, default loads", "1 tile/workgroup, non-temporal loads"]
+    b = N * 2 * heads * 128 * 128 * 4
+    rates = {}
+    for variant, name in enumerate(names):
+        def step(i):
+            rc = lib.gdn_probe_stream_tiles(ctypes.c_void_p(state.data_ptr()), heads,
+                                            ctypes.c_void_p(sets[i % 4].data_ptr()), N, 1.0,
+                                            variant, stream)
+            if rc != 0:
+                raise RuntimeError(f"gdn_probe_stream_tiles: hipError {rc}")
+        rates[name] = b / time_launches(step, max(100, args.steps), 20, torch) / 1e9
+    best = max(rates, key=rates.get)
+    return {"workload": "state stream of the decode step alone: 64 of 256 slots (rotating 4 "
+                        "disjoint sets, random order), 2 MiB read + 2 MiB written per slot",
+            "bytes": b, "GBps": rates[best], "us": b / rates[best] / 1e3, "best": best,
+            "hbm_frac": rates[best] / HBM_PEAK_GBPS, "variants_GBps": rates}
 
 
 def bench_gemm(args, torch):
@@ -499,30 +552,11 @@ def bench_copy(args, torch):
     return {"bytes": 2 * n * 4, "us": t * 1e6, "GBps": 2 * n * 4 / t / 1e9}
 
 
-def cpu_baseline(syn):
-    """The fp64 oracle, as it stands, on a bounded sample of the decode workload."""
-    from oracle import gdn_oracle as O
-    s = syn.QWEN3_NEXT
-    case = syn.decode_case(64)
-    ids = case["slot_ids"]
-    contents = syn.draw_pool_contents(case["pool_seed"], ids[:16], s, "bf16")
-    op = O.OraclePool(16, 1, s)
-    for j, sl in enumerate(ids[:16]):
-        op.S[j], op.X[j] = contents[int(sl)]
-    tok = case["tokens"]
-    n_done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < 10.0:
-        op.decode(0, np.arange(16), *(tok[n][:16] for n in "qkvab"), case["conv_w"])
-        n_done += 16
-    dt = time.perf_counter() - t0
+def cpu_threads():
     try:
-        cores = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": n_done / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
-            "sample": f"{n_done} decode tokens (16-slot decode steps, Qwen3-Next shapes, fp64 "
-                      f"literal matrix form) in {dt:.1f} s on {cpu_model()}"}
+        return os.cpu_count() or 1
 
 
 def cpu_model():
@@ -535,42 +569,106 @@ def cpu_model():
     return platform.processor() or "host"
 
 
-def cpu_other(syn):
-    """The fp64 oracle on bounded samples of the other workloads (context
-    beside cpu_baseline): the 8192-token prefill token by token and in its
-    chunked form (chunk 64), and the 4-token verify, each for a few seconds."""
+def _threaded(jobs, fn, nthr):
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(nthr) as ex:
+        return list(ex.map(fn, jobs))
+
+
+def _timed_rounds(round_fn, seconds, min_rounds=1):
+    round_fn()                       # warm-up
+    n, t0 = 0, time.perf_counter()
+    while n < min_rounds or time.perf_counter() - t0 < seconds:
+        round_fn()
+        n += 1
+    return n, time.perf_counter() - t0
+
+
+def cpu_baseline(syn):
+    """The oracle's fp32 variant (rank-1 form), as it stands, on the host:
+    decode steps of the 64-of-256-slot workload with the slots split over
+    one thread per available core (NumPy releases the GIL in the state
+    arithmetic; BLAS threads are held at 1 inside each thread), for about 6 s.
+    Returns (cpu_baseline, details), the details being bounded samples of the
+    other workloads run the same way."""
     from oracle import gdn_oracle as O
-    s = syn.QWEN3_NEXT
-    res = {}
-    case = syn.prefill_case()
-    tok = case["tokens"]
-    op = O.OraclePool(1, 1, s)
-    n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < 4.0 and n < 8192:
-        op.prefill(0, np.array([0, 16]), np.array([0]), *(tok[m][n:n + 16] for m in "qkvab"),
-                   case["conv_w"])
-        n += 16
-    res["prefill_token_loop_tok_s"] = n / (time.perf_counter() - t0)
-    S0 = np.zeros((s.h_v, s.d_v, s.d_k))
-    X0 = np.zeros((s.conv_k - 1, s.c_conv))
-    n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < 4.0 and n < 8192:
-        _, S0, X0 = O.chunked_sequence(S0, X0, *(tok[m][n:n + 256] for m in "qkvab"),
-                                       case["conv_w"], s, 64)
-        n += 256
-    res["prefill_chunked_tok_s"] = n / (time.perf_counter() - t0)
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:
+        limiter = None
+    s, io = syn.QWEN3_NEXT, "bf16"
+    nthr = cpu_threads()
+    f32 = np.float32
+
+    def slot_pools(ids, contents, shards):
+        pools = []
+        for sh in shards:
+            op = O.OraclePool(len(sh), 1, s, form="rank1", dtype=f32)
+            for j, i in enumerate(sh):
+                op.S[j], op.X[j] = contents[int(ids[i])]
+            pools.append((op, sh))
+        return pools
+
+    # decode, N slots
+    def decode_rate(N, seconds):
+        case = syn.decode_case(N)
+        ids, tok, w = case["slot_ids"], case["tokens"], case["conv_w"]
+        contents = syn.draw_pool_contents(case["pool_seed"], ids, s, io)
+        k = min(nthr, N)
+        pools = slot_pools(ids, contents, [sh for sh in np.array_split(np.arange(N), k) if len(sh)])
+        run = lambda p: p[0].decode(0, np.arange(len(p[1])), *(tok[m][p[1]] for m in "qkvab"), w)
+        n, dt = _timed_rounds(lambda: _threaded(pools, run, k), seconds)
+        return N * n / dt, n, dt, k
+
+    value, n64, dt64, k64 = decode_rate(64, 5.0)
+    detail = {"decode_tok_s": {"64": value}}
+    for N in (1, 4, 16):
+        detail["decode_tok_s"][str(N)] = decode_rate(N, 0.7)[0]
+    # verify: 128 slots x 4 tokens, accept_len U{1..4}
     vc = syn.verify_case()
-    vt = vc["tokens"]
-    op = O.OraclePool(16, 1, s)
-    n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < 4.0:
-        op.verify(0, np.arange(16), 4, *(vt[m][:16] for m in "qkvab"), vc["conv_w"],
-                  vc["accept_len"][:16])
-        n += 64
-    res["verify_tok_s"] = n / (time.perf_counter() - t0)
-    res["sample"] = ("one 8192-token sequence (first tokens, fp64 token loop and chunked form), "
-                     "16 slots x 4-token verify; Qwen3-Next shapes; " + cpu_model())
-    return res
+    vids, vt = vc["slot_ids"], vc["tokens"]
+    contents = syn.draw_pool_contents(vc["pool_seed"], vids, s, io)
+    pools = slot_pools(vids, contents, np.array_split(np.arange(len(vids)), nthr))
+    run = lambda p: p[0].verify(0, np.arange(len(p[1])), 4, *(vt[m][p[1]] for m in "qkvab"),
+                                vc["conv_w"], vc["accept_len"][p[1]])
+    n, dt = _timed_rounds(lambda: _threaded(pools, run, nthr), 2.0)
+    detail["verify_tok_s"] = 128 * 4 * n / dt
+    # prefill, one 8192-token sequence token by token (one thread; the
+    # oracle's step is vectorised over the layer's heads): the first 256 tokens
+    case = syn.prefill_case()
+    tok, w = case["tokens"], case["conv_w"]
+    t0 = time.perf_counter()
+    O.OraclePool(1, 1, s, form="rank1", dtype=f32).prefill(0, [0, 256], [0],
+                                                           *(tok[m][:256] for m in "qkvab"), w)
+    detail["prefill_token_loop_tok_s"] = 256 / (time.perf_counter() - t0)
+    # the same 256 tokens in the chunked form (chunk 64, fp64, one thread)
+    t0 = time.perf_counter()
+    O.chunked_sequence(np.zeros((s.h_v, s.d_v, s.d_k)), np.zeros((s.conv_k - 1, s.c_conv)),
+                       *(tok[m][:256] for m in "qkvab"), w, s, 64)
+    detail["prefill_chunked_fp64_one_thread_tok_s"] = 256 / (time.perf_counter() - t0)
+    # varlen: 16 sequences, one thread per sequence, the first 64 tokens of each
+    vc3 = syn.varlen_case()
+    cu, vtok = vc3["cu_seqlens"], vc3["tokens"]
+    seqs = [{m: vtok[m][cu[j]:cu[j] + 64] for m in "qkvab"} for j in range(len(cu) - 1)]
+    run = lambda t: O.OraclePool(1, 1, s, form="rank1", dtype=f32).prefill(
+        0, [0, 64], [0], *(t[m] for m in "qkvab"), vc3["conv_w"])
+    t0 = time.perf_counter()
+    _threaded(seqs, run, min(nthr, len(seqs)))
+    detail["varlen_tok_s"] = 64 * len(seqs) / (time.perf_counter() - t0)
+    if limiter is not None:
+        limiter.restore_original_limits()
+    detail["threads"] = nthr
+    detail["sample"] = ("decode of 1/4/16 slots ~0.7 s each (slots over up to one thread per "
+                        "core); verify 128 slots x 4 tokens ~2 s (slots over threads); prefill: "
+                        "the first 256 of the 8192 tokens on one thread, token by token (fp32) "
+                        "and in the chunked form (fp64, chunk 64); varlen: the first 64 tokens "
+                        "of each of the 16 sequences, one thread per sequence; fp32 rank-1 "
+                        "oracle unless stated")
+    base = {"value": value, "unit": "tokens/s", "cores": k64, "kind": "oracle",
+            "sample": f"{n64} decode steps of 64 of 256 slots (Qwen3-Next shapes) in {dt64:.1f} s, "
+                      f"fp32 rank-1 oracle, slots over {k64} threads on {cpu_model()}"}
+    return base, detail
 
 
 def main():
@@ -599,6 +697,9 @@ def main():
     if args.only in (None, "prefill") and not args.no_prefill:
         res["prefill"] = bench_prefill(args, torch, G, syn)
         print("# prefill done", file=sys.stderr, flush=True)
+    if args.only in (None, "stream"):
+        res["stream"] = bench_stream_ceiling(args, torch)
+        print(f"# stream ceiling done: {res['stream']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
     if args.only in (None, "copy"):
         res["copy"] = bench_copy(args, torch)
         print("# copy done", file=sys.stderr, flush=True)
@@ -607,8 +708,7 @@ def main():
         print("# gemm done", file=sys.stderr, flush=True)
     cpu = cpu_more = None
     if not args.no_cpu and args.only is None:
-        cpu = cpu_baseline(syn)
-        cpu_more = cpu_other(syn)
+        cpu, cpu_more = cpu_baseline(syn)
         print("# cpu baseline done", file=sys.stderr, flush=True)
     if "decode" not in res:
         print(json.dumps(res))
@@ -647,14 +747,38 @@ def main():
     if res.get("in_proj"):
         line["in_proj"] = res["in_proj"]
     if res.get("prefill"):
-        line["prefill"] = res["prefill"]
+        pf = res["prefill"]
+        one = pf.get("single", {})
+        flat = {"workload": "one 8192-token sequence, chunk 64, h_k=16 h_v=32 d=128, bf16 io, "
+                            "fp32 state (one call)",
+                "alg_MFLOP_per_token": prefill_flops_per_token(syn.QWEN3_NEXT, 64) / 1e6}
+        for k in ("us", "tok_s", "GBps", "hbm_frac", "mfma_frac_alg", "mfma_frac_exec"):
+            if k in one:
+                flat[k] = one[k]
+        if "split512" in pf:
+            flat["split512_us"] = pf["split512"]["us"]
+            if "us" in one:
+                flat["split512_over_single"] = pf["split512"]["us"] / one["us"]
+        if "varlen" in pf:
+            for k in ("us", "tok_s", "mfma_frac_alg", "mfma_frac_exec", "hbm_frac"):
+                flat["varlen_" + k] = pf["varlen"].get(k)
+        line["prefill"] = flat
+        line["prefill_detail"] = pf
+    if res.get("stream"):
+        st = dict(res["stream"])
+        st["decode_frac_of_ceiling"] = dec["gbps"] / st["GBps"]
+        if "verify" in line:
+            st["verify_frac_of_ceiling"] = line["verify"]["GBps"] / st["GBps"]
+        if "verify_ring" in line:
+            st["ring_verify_frac_of_ceiling"] = line["verify_ring"]["verify_GBps"] / st["GBps"]
+        line["stream_ceiling"] = st
     if res.get("copy"):
         line["copy_reference"] = res["copy"]
     if res.get("gemm"):
         line["mfma_reference"] = res["gemm"]
     if cpu:
         line["cpu_baseline"] = cpu
-        line["cpu_other"] = cpu_more
+        line["cpu_baseline_detail"] = cpu_more
     print(json.dumps(line), flush=True)
 
 

@@ -3,7 +3,9 @@
     python -m gated_deltanet_state_layer_amd.build
 
 Compiles every csrc/*.hip to an object under _build/ (in parallel) and links
-them into gated_deltanet_state_layer_amd/libgdn.so.  Always recompiles.
+them into gated_deltanet_state_layer_amd/libgdn.so, then the benchmark's
+bandwidth probe (probe/stream_probe.hip) into libgdn_probe.so.  Always
+recompiles.
 """
 from __future__ import annotations
 
@@ -19,6 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+# The benchmark's measurement probe (not part of the libgdn ABI).
+PROBE_SRC = os.path.join(PKG, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libgdn_probe.so")
 
 ARCH = "gfx950"
 FLAGS = [
@@ -57,8 +62,14 @@ def build(verbose: bool = False, extra=()) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    obj = _compile(PROBE_SRC, extra)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", PROBE_LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -78,7 +78,7 @@ def conv_silu_token(window: np.ndarray, x: np.ndarray, w: np.ndarray):
     y_c = silu( sum_j w[c, j] * X[j, c] ),  X = [window; x]  (row conv_k-1 = x).
     """
     X = np.concatenate([window, x[None, :]], axis=0)
-    z = np.zeros(x.shape[0], dtype=np.float64)
+    z = np.zeros(x.shape[0], dtype=X.dtype)
     for j in range(X.shape[0]):
         z += w[:, j] * X[j]
     return silu(z), X[1:].copy()
@@ -157,10 +157,13 @@ def delta_rule_step(S, q, k, v, a, b, form: str = "matrix"):
     return S_new, o
 
 
-def front_end(window, xq, xk, xv, conv_w, dims, q_scale, eps):
+def front_end(window, xq, xk, xv, conv_w, dims, q_scale, eps, dtype=np.float64):
     """conv+SiLU on the concatenated raw input, then the q/k normalisation.
-    Returns (q_hat [h_k,d_k], k_hat [h_k,d_k], v_hat [h_v,d_v], new window)."""
-    x = np.concatenate([xq.reshape(-1), xk.reshape(-1), xv.reshape(-1)]).astype(np.float64)
+    Returns (q_hat [h_k,d_k], k_hat [h_k,d_k], v_hat [h_v,d_v], new window).
+    All arithmetic in `dtype` (float64 for parity; float32 only for timing)."""
+    x = np.concatenate([xq.reshape(-1), xk.reshape(-1), xv.reshape(-1)]).astype(dtype)
+    window = np.asarray(window, dtype)
+    conv_w = np.asarray(conv_w, dtype)
     y, window = conv_silu_token(window, x, conv_w)
     q, k, v = split_channels(y, dims)
     q = l2norm(q, eps) * q_scale
@@ -168,12 +171,13 @@ def front_end(window, xq, xk, xv, conv_w, dims, q_scale, eps):
     return q, k, v, window
 
 
-def token_step(S, window, xq, xk, xv, a, b, conv_w, dims, q_scale, eps, form="matrix"):
+def token_step(S, window, xq, xk, xv, a, b, conv_w, dims, q_scale, eps, form="matrix",
+               dtype=np.float64):
     """One token through the layer core: conv+SiLU, normalisation, grouped
     heads, recurrence.  Returns (S', window', o [h_v, d_v])."""
-    q, k, v, window = front_end(window, xq, xk, xv, conv_w, dims, q_scale, eps)
+    q, k, v, window = front_end(window, xq, xk, xv, conv_w, dims, q_scale, eps, dtype)
     S, o = delta_rule_step(S, expand_groups(q, dims.h_v), expand_groups(k, dims.h_v), v,
-                           np.asarray(a, np.float64), np.asarray(b, np.float64), form)
+                           np.asarray(a, dtype), np.asarray(b, dtype), form)
     return S, window, o
 
 
@@ -189,17 +193,22 @@ class OraclePool:
 
     S: [n_slots, n_layers, h_v, d_v, d_k] float64
     X: [n_slots, n_layers, conv_k-1, C_conv] float64 (raw inputs, oldest first)
+
+    dtype=np.float32 runs the same steps in fp32: a timing variant only (the
+    CPU baseline of the benchmark), never a parity reference.
     """
 
-    def __init__(self, n_slots, n_layers, dims, q_scale=None, eps=1e-6, form="matrix"):
+    def __init__(self, n_slots, n_layers, dims, q_scale=None, eps=1e-6, form="matrix",
+                 dtype=np.float64):
         self.dims = dims
         self.n_slots, self.n_layers = n_slots, n_layers
         self.q_scale = dims.d_k ** -0.5 if q_scale is None else q_scale
         self.eps = eps
         self.form = form
+        self.dtype = dtype
         c_conv = 2 * dims.h_k * dims.d_k + dims.h_v * dims.d_v
-        self.S = np.zeros((n_slots, n_layers, dims.h_v, dims.d_v, dims.d_k))
-        self.X = np.zeros((n_slots, n_layers, dims.conv_k - 1, c_conv))
+        self.S = np.zeros((n_slots, n_layers, dims.h_v, dims.d_v, dims.d_k), dtype)
+        self.X = np.zeros((n_slots, n_layers, dims.conv_k - 1, c_conv), dtype)
 
     # -- bookkeeping -------------------------------------------------------
     def reset(self, slot_ids):
@@ -212,8 +221,8 @@ class OraclePool:
 
     def _step(self, slot, layer, xq, xk, xv, a, b, conv_w):
         S, X, o = token_step(self.S[slot, layer], self.X[slot, layer], xq, xk, xv, a, b,
-                             np.asarray(conv_w, np.float64), self.dims, self.q_scale,
-                             self.eps, self.form)
+                             np.asarray(conv_w, self.dtype), self.dims, self.q_scale,
+                             self.eps, self.form, self.dtype)
         self.S[slot, layer] = S
         self.X[slot, layer] = X
         return o
@@ -260,8 +269,8 @@ class OraclePool:
                 keep = (S.copy(), X.copy())
             for t in range(n_tok):
                 S, X, out[i, t] = token_step(S, X, q[i, t], k[i, t], v[i, t], a[i, t], b[i, t],
-                                             np.asarray(conv_w, np.float64), self.dims,
-                                             self.q_scale, self.eps, self.form)
+                                             np.asarray(conv_w, self.dtype), self.dims,
+                                             self.q_scale, self.eps, self.form, self.dtype)
                 if t + 1 == accept_len[i]:
                     keep = (S.copy(), X.copy())
             self.S[s, layer], self.X[s, layer] = keep

@@ -404,3 +404,23 @@ def test_in_projection_gate_symmetry_and_limits():
     _, _, _, a, b = O.in_projection(np.full((1, hidden), 100.0), np.concatenate(
         [np.zeros((10, hidden)), np.ones((6, hidden))]), dm)
     assert np.all(a < 1e-200) and np.all(b == 1.0)
+
+
+def test_fp32_timing_variant_tracks_fp64_oracle():
+    """The fp32 variant (used only to time the CPU baseline) runs the same
+    steps: on the tiny layer, after a 64-token prefill, decode and verify, its
+    outputs and states agree with the fp64 oracle to fp32 rounding."""
+    case = syn.tiny_layer_case()
+    s, w = case["shapes"], case["conv_w"]
+    pre, dec = case["prefill"], case["decode"]
+    res = {}
+    for dt in (np.float64, np.float32):
+        op = O.OraclePool(2, 1, s, form="rank1", dtype=dt)
+        o1 = op.prefill(0, [0, 64], [1], *(pre[n] for n in "qkvab"), w)
+        o2 = op.decode(0, [1], *(dec[n][:1] for n in "qkvab"), w)
+        o3 = op.verify(0, [1], 4, *(dec[n][1:5][None] for n in "qkvab"), w, np.array([3]))
+        res[dt] = (o1, o2, o3, op.S.astype(np.float64))
+        assert op.S.dtype == dt
+    for a, b in zip(res[np.float32], res[np.float64]):
+        a, b = np.nan_to_num(a), np.nan_to_num(b)
+        assert np.abs(a - b).max() <= 1e-4 * np.sqrt(np.mean(b * b)), np.abs(a - b).max()
