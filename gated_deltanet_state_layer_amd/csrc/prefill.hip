@@ -533,18 +533,34 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     // (qk, tile, ks), lane (m, q): token tile*16+m, d_k {32ks+4q+i, 32ks+16+4q+i}
     // (the d_k order in which the scan holds its state).  The scan builds the
     // state update's K^T operand from these itself (LDS transpose reads).
+    // Each value is split once: the fragments go to the workspace and, once
+    // every wave has read its rows, to LDS over those rows for KK^T and QK^T.
+    bf16x8* const lfr = reinterpret_cast<bf16x8*>(smem);   // [NQK] fragments
+    static_assert(NQK % (kThreads / 64) == 0, "fragments per wave");
+    static_assert((size_t)NQK * kFragVecs * 16 <= (size_t)(kMaxConvK - 1 + CP) * LD * sizeof(float),
+                  "fragments fit in the staging region (factor_lds_bytes)");
     {
+        constexpr int FPW = NQK / (kThreads / 64);
+        Frag fr[FPW];
         bf16x8* gqk = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
-        for (int f = wave; f < NQK; f += kThreads / 64) {
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) {
+            const int f = wave + i * (kThreads / 64);
             const int qk = f / (NT * NKS), tile = (f / NKS) % NT, ks = f % NKS;
             const float* row = (qk ? xk : xq) + (tile * 16 + m16) * LD + ks * 32 + q4 * 4;
             float x[8];
             ld4x2(x, row, row + 16);
-            store_frag(gqk, f, lane, split8(x));
+            fr[i] = split8(x);
+            store_frag(gqk, f, lane, fr[i]);
         }
+        __syncthreads();   // every wave has read its q^/k^ rows
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) store_frag(lfr, wave + i * (kThreads / 64), lane, fr[i]);
+        __syncthreads();
     }
 
-    // ---- KK^T and QK^T lower-triangular tiles: wave w takes tile row w.
+    // ---- KK^T and QK^T lower-triangular tiles: wave w takes tile row w.  A
+    // and B are the same split fragments (one d_k order on both sides).
     f32x4 kk[NT], qk[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
@@ -555,16 +571,12 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     if (ti < NT) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            float x[8];
-            ld8(x, xk + (ti * 16 + m16) * LD + ks * 32 + q4 * 8);
-            const Frag ak = split8(x);
-            ld8(x, xq + (ti * 16 + m16) * LD + ks * 32 + q4 * 8);
-            const Frag aq = split8(x);
+            const Frag ak = load_frag(lfr, (NT + ti) * NKS + ks, lane);
+            const Frag aq = load_frag(lfr, ti * NKS + ks, lane);
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) {
                 if (jt <= ti) {
-                    ld8(x, xk + (jt * 16 + m16) * LD + ks * 32 + q4 * 8);
-                    const Frag bk = split8(x);
+                    const Frag bk = load_frag(lfr, (NT + jt) * NKS + ks, lane);
                     kk[jt] = mma3(kk[jt], ak, bk);
                     qk[jt] = mma3(qk[jt], aq, bk);
                 }
@@ -617,6 +629,12 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
                     sP[t * LT + s] = pv;
                 }
             }
+        }
+        // T's upper blocks (2b, 2b+1) share a 32-wide k-step with a diagonal
+        // block in the T' fragments: zero them, so the fragments need no mask.
+        for (int e = tid; e < (NT / 2) * 256; e += kThreads) {
+            const int pb = e / 256, r = (e % 256) / 16, c = e % 16;
+            sT[(2 * pb * 16 + r) * LT + (2 * pb + 1) * 16 + c] = 0.f;
         }
         __syncthreads();
 
@@ -695,18 +713,18 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         // T' = T diag(b) and P fragments: (tp, tile, kc), lane (m, q): row
         // tile*16+m, cols 32kc+8q+e.  Both are lower triangular: fragments with
         // kc > tile/2 are all zero and are not written (the scan never fetches
-        // them); inside the others T's upper part is masked here.
+        // them); inside the others T's upper part is zero (see above).
         bf16x8* gtp = W.tpf + ((int64_t)ci * P.h_v + hv) * NTP * kFragVecs;
         for (int f = wave; f < NTP; f += kThreads / 64) {
             const int tp = f / (NT * NKC), tile = (f / NKC) % NT, kc = f % NKC;
             if (kc > tile / 2) continue;
             float x[8];
             ld8(x, (tp ? sP : sT) + (tile * 16 + m16) * LT + kc * 32 + q4 * 8);
-            if (tp == 0) {
+            if (tp == 0) {   // T' = T diag(b); T is zero above the diagonal here
                 float bb[8];
                 ld8(bb, s_b + kc * 32 + q4 * 8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = kc * 32 + q4 * 8 + e <= tile * 16 + m16 ? x[e] * bb[e] : 0.f;
+                for (int e = 0; e < 8; ++e) x[e] *= bb[e];
             }
             store_frag(gtp, f, lane, split8(x));
         }
