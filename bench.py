@@ -31,16 +31,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 
-# HBM traffic of the decode kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
-# then WRITE_SIZE, KiB per dispatch, averaged over the timed launches), each
-# scaled by bytes / counter of torch's copy kernel over 512 MiB measured the
-# same way (profiles/decode_hbm_traffic.txt).  Valid only for the kernel
-# source they were taken on: DECODE_SRC_SHA256 is checked at run time and the
-# traffic is reported as null when the source has changed since.
-DECODE_TRAFFIC = {"fetch_kib": 67857.33, "write_kib": 134740.77,
-                  "copy_fetch_scale": 536870912 / (262155.93 * 1024),
-                  "copy_write_scale": 536870912 / (524288.0 * 1024)}
-DECODE_SRC_SHA256 = "4d5ce4cc06c97678c5f999c3c12b391658c7d9fe160415c63ef74b914d4982f7"
+# HBM traffic of the decode kernel (decode_heads_kernel, in decode_rows.hip)
+# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch, averaged over the timed launches), each scaled by bytes / counter
+# of torch's copy kernel over 512 MiB measured the same way
+# (profiles/decode_hbm_traffic.txt).  Valid only for the kernel source they
+# were taken on: DECODE_SRC_SHA256 is checked at run time and the traffic is
+# reported as null when the source has changed since.
+DECODE_TRAFFIC = None
+DECODE_SRC_SHA256 = None
 
 
 # Executed bf16 MFMA flops of the prefill kernels per token, from rocprofv3
@@ -67,7 +66,7 @@ def decode_traffic_bytes():
     import hashlib
     if not DECODE_TRAFFIC or not DECODE_SRC_SHA256:
         return None
-    src = os.path.join(ROOT, "gated_deltanet_state_layer_amd", "csrc", "decode_verify.hip")
+    src = os.path.join(ROOT, "gated_deltanet_state_layer_amd", "csrc", "decode_rows.hip")
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != DECODE_SRC_SHA256:
         return None
     t = DECODE_TRAFFIC
@@ -729,7 +728,7 @@ def main():
         "hbm_frac": dec["gbps"] / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": dec["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dec["gbps"] / HBM_PEAK_GBPS, "traffic": decode_traffic_bytes(),
-                     "kernel": "decode_verify_kernel<128,bf16>",
+                     "kernel": "decode_heads_kernel<128,bf16,4,1,true>",
                      "bytes_per_launch": dec["bytes"], "us_per_launch": dec["sec"] * 1e6},
         "decode_per_launch": dec.get("per_launch"),
         "decode_hot_cache_GBps": dec.get("hot_gbps"),
@@ -739,6 +738,7 @@ def main():
     if "verify" in res:
         v = res["verify"]
         line["verify"] = {"workload": "128 slots x 4 tokens, accept_len U{1..4}",
+                          "kernel": "decode_heads_kernel<128,bf16,4,4,false>",
                           "us": v["sec"] * 1e6, "tok_s": v["tok_s"],
                           "accepted_tok_s": v["accepted_tok_s"], "GBps": v["gbps"],
                           "hbm_frac": v["gbps"] / HBM_PEAK_GBPS}

@@ -26,6 +26,7 @@ GDN_ERR_HOST = -7
 GDN_F32 = 0
 GDN_BF16 = 1
 GDN_VALIDATE = 1
+GDN_GROUP_KERNEL = 2
 GDN_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = (

@@ -23,6 +23,9 @@
 // ("Plan (research-based)", "What the research found" and "Why >150 is still
 // reachable": no per-position state snapshots).  Decode is the same kernel
 // with one token, so verify positions are bitwise equal to decode steps.
+// With d_k = 64 or 128 the library runs the head-split kernels of
+// decode_rows.hip instead (same arithmetic, bitwise equal); this kernel
+// serves the other head sizes.
 #include "gdn_common.h"
 
 namespace gdn {

@@ -31,7 +31,7 @@ gdn_status check_desc(const gdn_pool_desc* d) {
     if (!(d->q_scale >= 0.f) || !(d->norm_eps >= 0.f) || std::isinf(d->q_scale) ||
         std::isinf(d->norm_eps))
         return GDN_ERR_INVALID_ARG;
-    if (d->flags & ~GDN_VALIDATE) return GDN_ERR_INVALID_ARG;
+    if (d->flags & ~(GDN_VALIDATE | GDN_GROUP_KERNEL)) return GDN_ERR_INVALID_ARG;
     if (d->ring_len < 0) return GDN_ERR_INVALID_ARG;
     if (d->ring_len > kMaxRingSolve - kMaxVerifyTokens) return GDN_ERR_UNSUPPORTED;
     if (d->d_k != d->d_v) return GDN_ERR_UNSUPPORTED;
@@ -322,11 +322,17 @@ gdn_status gdn_decode_step(gdn_pool* pool, int32_t layer, int32_t n, const int32
         }
         // Few entries: split each head's rows over several workgroups so that
         // more CUs stream the state (same arithmetic, bitwise equal results).
-        const int nrb = decode_rows_split(pool, n);
-        const hipError_t e = nrb > 1 ? launch_decode_rows(pool, nrb, layer, n, slot_ids, q, k, v, a, b,
-                                                          conv_w, out, s)
-                                     : launch_decode_verify(pool, layer, n, slot_ids, 1, q, k, v, a, b,
-                                                            conv_w, nullptr, out, s);
+        // Otherwise one value head per workgroup (d_k 64 or 128), else the
+        // one-workgroup-per-group kernel.  All three are bitwise equal.
+        const bool group = pool->desc.flags & GDN_GROUP_KERNEL;
+        const int nrb = group ? 1 : decode_rows_split(pool, n);
+        const hipError_t e =
+            nrb > 1 ? launch_decode_rows(pool, nrb, layer, n, slot_ids, q, k, v, a, b, conv_w, out, s)
+            : !group && decode_heads_ok(pool)
+                ? launch_decode_heads(pool, layer, n, slot_ids, 1, q, k, v, a, b, conv_w, nullptr,
+                                      out, s)
+                : launch_decode_verify(pool, layer, n, slot_ids, 1, q, k, v, a, b, conv_w, nullptr,
+                                       out, s);
         return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     });
 }
@@ -346,10 +352,15 @@ gdn_status gdn_verify_step(gdn_pool* pool, int32_t layer, int32_t n, const int32
             if (st == GDN_OK) st = host_check_rings_empty(pool, layer, slot_ids, n, s);
             if (st != GDN_OK) return st;
         }
-        return launch_decode_verify(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len,
-                                    out, s) == hipSuccess
-                   ? GDN_OK
-                   : GDN_ERR_HIP;
+        // One value head per workgroup where it applies (d_k 64 or 128),
+        // else one workgroup per q/k group; bitwise equal.
+        const hipError_t e =
+            !(pool->desc.flags & GDN_GROUP_KERNEL) && decode_heads_ok(pool)
+                ? launch_decode_heads(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w,
+                                      accept_len, out, s)
+                : launch_decode_verify(pool, layer, n, slot_ids, n_tok, q, k, v, a, b, conv_w,
+                                       accept_len, out, s);
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     });
 }
 

@@ -144,6 +144,14 @@ hipError_t launch_decode_verify(const gdn_pool* pool, int32_t layer, int32_t n,
 // Low-batch decode with the rows of each head split over workgroups:
 // the split factor for n entries (1 = use the one-workgroup kernel).
 int decode_rows_split(const gdn_pool* pool, int32_t n);
+// Decode (n_tok = 1, no accept_len) and verify with one value head per
+// workgroup (d_k 64 or 128): batches above the row split.
+bool decode_heads_ok(const gdn_pool* pool);
+hipError_t launch_decode_heads(const gdn_pool* pool, int32_t layer, int32_t n,
+                               const int32_t* slot_ids, int32_t n_tok, const void* q,
+                               const void* k, const void* v, const float* a, const float* b,
+                               const float* conv_w, const int32_t* accept_len, void* out,
+                               hipStream_t stream);
 hipError_t launch_decode_rows(const gdn_pool* pool, int nrb, int32_t layer, int32_t n,
                               const int32_t* slot_ids, const void* q, const void* k, const void* v,
                               const float* a, const float* b, const float* conv_w, void* out,

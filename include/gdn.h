@@ -94,6 +94,11 @@ typedef int32_t gdn_dtype;
 
 /* flags */
 #define GDN_VALIDATE 1u /* check device index arrays on the host (synchronises) */
+/* Decode and verify always run the kernel with one workgroup per (entry,
+ * q/k group) instead of the finer splits chosen by batch size and d_k.  The
+ * results are bitwise the same; the flag exists so the kernels can be
+ * checked against each other. */
+#define GDN_GROUP_KERNEL 2u
 
 typedef struct {
     int32_t n_slots;   /* >= 1 */
@@ -106,7 +111,7 @@ typedef struct {
     gdn_dtype io_dtype; /* GDN_F32 or GDN_BF16: q, k, v, outputs and windows */
     float q_scale;     /* multiplies the normalised q; 0 -> 1/sqrt(d_k) */
     float norm_eps;    /* eps in x/sqrt(|x|^2+eps); 0 -> 1e-6 */
-    uint32_t flags;    /* GDN_VALIDATE or 0 */
+    uint32_t flags;    /* GDN_VALIDATE | GDN_GROUP_KERNEL, or 0 */
     int32_t ring_len;  /* tokens of the verify ring per slot and layer, 0..24 (0: no ring) */
 } gdn_pool_desc;
 

@@ -32,6 +32,21 @@ def test_header_declares_the_documented_calls():
         assert want in names
 
 
+def test_binding_constants_match_the_header():
+    """Every GDN_ constant of the binding has the value include/gdn.h gives."""
+    from gated_deltanet_state_layer_amd import binding as B
+    text = open(HEADER).read()
+    seen = 0
+    for name, expr in re.findall(r"^#define (GDN_\w+) (.+?)\s*(?:/\*.*)?$", text, re.M):
+        if not hasattr(B, name):
+            continue
+        expr = re.sub(r"\(size_t\)", "", expr)
+        expr = re.sub(r"(\d+)u\b", r"\1", expr)
+        assert getattr(B, name) == eval(expr, {}), name
+        seen += 1
+    assert seen >= 12
+
+
 def test_library_exports_every_declared_symbol(lib):
     from gated_deltanet_state_layer_amd import binding
     for name in declared_functions():
@@ -73,7 +88,7 @@ def test_pool_bytes_layout_with_a_verify_ring(lib):
 
 @pytest.mark.parametrize("field,value,status", [
     ("n_slots", 0, -1), ("h_v", 3, -1), ("d_k", 96, -2), ("d_v", 32, -2), ("conv_k", 0, -1), ("conv_k", 1, -2),
-    ("conv_k", 9, -2), ("io_dtype", 7, -1), ("flags", 8, -1), ("q_scale", -1.0, -1),
+    ("conv_k", 9, -2), ("io_dtype", 7, -1), ("flags", 4, -1), ("flags", 8, -1), ("q_scale", -1.0, -1),
     ("ring_len", -1, -1), ("ring_len", 25, -2),
 ])
 def test_bad_descriptor_is_rejected(lib, field, value, status):
@@ -83,6 +98,15 @@ def test_bad_descriptor_is_rejected(lib, field, value, status):
     sb, ab = ctypes.c_size_t(7), ctypes.c_size_t(7)
     assert lib.gdn_pool_bytes(ctypes.byref(d), ctypes.byref(sb), ctypes.byref(ab)) == status
     assert sb.value == 7 and ab.value == 7
+
+
+def test_known_flags_are_accepted(lib):
+    from gated_deltanet_state_layer_amd import binding as B
+    for flags in (B.GDN_VALIDATE, B.GDN_GROUP_KERNEL, B.GDN_VALIDATE | B.GDN_GROUP_KERNEL):
+        d = B.make_desc(4, 1, 2, 4, 64, 64, 4, flags=flags)
+        sb, ab = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        assert lib.gdn_pool_bytes(ctypes.byref(d), ctypes.byref(sb), ctypes.byref(ab)) == 0
+        assert (sb.value, ab.value) == B.pool_bytes(B.make_desc(4, 1, 2, 4, 64, 64, 4))
 
 
 def test_null_arguments_are_rejected_before_any_device_work(lib):

@@ -5,6 +5,7 @@ invariance, verify == sequential decode)."""
 import numpy as np
 import pytest
 
+import gated_deltanet_state_layer_amd as G
 import gdn_synth as syn
 from gpu_util import (check_f32, check_out, dev, host, load_slots, make_pool, oracle_pool, say,
                       scramble_pool, tokens_to_dev)
@@ -116,8 +117,9 @@ def test_batched_decode_is_bitwise_batch_invariant():
 def test_row_split_decode_is_bitwise_one_workgroup_decode(h_k, h_v, d, io, n):
     """Few entries: decode spreads each head's rows over several workgroups
     (the q/k window rolled by the last of them).  Three consecutive steps,
-    with a padding entry, equal the one-workgroup kernel (verify with one
-    token, accept_len 1) bitwise, and every roll counter is back to zero."""
+    with a padding entry, equal the one-workgroup-per-group kernel (a pool
+    with GDN_GROUP_KERNEL; verify with one token, accept_len 1) bitwise, and
+    every roll counter is back to zero."""
     s = syn.Shapes(h_k, h_v, d, d, 4)
     say(f"row-split decode: {s} io={io} n={n}")
     rng = np.random.default_rng(300 + n + d)
@@ -128,7 +130,7 @@ def test_row_split_decode_is_bitwise_one_workgroup_decode(h_k, h_v, d, io, n):
     contents = syn.draw_pool_contents(55, ids_np, s, io)
     pa = make_pool(s, n_slots, io)
     load_slots(pa, contents)
-    pb = make_pool(s, n_slots, io)
+    pb = make_pool(s, n_slots, io, flags=G.GDN_GROUP_KERNEL)
     load_slots(pb, contents)
     ids = dev(ids_pad, torch.int32)
     one = dev(np.ones(n + 1, np.int32), torch.int32)
@@ -143,6 +145,58 @@ def test_row_split_decode_is_bitwise_one_workgroup_decode(h_k, h_v, d, io, n):
         assert torch.isnan(oa[n].float()).all(), "padding entry's output was written"
     assert torch.equal(pa.state, pb.state) and torch.equal(pa.window, pb.window)
     assert pa.error() == 0
+    win_bytes = pa.window.numel() * pa.window.element_size()
+    off = (win_bytes + 255) // 256 * 256 + 256
+    ctr = pa._aux_buf[off:off + n_slots * h_k * 4].view(torch.int32)
+    assert not ctr.any(), "a roll counter is not back to zero"
+
+
+@pytest.mark.parametrize("h_k,h_v,d,io,n", [(16, 32, 128, "bf16", 64), (16, 32, 128, "f32", 40),
+                                            (4, 16, 64, "bf16", 48), (3, 6, 128, "bf16", 130)])
+def test_head_split_decode_and_verify_are_bitwise_group_kernel(h_k, h_v, d, io, n):
+    """Batches beyond the row split run one value head per workgroup (the
+    q/k window rolled by the last of a group's workgroups).  Decode steps,
+    verify of 2, 4 and 8 tokens with mixed acceptance (0 and n_tok
+    included), and a commit-only verify (no outputs) equal the
+    one-workgroup-per-group kernel bitwise; every roll counter ends at zero."""
+    s = syn.Shapes(h_k, h_v, d, d, 4)
+    say(f"head-split decode/verify: {s} io={io} n={n}")
+    rng = np.random.default_rng(500 + n + d)
+    n_slots = n + 9
+    ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
+    ids_pad = np.concatenate([ids_np[:n // 2], [-1], ids_np[n // 2:]]).astype(np.int32)
+    w = dev(syn.draw_conv_weights(rng, s))
+    contents = syn.draw_pool_contents(66, ids_np, s, io)
+    pa = make_pool(s, n_slots, io)
+    pb = make_pool(s, n_slots, io, flags=G.GDN_GROUP_KERNEL)
+    for p in (pa, pb):
+        scramble_pool(p, 3)
+        load_slots(p, contents)
+    ids = dev(ids_pad, torch.int32)
+    m = len(ids_pad)
+    for step in range(2):
+        td = tokens_to_dev(syn.draw_tokens(rng, s, (m,), io), io)
+        oa, ob = _decode(pa, 0, ids, td, w, io), _decode(pb, 0, ids, td, w, io)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.nan_to_num(oa, nan=7.0), torch.nan_to_num(ob, nan=7.0)), \
+            f"decode {step}"
+        assert torch.isnan(oa[n // 2].float()).all(), "padding entry's output was written"
+    for n_tok in (2, 4, 8):
+        td = tokens_to_dev(syn.draw_tokens(rng, s, (m, n_tok), io), io)
+        acc = dev((np.arange(m) * 3 % (n_tok + 1)).astype(np.int32), torch.int32)
+        oa, ob = _verify(pa, 0, ids, n_tok, td, w, acc), _verify(pb, 0, ids, n_tok, td, w, acc)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.nan_to_num(oa, nan=7.0), torch.nan_to_num(ob, nan=7.0)), \
+            f"verify n_tok={n_tok}"
+        assert torch.equal(pa.state, pb.state) and torch.equal(pa.window, pb.window), \
+            f"verify n_tok={n_tok}: slots differ"
+    td = tokens_to_dev(syn.draw_tokens(rng, s, (m, 4), io), io)
+    acc = dev((np.arange(m) % 5).astype(np.int32), torch.int32)
+    for p in (pa, pb):
+        p.verify(0, ids, 4, td["q"], td["k"], td["v"], td["a"], td["b"], w, acc, None)
+    torch.cuda.synchronize()
+    assert torch.equal(pa.state, pb.state) and torch.equal(pa.window, pb.window), "commit-only"
+    assert pa.error() == 0 and pb.error() == 0
     win_bytes = pa.window.numel() * pa.window.element_size()
     off = (win_bytes + 255) // 256 * 256 + 256
     ctr = pa._aux_buf[off:off + n_slots * h_k * 4].view(torch.int32)
