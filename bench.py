@@ -38,8 +38,10 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 # (profiles/decode_hbm_traffic.txt).  Valid only for the kernel source they
 # were taken on: DECODE_SRC_SHA256 is checked at run time and the traffic is
 # reported as null when the source has changed since.
-DECODE_TRAFFIC = None
-DECODE_SRC_SHA256 = None
+DECODE_TRAFFIC = {"fetch_kib": 68900.93, "write_kib": 134753.09,
+                  "copy_fetch_scale": 536870912 / (262155.93 * 1024),
+                  "copy_write_scale": 536870912 / (524288.0 * 1024)}
+DECODE_SRC_SHA256 = "e5a23a53c65d1cf4245f064aad40c171f2ead96029a3935eab7040e4be21e843"
 
 
 # Executed bf16 MFMA flops of the prefill kernels per token, from rocprofv3
@@ -50,7 +52,7 @@ DECODE_SRC_SHA256 = None
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
 # (profiles/prefill_mfma_counters.txt; profiles/prefill_hbm_traffic.txt has the bytes)
-PREFILL_SRC_SHA256 = "370a22a57d504a00f7e611caa085d9527c22a8e9707fd2e0fec375d166ceaa32"
+PREFILL_SRC_SHA256 = "9bd34199d79c862913b65d300cb425b28d2280b9d6bcf26af0843b3c5322631d"
 
 
 def prefill_exec_flop_per_token(case):
