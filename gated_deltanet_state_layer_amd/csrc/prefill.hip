@@ -31,6 +31,7 @@
 // order, so the scan's serial loop only splits what it produces itself; the
 // transposed K^ of the state update is read from LDS with the gfx950
 // transposing load instead of being stored twice.
+#include <algorithm>
 #include <mutex>
 
 #include "gdn_common.h"
@@ -271,30 +272,37 @@ template <> struct Vec<float> {
 
 // grid (max_chunks, h_k), 256 threads; with fused_n_seq > 0 (at most 64
 // sequences) each workgroup finds its chunk from cu_seqlens itself, else it
-// reads the prep kernel's chunk record.  Dynamic LDS: the chunk's raw q|k rows
-// (conv_k-1 rows of left context, then CP tokens), overwritten in place by
-// the conv+SiLU outputs and normalised; later reused for A, T and P.
-// KC > 0: conv taps fixed at compile time (must equal conv_k); 0: runtime.
-template <int D, int CP, int KC, typename T>
-__global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
+// reads the prep kernel's chunk record.  The q|k channels of the group are
+// staged in NPASS passes (1: all 2D at once, the shortest chain for grids of
+// one round; 2: q, then k, in half the LDS, so that three workgroups fit on
+// a CU).  KC > 0: conv taps fixed at compile time (must equal conv_k); 0:
+// runtime.
+template <int D, int CP, int KC, int NPASS, typename T>
+__global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ q,
     const T* __restrict__ k, const float* __restrict__ a, const float* __restrict__ b,
     const float* __restrict__ conv_w, Ckpt ck, int fused_n_seq, int total, int max_chunks) {
-    constexpr int LD = 2 * D + 4;      // row of the staged q|k lines (floats)
+    static_assert(NPASS == 1 || NPASS == 2, "staging passes");
+    constexpr int CW = 2 * D / NPASS;  // q|k channels staged per pass
+    constexpr int LD = CW + 4;         // row of the staged lines (floats)
     constexpr int LT = CP + 4;         // padded row of A, T, P (16-byte aligned)
     constexpr int NT = CP / 16;        // token tiles
     constexpr int NKS = D / 32;        // k-steps over d_k
     constexpr int NKC = CP / 32;       // k-steps over tokens
     constexpr int NQK = 2 * NT * NKS, NTP = 2 * NT * NKC;
     constexpr int VN = Vec<T>::N;
+    // Dynamic LDS, reused phase by phase (factor_lds_bytes):
+    //   per pass:  raw rows [K-1+CP][LD] of its channels, row r <-> position
+    //              t0-(K-1)+r, overwritten in place by the conv+SiLU outputs
+    //              (row t) and normalised;
+    //   then       the K^ fragments [NT*NKS] (B operands of KK^T, QK^T);
+    //   then       A [CP][LT] and T [CP][LT]; P goes over A once T is done.
     extern __shared__ __align__(16) float smem[];
-    float* xr = smem;                  // [K-1+CP][LD]; row r <-> position t0-(K-1)+r
-    float* xq = xr;                    // after the conv: q of token t at xq[t*LD + c]
-    float* xk = xr + D;                //                 k of token t at xk[t*LD + c]
-    float* sA = smem;                  // [CP][LT]  (after q^, k^ are consumed)
-    float* sT = sA + CP * LT;          // [CP][LT]
-    float* sP = sT + CP * LT;          // [CP][LT]
+    float* xr = smem;
+    float* sA = smem;
+    float* sT = sA + CP * LT;
+    float* sP = sA;
     constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
     constexpr int kMaxGroup = 4;                   // value heads per group kept in LDS
     // Cumulative log-decay in fp64: with a -> 0 (log a down to the clamp)
@@ -395,34 +403,49 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
         ab_b = b[tok * P.h_v + g * G + ab_hl];
     }
 
-    // ---- stage the raw q|k rows with 16-byte loads: window rows before the
-    // sequence start, zeros past the chunk's valid tokens.  Every load of a
-    // thread is issued before the first is used (source pointer selected,
-    // position clamped into the chunk), so the staging costs one round trip.
+    // ---- per pass: stage the raw rows, conv + SiLU in place, normalise, and
+    // split the wave's token tile into MFMA fragments.  Channel c of pass p
+    // is q|k channel p*CW + c (q below D).  Wave w builds the fragments of
+    // token tile w, so the A operands of KK^T and QK^T stay in its
+    // registers; the K^ fragments also go to LDS as the B operands of every
+    // tile row.
+    Frag fq[NKS], fk[NKS];
+    // q|k channel x of the group -> its conv/window channel
+    const auto conv_ch = [&](int x) { return x < D ? g * D + x : P.h_k * D + g * D + (x - D); };
+    // Raw rows with 16-byte loads, every pass's issued here, before the
+    // first is used (source pointer selected, position clamped into the
+    // chunk), so the staging costs one round trip: window rows before the
+    // sequence start, zeros past the chunk's valid tokens.
+    const int nrow = K - 1 + CP;
+    constexpr int vpr = CW / VN;
+    constexpr int NST = ((KM - 1 + CP) * vpr + kThreads - 1) / kThreads;
+    static_assert(kThreads % vpr == 0, "a thread keeps its column across iterations");
+    constexpr int RPI = kThreads / vpr;               // rows per iteration
+    uint4 raw[NPASS][NST];
     {
-        const int nrow = K - 1 + CP;
-        constexpr int vpr = 2 * D / VN;
-        constexpr int NST = ((KM - 1 + CP) * vpr + kThreads - 1) / kThreads;
-        static_assert(kThreads % vpr == 0, "a thread keeps its column across iterations");
-        constexpr int RPI = kThreads / vpr;               // rows per iteration
         const int cv0 = (tid % vpr) * VN, r0 = tid / vpr;
-        const bool isk0 = cv0 >= D;
-        const int cc0 = isk0 ? cv0 - D : cv0;
         const int64_t tstride = (int64_t)P.h_k * D;       // elements between tokens
-        const T* tok_base = (isk0 ? k : q) + t0 * tstride + g * D + cc0;   // token t0 of the column
-        const T* win_base = win + (isk0 ? P.h_k * D : 0) + g * D + cc0;
-        uint4 raw[NST];
 #pragma unroll
-        for (int it = 0; it < NST; ++it) {
-            const int r = min(r0 + it * RPI, nrow - 1);
-            const int dt = min(r - (K - 1), L - 1);       // token offset from t0, clamped into the chunk
-            const int64_t p = t0 + dt;
-            const T* src = p >= s0 ? tok_base + (int64_t)dt * tstride
-                                   : win_base + (int64_t)(K - 1 + (int)(p - s0)) * C;
-            raw[it] = *reinterpret_cast<const uint4*>(src);
+        for (int pass = 0; pass < NPASS; ++pass) {
+            const int x0 = pass * CW + cv0;               // q|k channel of the column
+            const T* tok_base = (x0 < D ? q + x0 : k + (x0 - D)) + t0 * tstride + g * D;
+            const T* win_base = win + conv_ch(x0);
+#pragma unroll
+            for (int it = 0; it < NST; ++it) {
+                const int r = min(r0 + it * RPI, nrow - 1);
+                const int dt = min(r - (K - 1), L - 1);       // token offset from t0, clamped into the chunk
+                const int64_t p = t0 + dt;
+                const T* ps = p >= s0 ? tok_base + (int64_t)dt * tstride
+                                      : win_base + (int64_t)(K - 1 + (int)(p - s0)) * C;
+                raw[pass][it] = *reinterpret_cast<const uint4*>(ps);
+            }
         }
+    }
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int xb = pass * CW;   // first q|k channel of the pass
         // a/b arrive with the first staging loads; consume them only now
-        if (tid < G * CP) {
+        if (pass == 0 && tid < G * CP) {
             s_la[ab_hl][ab_t] = ab_t < L ? fmaxf(__logf(ab_a), kLogDecayMin) : 0.f;
             s_bb[ab_hl][ab_t] = ab_t < L ? ab_b : 0.f;
         }
@@ -434,130 +457,138 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
                 const bool valid = t0 - (K - 1) + r < t0 + L;
                 float x[VN];
 #pragma unroll
-                for (int i = 0; i < VN; ++i) x[i] = valid ? Vec<T>::at(raw[it], i) : 0.f;
+                for (int i = 0; i < VN; ++i) x[i] = valid ? Vec<T>::at(raw[pass][it], i) : 0.f;
 #pragma unroll
                 for (int i = 0; i < VN; i += 4)
                     *reinterpret_cast<float4*>(xr + r * LD + cv + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
             }
         }
-    }
-    __syncthreads();
-    // The sequence's first chunk owns the window of these channels: store the
-    // last conv_k-1 raw inputs of the sequence (old window rows come from LDS).
-    if (cpos == 0) {
-        for (int e = tid; e < (K - 1) * 2 * D; e += kThreads) {
-            const int m = e / (2 * D), c = e % (2 * D);
-            const bool isk = c >= D;
-            const int cc = isk ? c - D : c;
-            const int64_t p = s0 + len - (K - 1) + m;
-            const float x = p >= s0 ? Io<T>::load(isk ? k : q, (p * P.h_k + g) * D + cc)
-                                    : xr[(int)(K - 1 + (p - s0)) * LD + c];
-            Io<T>::store(win, (int64_t)m * C + (isk ? P.h_k * D : 0) + g * D + cc, x);
+        __syncthreads();
+        // The sequence's first chunk owns the window of these channels: store
+        // the last conv_k-1 raw inputs of the sequence (old window rows come
+        // from LDS).
+        if (cpos == 0) {
+            for (int e = tid; e < (K - 1) * CW; e += kThreads) {
+                const int m = e / CW, c = e % CW, x = xb + c;
+                const int64_t pp = s0 + len - (K - 1) + m;
+                const float v = pp >= s0 ? Io<T>::load(x < D ? q : k, (pp * P.h_k + g) * D + (x < D ? x : x - D))
+                                         : xr[(int)(K - 1 + (pp - s0)) * LD + c];
+                Io<T>::store(win, (int64_t)m * C + conv_ch(x), v);
+            }
+        }
+        // A checkpoint after this chunk (full, ending on a multiple of the
+        // checkpoint interval) holds these channels' last conv_k-1 raw rows.
+        if (ck.every_chunks > 0 && L == chunk && (cpos + 1) % ck.every_chunks == 0) {
+            const int m = (cpos + 1) / ck.every_chunks - 1;
+            const int cs = m < ck.off[j + 1] - ck.off[j] ? ck.slots[ck.off[j] + m] : -1;
+            if (cs >= 0 && cs < P.n_slots) {
+                T* cwin = reinterpret_cast<T*>(P.window) + ((int64_t)cs * P.n_layers + layer) * (int64_t)(K - 1) * C;
+                for (int e = tid; e < (K - 1) * CW; e += kThreads) {
+                    const int r = e / CW, c = e % CW;
+                    Io<T>::store(cwin, (int64_t)r * C + conv_ch(xb + c), xr[(chunk + r) * LD + c]);
+                }
+            }
+        }
+        // ---- conv + SiLU: one channel and TPH consecutive tokens per thread.
+        // y_t lands in row t, which no later token of the channel reads; the
+        // K-1 rows past the thread's slice are the next slice's first outputs,
+        // so they are read into registers before a barrier.
+        {
+            constexpr int TPH = CP / (kThreads / CW);
+            static_assert(kThreads % CW == 0 && TPH >= 1, "token slices of the conv");
+            const int c = tid % CW, t0c = (tid / CW) * TPH;
+            float w[KM], line[KM - 1], tail[KM - 1];
+#pragma unroll
+            for (int m = 0; m < KM; ++m) w[m] = m < K ? conv_w[(int64_t)conv_ch(xb + c) * K + m] : 0.f;
+#pragma unroll
+            for (int m = 0; m < KM - 1; ++m) {
+                line[m] = m < K - 1 ? xr[(t0c + m) * LD + c] : 0.f;
+                tail[m] = m < K - 1 && TPH < CP ? xr[(t0c + TPH + m) * LD + c] : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < TPH; ++i) {
+                // raw row t0c+i+K-1: in LDS (this slice's, or with one slice
+                // every row), or one of the saved tail rows
+                float x = 0.f;
+                if (i + K - 1 < TPH || TPH == CP) {
+                    x = xr[(t0c + i + K - 1) * LD + c];
+                } else {
+#pragma unroll
+                    for (int m = 0; m < KM - 1; ++m)
+                        if (i + K - 1 - TPH == m) x = tail[m];
+                }
+                float z = 0.f;
+#pragma unroll
+                for (int m = 0; m < KM - 1; ++m)
+                    if (m < K - 1) z = fmaf(w[m], line[m], z);
+                z = fmaf(w[K - 1], x, z);
+                xr[(t0c + i) * LD + c] = t0c + i < L ? silu(z) : 0.f;
+#pragma unroll
+                for (int m = 0; m < KM - 1; ++m)
+                    line[m] = (m == K - 2) ? x : (m < K - 2 ? line[m + 1] : line[m]);
+            }
         }
         __syncthreads();
-    }
-    // A checkpoint after this chunk (full, ending on a multiple of the
-    // checkpoint interval) holds these channels' last conv_k-1 raw rows.
-    if (ck.every_chunks > 0 && L == chunk && (cpos + 1) % ck.every_chunks == 0) {
-        const int m = (cpos + 1) / ck.every_chunks - 1;
-        const int cs = m < ck.off[j + 1] - ck.off[j] ? ck.slots[ck.off[j] + m] : -1;
-        if (cs >= 0 && cs < P.n_slots) {
-            T* cwin = reinterpret_cast<T*>(P.window) + ((int64_t)cs * P.n_layers + layer) * (int64_t)(K - 1) * C;
-            for (int e = tid; e < (K - 1) * 2 * D; e += kThreads) {
-                const int r = e / (2 * D), c = e % (2 * D);
-                const int gc = c >= D ? P.h_k * D + g * D + (c - D) : g * D + c;
-                Io<T>::store(cwin, (int64_t)r * C + gc, xr[(chunk + r) * LD + c]);
+        // ---- normalisation of each of q, k (h = 0, 1) staged in this pass:
+        // a quad of lanes per token (lane part p sums channels
+        // [p*D/4, (p+1)*D/4) of it, the quad adds up), then the same lanes
+        // scale their channels in place.
+        {
+            const int t = wave * 16 + (lane >> 2), part = lane & 3;
+            constexpr int CPL = D / 4;
+            if (t < CP) {   // uniform per wave
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (h * D < xb || h * D >= xb + CW) continue;   // not in this pass
+                    float* row = xr + t * LD + (h * D - xb) + part * CPL;
+                    float sq = 0.f;
+#pragma unroll
+                    for (int jj = 0; jj < CPL; jj += 4) {
+                        const float4 x = *reinterpret_cast<const float4*>(row + jj);
+                        sq = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, sq))));
+                    }
+                    sq = group_sum<4>(sq);
+                    const float rs = (h ? 1.0f : P.q_scale) / sqrtf(sq + P.eps);
+#pragma unroll
+                    for (int jj = 0; jj < CPL; jj += 4) {
+                        float4 x = *reinterpret_cast<const float4*>(row + jj);
+                        x.x *= rs; x.y *= rs; x.z *= rs; x.w *= rs;
+                        *reinterpret_cast<float4*>(row + jj) = x;
+                    }
+                }
             }
         }
-        __syncthreads();   // the conv below overwrites staged rows
-    }
-    // ---- conv + SiLU in place, one channel per thread: y_t lands in row t,
-    // which no later token of the channel reads.
-    for (int c = tid; c < 2 * D; c += kThreads) {
-        const int gc = (c >= D ? P.h_k * D + g * D + (c - D) : g * D + c);
-        float w[KM], line[KM - 1];
-#pragma unroll
-        for (int m = 0; m < KM; ++m) w[m] = m < K ? conv_w[(int64_t)gc * K + m] : 0.f;
-#pragma unroll
-        for (int m = 0; m < KM - 1; ++m) line[m] = m < K - 1 ? xr[m * LD + c] : 0.f;
-#pragma unroll 16
-        for (int t = 0; t < CP; ++t) {
-            const float x = xr[(t + K - 1) * LD + c];
-            float z = 0.f;
-#pragma unroll
-            for (int m = 0; m < KM - 1; ++m)
-                if (m < K - 1) z = fmaf(w[m], line[m], z);
-            z = fmaf(w[K - 1], x, z);
-            xr[t * LD + c] = t < L ? silu(z) : 0.f;
-#pragma unroll
-            for (int m = 0; m < KM - 1; ++m)
-                line[m] = (m == K - 2) ? x : (m < K - 2 ? line[m + 1] : line[m]);
-        }
-    }
-    __syncthreads();
-
-    // ---- q/k normalisation: a quad of lanes per token (lane part p sums
-    // channels [p*D/4, (p+1)*D/4) of q and of k, the quad adds up), then the
-    // same lanes scale their channels in place.
-    {
-        const int t = wave * 16 + (lane >> 2), part = lane & 3;
-        constexpr int CPL = D / 4;
-        if (t < CP) {   // uniform per wave
-            float* rq_row = xq + t * LD + part * CPL;
-            float* rk_row = xk + t * LD + part * CPL;
-            float sq = 0.f, sk = 0.f;
-#pragma unroll
-            for (int j = 0; j < CPL; j += 4) {
-                const float4 x = *reinterpret_cast<const float4*>(rq_row + j);
-                const float4 y = *reinterpret_cast<const float4*>(rk_row + j);
-                sq = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, sq))));
-                sk = fmaf(y.x, y.x, fmaf(y.y, y.y, fmaf(y.z, y.z, fmaf(y.w, y.w, sk))));
-            }
-            sq = group_sum<4>(sq);
-            sk = group_sum<4>(sk);
-            const float rq = P.q_scale / sqrtf(sq + P.eps), rk = 1.0f / sqrtf(sk + P.eps);
-#pragma unroll
-            for (int j = 0; j < CPL; j += 4) {
-                float4 x = *reinterpret_cast<const float4*>(rq_row + j);
-                float4 y = *reinterpret_cast<const float4*>(rk_row + j);
-                x.x *= rq; x.y *= rq; x.z *= rq; x.w *= rq;
-                y.x *= rk; y.y *= rk; y.z *= rk; y.w *= rk;
-                *reinterpret_cast<float4*>(rq_row + j) = x;
-                *reinterpret_cast<float4*>(rk_row + j) = y;
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- q^/k^ fragments for the scan.  [Q;K] S0^T operands: fragment
-    // (qk, tile, ks), lane (m, q): token tile*16+m, d_k {32ks+4q+i, 32ks+16+4q+i}
-    // (the d_k order in which the scan holds its state).  The scan builds the
-    // state update's K^T operand from these itself (LDS transpose reads).
-    // Each value is split once: the fragments go to the workspace and, once
-    // every wave has read its rows, to LDS over those rows for KK^T and QK^T.
-    bf16x8* const lfr = reinterpret_cast<bf16x8*>(smem);   // [NQK] fragments
-    static_assert(NQK % (kThreads / 64) == 0, "fragments per wave");
-    static_assert((size_t)NQK * kFragVecs * 16 <= (size_t)(kMaxConvK - 1 + CP) * LD * sizeof(float),
-                  "fragments fit in the staging region (factor_lds_bytes)");
-    {
-        constexpr int FPW = NQK / (kThreads / 64);
-        Frag fr[FPW];
-        bf16x8* gqk = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
-#pragma unroll
-        for (int i = 0; i < FPW; ++i) {
-            const int f = wave + i * (kThreads / 64);
-            const int qk = f / (NT * NKS), tile = (f / NKS) % NT, ks = f % NKS;
-            const float* row = (qk ? xk : xq) + (tile * 16 + m16) * LD + ks * 32 + q4 * 4;
-            float x[8];
-            ld4x2(x, row, row + 16);
-            fr[i] = split8(x);
-            store_frag(gqk, f, lane, fr[i]);
-        }
-        __syncthreads();   // every wave has read its q^/k^ rows
-#pragma unroll
-        for (int i = 0; i < FPW; ++i) store_frag(lfr, wave + i * (kThreads / 64), lane, fr[i]);
         __syncthreads();
+        // ---- fragments (qk, tile = wave, ks), lane (m, q): token tile*16+m,
+        // d_k {32ks+4q+i, 32ks+16+4q+i} (the d_k order in which the scan holds
+        // its state); each value is split once.  The scan builds the state
+        // update's K^T operand from these itself (LDS transpose reads).
+        if (wave < NT) {
+            bf16x8* gqk = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (h * D < xb || h * D >= xb + CW) continue;   // not in this pass
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const float* row = xr + (wave * 16 + m16) * LD + (h * D - xb) + ks * 32 + q4 * 4;
+                    float x[8];
+                    ld4x2(x, row, row + 16);
+                    const Frag f = split8(x);
+                    store_frag(gqk, (h * NT + wave) * NKS + ks, lane, f);
+                    if (h) fk[ks] = f;
+                    else fq[ks] = f;
+                }
+            }
+        }
+        __syncthreads();   // the next pass (or the fragments below) overwrite the rows
     }
+    bf16x8* const lfr = reinterpret_cast<bf16x8*>(smem);   // [NT*NKS] K^ fragments
+    if (wave < NT) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) store_frag(lfr, wave * NKS + ks, lane, fk[ks]);
+    }
+    __syncthreads();
 
     // ---- KK^T and QK^T lower-triangular tiles: wave w takes tile row w.  A
     // and B are the same split fragments (one d_k order on both sides).
@@ -571,19 +602,17 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
     if (ti < NT) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const Frag ak = load_frag(lfr, (NT + ti) * NKS + ks, lane);
-            const Frag aq = load_frag(lfr, ti * NKS + ks, lane);
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) {
                 if (jt <= ti) {
-                    const Frag bk = load_frag(lfr, (NT + jt) * NKS + ks, lane);
-                    kk[jt] = mma3(kk[jt], ak, bk);
-                    qk[jt] = mma3(qk[jt], aq, bk);
+                    const Frag bk = load_frag(lfr, jt * NKS + ks, lane);
+                    kk[jt] = mma3(kk[jt], fk[ks], bk);
+                    qk[jt] = mma3(qk[jt], fq[ks], bk);
                 }
             }
         }
     }
-    __syncthreads();   // q^, k^ LDS region is reused below
+    __syncthreads();   // the fragment region is reused below
 
     // ---- per value head of the group: decay, A, T = (I+A)^-1, T', P.
     for (int hl = 0; hl < G; ++hl) {
@@ -603,9 +632,10 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             }
         }
         __syncthreads();
-        // A (strictly lower) and P (lower incl. diagonal) into LDS.  The lane's
-        // four rows share their g and b (one vector read each); blocks above
-        // the diagonal are plain zeros.
+        // A (strictly lower) into LDS, P (lower incl. diagonal) into
+        // registers until T is done.  The lane's four rows share their g and b
+        // (one vector read each); blocks above the diagonal are plain zeros.
+        float pvr[NT][4];
         if (ti < NT) {
             const double2 ga = *reinterpret_cast<const double2*>(s_g + ti * 16 + q4 * 4);
             const double2 gb = *reinterpret_cast<const double2*>(s_g + ti * 16 + q4 * 4 + 2);
@@ -626,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
                         pv = s <= t ? qk[jt][r] * dec : 0.f;
                     }
                     sA[t * LT + s] = av;
-                    sP[t * LT + s] = pv;
+                    pvr[jt][r] = pv;
                 }
             }
         }
@@ -710,6 +740,14 @@ __global__ __launch_bounds__(kThreads) void prefill_factor_kernel(
             }
             __syncthreads();
         }
+        // P over A (A and the block products kept in its upper part are done).
+        if (ti < NT) {
+#pragma unroll
+            for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sP[(ti * 16 + q4 * 4 + r) * LT + jt * 16 + m16] = pvr[jt][r];
+        }
+        __syncthreads();
         // T' = T diag(b) and P fragments: (tp, tile, kc), lane (m, q): row
         // tile*16+m, cols 32kc+8q+e.  Both are lower triangular: fragments with
         // kc > tile/2 are all zero and are not written (the scan never fetches
@@ -1238,11 +1276,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     }
 }
 
-template <int D, int CP>
+// Factor grids up to this many workgroups run in one round at two per CU.
+constexpr int64_t kFactorOneRoundWgs = 512;
+
+// Dynamic LDS of the factor kernel: the largest of its phases (staged rows
+// of a pass, the K^ fragments, A and T).
+template <int D, int CP, int KC, int NPASS>
 size_t factor_lds_bytes() {
-    const size_t a = (size_t)(kMaxConvK - 1 + CP) * (2 * D + 4) * sizeof(float);
-    const size_t b = (size_t)3 * CP * (CP + 4) * sizeof(float);
-    return a > b ? a : b;
+    constexpr int KM = KC > 0 ? KC : kMaxConvK;
+    const size_t a = (size_t)(KM - 1 + CP) * (2 * D / NPASS + 4) * sizeof(float);
+    const size_t f = (size_t)(CP / 16) * (D / 32) * kFragVecs * 16;
+    const size_t b = (size_t)2 * CP * (CP + 4) * sizeof(float);
+    return std::max(a, std::max(f, b));
 }
 
 template <int D, int CP, int KC, typename T>
@@ -1251,10 +1296,19 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
                       const void* q, const void* k, const void* v, const float* a, const float* b,
                       const float* conv_w, void* out, Ckpt ck, hipStream_t stream) {
     const PoolView& P = pool->view;
-    static std::atomic<uint64_t> factor_lds{0}, scan_lds{0};
-    const size_t lf = factor_lds_bytes<D, CP>();
+    static std::atomic<uint64_t> factor1_lds{0}, factor2_lds{0}, scan_lds{0};
+    // Factor grids that run in one round (two workgroups per CU on the 256
+    // CUs) stage q|k in one pass (the shorter chain per workgroup); larger
+    // grids in two, for three workgroups per CU.  Measured at chunk 64 on a
+    // Qwen3-Next layer: 16 calls of 512 tokens 866 -> (one pass) us, one
+    // 8192-token call 430 -> 416 us and the 16-sequence varlen batch
+    // 1537 -> 1442 us with two passes.
+    const bool one_pass = (int64_t)mc * P.h_k <= kFactorOneRoundWgs;
+    const size_t lf = one_pass ? factor_lds_bytes<D, CP, KC, 1>() : factor_lds_bytes<D, CP, KC, 2>();
     const size_t ls = ScanLds<D, CP>::bytes;
-    hipError_t e = allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, T>, lf, &factor_lds);
+    hipError_t e = one_pass
+        ? allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, 1, T>, lf, &factor1_lds)
+        : allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, 2, T>, lf, &factor2_lds);
     if (e != hipSuccess) return e;
     e = allow_dynamic_lds(&prefill_scan_kernel<D, CP, KC, T>, ls, &scan_lds);
     if (e != hipSuccess) return e;
@@ -1266,9 +1320,14 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
-                       stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
-                       static_cast<const T*>(k), a, b, conv_w, ck, fused, total, mc);
+    if (one_pass)
+        hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, 1, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
+                           stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
+                           static_cast<const T*>(k), a, b, conv_w, ck, fused, total, mc);
+    else
+        hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, 2, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
+                           stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
+                           static_cast<const T*>(k), a, b, conv_w, ck, fused, total, mc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<D, CP, KC, T>), dim3((D / kRows) * P.h_v * n_seq),

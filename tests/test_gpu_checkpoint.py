@@ -69,14 +69,18 @@ def _oracle_checkpoints(s, contents, ids_np, cu, tok, w, every):
     return out, snaps, op
 
 
-@pytest.mark.parametrize("d,chunk,every,io", [(64, 64, 128, "bf16"), (32, 16, 48, "f32")])
-def test_prefill_checkpoints_vs_oracle(d, chunk, every, io):
+@pytest.mark.parametrize("h_k,h_v,d,chunk,every,io", [(1, 2, 64, 64, 128, "bf16"),
+                                                      (1, 2, 32, 16, 48, "f32"),
+                                                      (16, 32, 32, 16, 160, "f32")])
+def test_prefill_checkpoints_vs_oracle(h_k, h_v, d, chunk, every, io):
     """Two sequences (one continuing from a non-zero slot), checkpoints every
     `every` tokens into listed slots: each checkpoint slot holds the state
     and window after that many tokens; a checkpoint row past the sequence's
-    end and a negative checkpoint slot leave their slots untouched."""
-    s = syn.Shapes(1, 2, d, d, 4)
-    say(f"checkpoints: d={d} chunk={chunk} every={every} io={io}")
+    end and a negative checkpoint slot leave their slots untouched.  The last
+    case has more than 512 (chunk, q/k head) work items, so the factor stages
+    q and k in two passes."""
+    s = syn.Shapes(h_k, h_v, d, d, 4)
+    say(f"checkpoints: {s} chunk={chunk} every={every} io={io}")
     rng = np.random.default_rng(500 + d)
     lens = [4 * every + 8, 2 * every + every // 2]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
