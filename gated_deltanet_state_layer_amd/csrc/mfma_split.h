@@ -68,6 +68,21 @@ __device__ __forceinline__ void mma3_n(f32x4* acc, const Frag* a, const Frag* b)
     for (int j = 0; j < N; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j].hi, b[j].hi, acc[j], 0, 0, 0);
 }
 
+// Fragment buffers: [fragment][hi | lo][64 lanes] of 16-byte vectors, 2 KiB
+// per fragment, so a wave reads or writes one half in one coalesced 1 KiB.
+constexpr int kFragVecs = 128;   // bf16x8 per fragment
+
+__device__ __forceinline__ void store_frag(bf16x8* base, int f, int lane, const Frag& x) {
+    base[f * kFragVecs + lane] = x.hi;
+    base[f * kFragVecs + 64 + lane] = x.lo;
+}
+__device__ __forceinline__ Frag load_frag(const bf16x8* base, int f, int lane) {
+    Frag x;
+    x.hi = base[f * kFragVecs + lane];
+    x.lo = base[f * kFragVecs + 64 + lane];
+    return x;
+}
+
 // Eight floats from two 16-byte aligned groups of four.
 __device__ __forceinline__ void ld4x2(float* dst, const float* lo, const float* hi) {
     const float4 x0 = *reinterpret_cast<const float4*>(lo);

@@ -46,20 +46,6 @@ constexpr float kLogDecayMin = -87.f;
 
 // ------------------------------------------------------------ MFMA helpers
 
-// Fragment buffers: [fragment][hi | lo][64 lanes] of 16-byte vectors, 2 KiB
-// per fragment, so a wave reads or writes one half in one coalesced 1 KiB.
-constexpr int kFragVecs = 128;   // bf16x8 per fragment
-
-__device__ __forceinline__ void store_frag(bf16x8* base, int f, int lane, const Frag& x) {
-    base[f * kFragVecs + lane] = x.hi;
-    base[f * kFragVecs + 64 + lane] = x.lo;
-}
-__device__ __forceinline__ Frag load_frag(const bf16x8* base, int f, int lane) {
-    Frag x;
-    x.hi = base[f * kFragVecs + lane];
-    x.lo = base[f * kFragVecs + 64 + lane];
-    return x;
-}
 // Scatter four consecutive k values (hi and lo) into lane `dl`, elements
 // e0..e0+3, of B fragment f.
 __device__ __forceinline__ void store_frag4(bf16x8* base, int f, int dl, int e0, const float* x) {

@@ -114,8 +114,12 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
     constexpr bool VERIFY = MODE == kModeVerify, FLUSH = MODE == kModeFlush;
     constexpr int NCH = 3 * D;             // conv channels read: q, k, v of this head
     constexpr int CPT = (NCH + kThreads - 1) / kThreads;
-    __shared__ __align__(16) float kn[NTOK * KP];          // k^ rows: ring, then new tokens
-    __shared__ __align__(16) float qn[VERIFY ? 16 * KP : 4];   // q^ rows of the drafts
+    // k^ rows (ring, then new tokens) and, for a verify, the q^ rows of the
+    // drafts; a verify reads them only to split them into fragments, which
+    // then go over them (fr below)
+    __shared__ __align__(16) float kq[NTOK * KP + (VERIFY ? 16 * KP : 0)];
+    float* const kn = kq;
+    float* const qn = kq + NTOK * KP;
     __shared__ __align__(16) float vt[D * MP];             // v transposed: [d_v][token]
     __shared__ __align__(16) float mA[NTOK * MP];          // A; later A10 T00
     __shared__ __align__(16) float mT[NTOK * MP];          // T = (I+A)^-1
@@ -126,6 +130,16 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
     // only ~1e-5 of the differences that the decays are made of.
     __shared__ __align__(16) double sgd[NTOK];
     __shared__ __align__(16) float sge[NTOK];
+    // K^ (token tiles) and Q^ (verify) rows split once into MFMA fragments,
+    // fragment ks * NKT + tt: shared by the Gram blocks and X = [K; Q] S^T of
+    // every wave (lane (m, q): row 16 tt + m, d_k 32 ks + 4q.. and +16..).  A
+    // verify keeps them over its k^/q^ rows; a commit still needs its k^
+    // rows (the fold, the ring append), so it keeps them apart.
+    constexpr int NKT = NT + (VERIFY ? 1 : 0);
+    constexpr int NFR = NKS * NKT;
+    static_assert(!VERIFY || NFR * kFragVecs * 16 <= (int)sizeof(kq), "fragments fit over the rows");
+    __shared__ __align__(16) bf16x8 fr_sep[VERIFY ? 1 : NFR * kFragVecs];
+    bf16x8* const fr = VERIFY ? reinterpret_cast<bf16x8*>(kq) : fr_sep;
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -371,6 +385,24 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
             rb[(int64_t)(c + tid) * P.h_v + h] = sb[c + tid];
         }
     } else {
+        // ---- K^ / Q^ fragments, each split once for the workgroup (all rows
+        // are read before any fragment is written: they share LDS in a verify)
+        constexpr int FPW = (NFR + NWAVE - 1) / NWAVE;
+        Frag frw[FPW];
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) {
+            const int f = min(wave + i * NWAVE, NFR - 1);
+            const int ks = f / NKT, tt = f % NKT;
+            const float* row = (tt < NT ? kn + (tt * 16 + m16) * KP : qn + m16 * KP) + ks * 32 + q4 * 4;
+            float x[8];
+            ld4x2(x, row, row + 16);
+            frw[i] = split8(x);
+        }
+        if constexpr (VERIFY) __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FPW; ++i)
+            if (wave + i * NWAVE < NFR) store_frag(fr, wave + i * NWAVE, lane, frw[i]);
+        __syncthreads();
         // ---- Gram blocks on the matrix cores: KK^T (lower blocks) -> A and
         // QK^T (verify) -> P, with the decays applied on the way to LDS
         constexpr int NKK = NT * (NT + 1) / 2;
@@ -378,16 +410,11 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
         for (int job = wave; job < NJOB; job += NWAVE) {
             const bool isq = job >= NKK;
             const int ti = isq ? 0 : (job == 0 ? 0 : 1), tj = isq ? job - NKK : (job == 2 ? 1 : 0);
-            const float* arow = (isq ? qn : kn) + (ti * 16 + m16) * KP + q4 * 8;
-            const float* brow = kn + (tj * 16 + m16) * KP + q4 * 8;
+            const int fa = isq ? NT : ti, fb = tj;   // fragment tiles of the two operands
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                float x[8], y[8];
-                ld8(x, arow + ks * 32);
-                ld8(y, brow + ks * 32);
-                acc = mma3(acc, split8(x), split8(y));
-            }
+            for (int ks = 0; ks < NKS; ++ks)
+                acc = mma3(acc, load_frag(fr, ks * NKT + fa, lane), load_frag(fr, ks * NKT + fb, lane));
             const int s = tj * 16 + m16;             // column token
             const double gs = sgd[s];
 #pragma unroll
@@ -461,16 +488,12 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
         f32x4 xacc[NX];
 #pragma unroll
         for (int j = 0; j < NX; ++j) xacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        static_assert(NT + NQ == NKT, "fragment tiles of X");
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             Frag kf[NT + NQ], sf[RTW];
 #pragma unroll
-            for (int tt = 0; tt < NT + NQ; ++tt) {
-                float y[8];
-                const float* row = (tt < NT ? kn + (tt * 16 + m16) * KP : qn + m16 * KP) + ks * 32 + q4 * 4;
-                ld4x2(y, row, row + 16);
-                kf[tt] = split8(y);
-            }
+            for (int tt = 0; tt < NT + NQ; ++tt) kf[tt] = load_frag(fr, ks * NKT + tt, lane);
 #pragma unroll
             for (int i = 0; i < RTW; ++i) {
                 float x[8];
