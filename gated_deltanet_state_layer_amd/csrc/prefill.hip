@@ -1099,6 +1099,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                 fb[ks] = load_frag(s_stf, ks, lane);
                 acc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+            // the v rows of the tile, requested with the state fragments so
+            // that R waits for the MFMAs only (not another LDS round trip)
+            const float4 v4 = *reinterpret_cast<const float4*>(s_v + buf * CP * kRows + m16 * CP + tw * 16 + q4 * 4);
+            __builtin_amdgcn_sched_barrier(0);
             mma3_n<NKS>(acc, fqk[1], fb);
             // K^ rows of this token tile into LDS in natural [token][d_k]
             // order (fragment elements 0-3 are d_k 32ks+4q.., 4-7 are +16).
@@ -1119,7 +1123,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             f32x4 ak = acc[0];
 #pragma unroll
             for (int ks = 1; ks < NKS; ++ks) ak += acc[ks];
-            const float4 v4 = *reinterpret_cast<const float4*>(s_v + buf * CP * kRows + m16 * CP + tw * 16 + q4 * 4);
             const float r4[4] = {v4.x - g4.x * ak[0], v4.y - g4.y * ak[1],
                                  v4.z - g4.z * ak[2], v4.w - g4.w * ak[3]};
             store_frag4(s_rf, tw >> 1, dst_lane, dst_e0, r4);
