@@ -76,6 +76,12 @@ __device__ __forceinline__ void store_frag(bf16x8* base, int f, int lane, const 
     base[f * kFragVecs + lane] = x.hi;
     base[f * kFragVecs + 64 + lane] = x.lo;
 }
+// The same with non-temporal stores, for fragments written to global memory
+// that the writing kernel does not read again.
+__device__ __forceinline__ void store_frag_nt(bf16x8* base, int f, int lane, const Frag& x) {
+    __builtin_nontemporal_store(x.hi, base + f * kFragVecs + lane);
+    __builtin_nontemporal_store(x.lo, base + f * kFragVecs + 64 + lane);
+}
 __device__ __forceinline__ Frag load_frag(const bf16x8* base, int f, int lane) {
     Frag x;
     x.hi = base[f * kFragVecs + lane];

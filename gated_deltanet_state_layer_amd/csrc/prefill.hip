@@ -63,6 +63,62 @@ __device__ __forceinline__ void store_frag4(bf16x8* base, int f, int dl, int e0,
     *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(base + f * kFragVecs + 64 + dl) + e0) = l;
 }
 
+// ----------------------------------------------- 16x16 fp32 blocks in LDS
+
+// acc + X Z for 16x16 fp32 blocks in LDS (row stride LT floats), on one
+// wave's VALU: the lane holds row lane/4, columns 4*(lane%4)..+3.  Two
+// halves of the inner index, each loaded as a whole before its FMAs; the
+// scheduling barriers keep the next half's loads from being hoisted (about
+// 40 registers at a time).
+template <int LT>
+__device__ __forceinline__ f32x4 blk_mac(f32x4 acc, const float* X, const float* Z, int lane) {
+    const int r = lane >> 2, c4 = (lane & 3) * 4;
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 8) {
+        const float4 xa = *reinterpret_cast<const float4*>(X + r * LT + k0);
+        const float4 xb = *reinterpret_cast<const float4*>(X + r * LT + k0 + 4);
+        const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+        f32x4 z[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) z[k] = *reinterpret_cast<const f32x4*>(Z + (k0 + k) * LT + c4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += x[k] * z[k];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+}
+
+// The same for two left operands sharing Z: acc0 + X0 Z and acc1 + X1 Z.
+template <int LT>
+__device__ __forceinline__ void blk_mac2(f32x4& acc0, f32x4& acc1, const float* X0, const float* X1,
+                                         const float* Z, int lane) {
+    const int r = lane >> 2, c4 = (lane & 3) * 4;
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 8) {
+        float x0[8], x1[8];
+        ld8(x0, X0 + r * LT + k0);
+        ld8(x1, X1 + r * LT + k0);
+        f32x4 z[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) z[k] = *reinterpret_cast<const f32x4*>(Z + (k0 + k) * LT + c4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            acc0 += x0[k] * z[k];
+            acc1 += x1[k] * z[k];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Orders one wave's LDS writes before its later LDS reads of other lanes'
+// values (a wave's LDS operations complete in order; the fences keep the
+// compiler from moving accesses across).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // --------------------------------------------------------------- workspace
 
 // Fragment counts per (chunk, head): CP tokens per chunk (padded), NT = CP/16
@@ -294,13 +350,26 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
     // Cumulative log-decay in fp64: with a -> 0 (log a down to the clamp)
     // |g| reaches hundreds within a chunk, where fp32 would keep only ~1e-5
     // of the differences g_t - g_s that the decays are made of.
-    __shared__ __align__(16) double s_g[CP];
-    __shared__ __align__(16) float s_b[CP];
-    __shared__ float s_la[kMaxGroup][CP], s_bb[kMaxGroup][CP];
+    __shared__ __align__(16) double s_gg[kMaxGroup][CP];
+    __shared__ __align__(16) float s_bb[kMaxGroup][CP];
+    __shared__ float s_la[kMaxGroup][CP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
     const int ci = blockIdx.x, g = blockIdx.y;
+    // q|k channel x of the group -> its conv/window channel
+    const auto conv_ch = [&](int x) { return x < D ? g * D + x : P.h_k * D + g * D + (x - D); };
+    // The conv taps of this thread's channel in every pass, fetched first:
+    // they do not depend on the chunk.
+    float cw[NPASS][KM];
+    {
+        const int Kw = KC > 0 ? KC : P.conv_k;
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass)
+#pragma unroll
+            for (int m = 0; m < KM; ++m)
+                cw[pass][m] = m < Kw ? conv_w[(int64_t)conv_ch(pass * CW + tid % CW) * Kw + m] : 0.f;
+    }
     int j, slot, len, cpos;   // sequence, its slot and length, chunk index inside it
     int64_t s0;
     if (fused_n_seq > 0) {
@@ -396,8 +465,6 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
     // registers; the K^ fragments also go to LDS as the B operands of every
     // tile row.
     Frag fq[NKS], fk[NKS];
-    // q|k channel x of the group -> its conv/window channel
-    const auto conv_ch = [&](int x) { return x < D ? g * D + x : P.h_k * D + g * D + (x - D); };
     // Raw rows with 16-byte loads, every pass's issued here, before the
     // first is used (source pointer selected, position clamped into the
     // chunk), so the staging costs one round trip: window rows before the
@@ -483,9 +550,8 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
             constexpr int TPH = CP / (kThreads / CW);
             static_assert(kThreads % CW == 0 && TPH >= 1, "token slices of the conv");
             const int c = tid % CW, t0c = (tid / CW) * TPH;
-            float w[KM], line[KM - 1], tail[KM - 1];
-#pragma unroll
-            for (int m = 0; m < KM; ++m) w[m] = m < K ? conv_w[(int64_t)conv_ch(xb + c) * K + m] : 0.f;
+            const float* w = cw[pass];
+            float line[KM - 1], tail[KM - 1];
 #pragma unroll
             for (int m = 0; m < KM - 1; ++m) {
                 line[m] = m < K - 1 ? xr[(t0c + m) * LD + c] : 0.f;
@@ -549,7 +615,10 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         // ---- fragments (qk, tile = wave, ks), lane (m, q): token tile*16+m,
         // d_k {32ks+4q+i, 32ks+16+4q+i} (the d_k order in which the scan holds
         // its state); each value is split once.  The scan builds the state
-        // update's K^T operand from these itself (LDS transpose reads).
+        // update's K^T operand from these itself (LDS transpose reads).  The
+        // workspace is written with non-temporal stores: only the scan, a
+        // later launch, reads it, and lines left dirty in L2 would lengthen
+        // the write-back at the end of this launch.
         if (wave < NT) {
             bf16x8* gqk = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
 #pragma unroll
@@ -561,7 +630,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
                     float x[8];
                     ld4x2(x, row, row + 16);
                     const Frag f = split8(x);
-                    store_frag(gqk, (h * NT + wave) * NKS + ks, lane, f);
+                    store_frag_nt(gqk, (h * NT + wave) * NKS + ks, lane, f);
                     if (h) fk[ks] = f;
                     else fq[ks] = f;
                 }
@@ -585,6 +654,17 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         qk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int ti = wave;  // tile row
+    // Cumulative log-decay of value head hl of the group by wave hl (the
+    // first waves have the fewest tile rows below).
+    if (wave < G) {
+        double la = lane < CP ? (double)s_la[wave][lane] : 0.0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {   // inclusive prefix sum (CP <= 64)
+            const double y = __shfl_up(la, o);
+            if (lane >= o) la += y;
+        }
+        if (lane < CP) s_gg[wave][lane] = la;
+    }
     if (ti < NT) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -603,21 +683,8 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
     // ---- per value head of the group: decay, A, T = (I+A)^-1, T', P.
     for (int hl = 0; hl < G; ++hl) {
         const int hv = g * G + hl;
-        // cumulative log-decay and b for the chunk's tokens (zero past L)
-        if (wave == 0) {
-            double la = lane < CP ? (double)s_la[hl][lane] : 0.0;
-            const float bt = lane < CP ? s_bb[hl][lane] : 0.f;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {   // inclusive prefix sum (CP <= 64)
-                const double y = __shfl_up(la, o);
-                if (lane >= o) la += y;
-            }
-            if (lane < CP) {
-                s_g[lane] = la;
-                s_b[lane] = bt;
-            }
-        }
-        __syncthreads();
+        const double* s_g = s_gg[hl];   // cumulative log-decay (zero past L)
+        const float* s_b = s_bb[hl];    // b (zero past L)
         // A (strictly lower) into LDS, P (lower incl. diagonal) into
         // registers until T is done.  The lane's four rows share their g and b
         // (one vector read each); blocks above the diagonal are plain zeros.
@@ -681,48 +748,48 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
             }
         }
         __syncthreads();
-        // Off-diagonal blocks by distance: M = sum_{m=bj}^{bi-1} A_{bi,m} T_{m,bj}
-        // (kept in the zero upper block (bj, bi) of A), then T_{bi,bj} = -T_{bi,bi} M.
-        // One 1x4 strip per quad of lanes; each lane of the quad sums a quarter
-        // of the inner index, then the quad adds up (DPP).  (NT-dist)*256 lanes
-        // of work per distance: every thread runs the same number of passes.
-#pragma unroll
-        for (int dist = 1; dist < NT; ++dist) {
-            const int nsub = (NT - dist) * 256;
-            for (int e = tid; e < nsub; e += kThreads) {
-                const int pp = e & 3, item = e >> 2;
-                const int bj = item / 64, bi = bj + dist;
-                const int r = (item % 64) / 4, c4 = (item % 4) * 4;
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < dist; ++kb) {
-                    const int mb = bj + kb;
-#pragma unroll
-                    for (int x4 = 0; x4 < 4; ++x4) {
-                        const int x = 4 * pp + x4;
-                        acc += sA[(bi * 16 + r) * LT + mb * 16 + x] *
-                               *reinterpret_cast<const f32x4*>(sT + (mb * 16 + x) * LT + bj * 16 + c4);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = group_sum<4>(acc[i]);
-                if (pp == 0) *reinterpret_cast<f32x4*>(sA + (bj * 16 + r) * LT + bi * 16 + c4) = acc;
+        // Off-diagonal blocks by block doubling: for each pair of adjacent
+        // runs of s blocks (s = 1, then 2 for four blocks), the lower-left
+        // part of T is -T_BB L_BA T_AA (L = I + A; runs A above B).  One wave
+        // per output block; the products X = L_BA T_AA that it needs go
+        // through A's upper blocks (zero, unused), each private to one wave,
+        // within the wave (no workgroup barrier between the two products).
+        {
+            const int r = lane >> 2, c4 = (lane & 3) * 4;
+            const auto blkA = [&](int bi, int bj) { return sA + bi * 16 * LT + bj * 16; };
+            const auto blkT = [&](int bi, int bj) { return sT + bi * 16 * LT + bj * 16; };
+            const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int wu = __builtin_amdgcn_readfirstlane(wave);   // wave index, known uniform
+            if (wu < NT / 2) {   // s = 1: block (2w+1, 2w)
+                const int bi = 2 * wu + 1, bj = 2 * wu;
+                float* xs = blkA(0, 1 + wu);
+                const f32x4 x = blk_mac<LT>(zero, blkA(bi, bj), blkT(bj, bj), lane);
+                *reinterpret_cast<f32x4*>(xs + r * LT + c4) = x;
+                wave_lds_sync();
+                *reinterpret_cast<f32x4*>(blkT(bi, bj) + r * LT + c4) = -blk_mac<LT>(zero, blkT(bi, bi), xs, lane);
             }
             __syncthreads();
-            for (int e = tid; e < nsub; e += kThreads) {
-                const int pp = e & 3, item = e >> 2;
-                const int bj = item / 64, bi = bj + dist;
-                const int r = (item % 64) / 4, c4 = (item % 4) * 4;
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int x4 = 0; x4 < 4; ++x4) {
-                    const int x = 4 * pp + x4;
-                    acc += sT[(bi * 16 + r) * LT + bi * 16 + x] *
-                           *reinterpret_cast<const f32x4*>(sA + (bj * 16 + x) * LT + bi * 16 + c4);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = group_sum<4>(acc[i]);
-                if (pp == 0) *reinterpret_cast<f32x4*>(sT + (bi * 16 + r) * LT + bj * 16 + c4) = -acc;
+            if (NT == 4) {
+                // s = 2: block (bi, bj) = (2 + w/2, w%2) of T is
+                // -(T_{bi,2} X_{2,bj} + T_{bi,3} X_{3,bj}) with
+                // X_{m,bj} = A_{m,0} T_{0,bj} + A_{m,1} T_{1,bj}.  T_{0,1} and
+                // T_{2,3} are zero, so every wave runs the same products.  The
+                // wave's two X blocks go to unused upper blocks: of A,
+                // (0,1) (0,2) | (0,3) (1,2) | (1,3) (2,3) for waves 0-2, and of
+                // T, (0,2) (0,3) for wave 3.
+                const int bi = 2 + wu / 2, bj = wu % 2;
+                float* const xb = wu == 3 ? sT : sA;
+                float* xs2 = xb + (wu == 2 ? 16 * LT : 0) + (wu == 0 ? 1 : wu == 3 ? 2 : 3) * 16;
+                float* xs3 = xb + wu % 3 * 16 * LT + (wu == 2 || wu == 3 ? 3 : 2) * 16;
+                f32x4 x2 = zero, x3 = zero;
+                blk_mac2<LT>(x2, x3, blkA(2, 0), blkA(3, 0), blkT(0, bj), lane);
+                blk_mac2<LT>(x2, x3, blkA(2, 1), blkA(3, 1), blkT(1, bj), lane);
+                *reinterpret_cast<f32x4*>(xs2 + r * LT + c4) = x2;
+                *reinterpret_cast<f32x4*>(xs3 + r * LT + c4) = x3;
+                wave_lds_sync();
+                f32x4 t = blk_mac<LT>(zero, blkT(bi, 2), xs2, lane);
+                t = blk_mac<LT>(t, blkT(bi, 3), xs3, lane);
+                *reinterpret_cast<f32x4*>(blkT(bi, bj) + r * LT + c4) = -t;
             }
             __syncthreads();
         }
@@ -750,12 +817,12 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] *= bb[e];
             }
-            store_frag(gtp, f, lane, split8(x));
+            store_frag_nt(gtp, f, lane, split8(x));
         }
         if (tid < 2 * CP) {   // gamma_t, then eta_t = exp(g_last - g_t), from fp64 g
             const int t = tid % CP;
             const float e = tid < CP ? (float)s_g[t] : (float)(s_g[CP - 1] - s_g[t]);
-            W.gl[((int64_t)ci * P.h_v + hv) * 2 * CP + tid] = __expf(e);
+            __builtin_nontemporal_store(__expf(e), W.gl + ((int64_t)ci * P.h_v + hv) * 2 * CP + tid);
         }
         __syncthreads();
     }
