@@ -582,54 +582,40 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
             }
         }
         __syncthreads();
-        // ---- normalisation of each of q, k (h = 0, 1) staged in this pass:
-        // a quad of lanes per token (lane part p sums channels
-        // [p*D/4, (p+1)*D/4) of it, the quad adds up), then the same lanes
-        // scale their channels in place.
-        {
-            const int t = wave * 16 + (lane >> 2), part = lane & 3;
-            constexpr int CPL = D / 4;
-            if (t < CP) {   // uniform per wave
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    if (h * D < xb || h * D >= xb + CW) continue;   // not in this pass
-                    float* row = xr + t * LD + (h * D - xb) + part * CPL;
-                    float sq = 0.f;
-#pragma unroll
-                    for (int jj = 0; jj < CPL; jj += 4) {
-                        const float4 x = *reinterpret_cast<const float4*>(row + jj);
-                        sq = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, sq))));
-                    }
-                    sq = group_sum<4>(sq);
-                    const float rs = (h ? 1.0f : P.q_scale) / sqrtf(sq + P.eps);
-#pragma unroll
-                    for (int jj = 0; jj < CPL; jj += 4) {
-                        float4 x = *reinterpret_cast<const float4*>(row + jj);
-                        x.x *= rs; x.y *= rs; x.z *= rs; x.w *= rs;
-                        *reinterpret_cast<float4*>(row + jj) = x;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        // ---- fragments (qk, tile = wave, ks), lane (m, q): token tile*16+m,
-        // d_k {32ks+4q+i, 32ks+16+4q+i} (the d_k order in which the scan holds
-        // its state); each value is split once.  The scan builds the state
-        // update's K^T operand from these itself (LDS transpose reads).  The
-        // workspace is written with non-temporal stores: only the scan, a
-        // later launch, reads it, and lines left dirty in L2 would lengthen
-        // the write-back at the end of this launch.
+        // ---- normalisation and fragments (qk, tile = wave, ks), lane (m, q):
+        // token tile*16+m, d_k {32ks+4q+i, 32ks+16+4q+i} (the d_k order in
+        // which the scan holds its state).  The four lanes of a token
+        // (q = 0..3, 16 lanes apart) hold all of its D channels of q (h = 0)
+        // or k (h = 1): they add up their sums of squares, scale, and split
+        // each value once.  The scan builds the state update's K^T operand
+        // from these itself (LDS transpose reads).  The workspace is written
+        // with non-temporal stores: only the scan, a later launch, reads it,
+        // and lines left dirty in L2 would lengthen the write-back at the end
+        // of this launch.
         if (wave < NT) {
             bf16x8* gqk = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 if (h * D < xb || h * D >= xb + CW) continue;   // not in this pass
+                float x[NKS][8];
+                float sq = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const float* row = xr + (wave * 16 + m16) * LD + (h * D - xb) + ks * 32 + q4 * 4;
-                    float x[8];
-                    ld4x2(x, row, row + 16);
-                    const Frag f = split8(x);
+                    ld4x2(x[ks], row, row + 16);
+                }
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sq = fmaf(x[ks][e], x[ks][e], sq);
+                sq += __shfl_xor(sq, 16);
+                sq += __shfl_xor(sq, 32);
+                const float rs = (h ? 1.0f : P.q_scale) / sqrtf(sq + P.eps);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[ks][e] *= rs;
+                    const Frag f = split8(x[ks]);
                     store_frag_nt(gqk, (h * NT + wave) * NKS + ks, lane, f);
                     if (h) fk[ks] = f;
                     else fq[ks] = f;
