@@ -318,14 +318,19 @@ template <> struct Vec<float> {
 // staged in NPASS passes (1: all 2D at once, the shortest chain for grids of
 // one round; 2: q, then k, in half the LDS, so that three workgroups fit on
 // a CU).  KC > 0: conv taps fixed at compile time (must equal conv_k); 0:
-// runtime.
-template <int D, int CP, int KC, int NPASS, typename T>
-__global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_kernel(
+// runtime.  NW = 8 waves (one pass, grids of at most one workgroup per CU):
+// two groups of four waves solve two value heads side by side, and the
+// fragment phase splits q (waves 0-3) from k (waves 4-7).
+template <int D, int CP, int KC, int NPASS, int NW, typename T>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void prefill_factor_kernel(
     PoolView P, Ws W, int layer, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slot_ids, int chunk, const T* __restrict__ q,
     const T* __restrict__ k, const float* __restrict__ a, const float* __restrict__ b,
     const float* __restrict__ conv_w, Ckpt ck, int fused_n_seq, int total, int max_chunks) {
     static_assert(NPASS == 1 || NPASS == 2, "staging passes");
+    static_assert(NW == 4 || (NW == 8 && NPASS == 1), "waves per workgroup");
+    constexpr int NTH = 64 * NW;       // threads
+    constexpr int HP = NW / 4;         // value heads solved side by side
     constexpr int CW = 2 * D / NPASS;  // q|k channels staged per pass
     constexpr int LD = CW + 4;         // row of the staged lines (floats)
     constexpr int LT = CP + 4;         // padded row of A, T, P (16-byte aligned)
@@ -339,12 +344,11 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
     //              t0-(K-1)+r, overwritten in place by the conv+SiLU outputs
     //              (row t) and normalised;
     //   then       the K^ fragments [NT*NKS] (B operands of KK^T, QK^T);
-    //   then       A [CP][LT] and T [CP][LT]; P goes over A once T is done.
+    //   then       per head of the round, A [CP][LT] and T [CP][LT]; P goes
+    //              over A once T is done; with two groups, the exchanged
+    //              KK^T and QK^T tiles after them.
     extern __shared__ __align__(16) float smem[];
     float* xr = smem;
-    float* sA = smem;
-    float* sT = sA + CP * LT;
-    float* sP = sA;
     constexpr int KM = KC > 0 ? KC : kMaxConvK;   // compile-time tap bound
     constexpr int kMaxGroup = 4;                   // value heads per group kept in LDS
     // Cumulative log-decay in fp64: with a -> 0 (log a down to the clamp)
@@ -356,6 +360,9 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
+    const int gi = HP == 2 ? wave >> 2 : 0;   // wave group
+    const int lw = wave & 3;                  // wave in its group
+    const int gt = tid & 255;                 // thread in its group
     const int ci = blockIdx.x, g = blockIdx.y;
     // q|k channel x of the group -> its conv/window channel
     const auto conv_ch = [&](int x) { return x < D ? g * D + x : P.h_k * D + g * D + (x - D); };
@@ -448,8 +455,8 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
 
     // ---- a and b of the chunk's tokens for every value head of the group,
     // fetched with the staging loads (unconditional, positions clamped into
-    // the chunk; log a clamped; zero past L).  G * CP <= kThreads.
-    static_assert(kMaxGroup * 64 <= kThreads, "one a/b value per thread");
+    // the chunk; log a clamped; zero past L).  G * CP <= NTH.
+    static_assert(kMaxGroup * 64 <= NTH, "one a/b value per thread");
     const int ab_hl = min(tid / CP, G - 1), ab_t = tid % CP;
     float ab_a, ab_b;
     {
@@ -471,9 +478,9 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
     // sequence start, zeros past the chunk's valid tokens.
     const int nrow = K - 1 + CP;
     constexpr int vpr = CW / VN;
-    constexpr int NST = ((KM - 1 + CP) * vpr + kThreads - 1) / kThreads;
-    static_assert(kThreads % vpr == 0, "a thread keeps its column across iterations");
-    constexpr int RPI = kThreads / vpr;               // rows per iteration
+    constexpr int NST = ((KM - 1 + CP) * vpr + NTH - 1) / NTH;
+    static_assert(NTH % vpr == 0, "a thread keeps its column across iterations");
+    constexpr int RPI = NTH / vpr;                    // rows per iteration
     uint4 raw[NPASS][NST];
     {
         const int cv0 = (tid % vpr) * VN, r0 = tid / vpr;
@@ -504,7 +511,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         }
 #pragma unroll
         for (int it = 0; it < NST; ++it) {
-            const int e = tid + it * kThreads;
+            const int e = tid + it * NTH;
             if (e < nrow * vpr) {
                 const int r = e / vpr, cv = (e % vpr) * VN;
                 const bool valid = t0 - (K - 1) + r < t0 + L;
@@ -521,7 +528,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         // the last conv_k-1 raw inputs of the sequence (old window rows come
         // from LDS).
         if (cpos == 0) {
-            for (int e = tid; e < (K - 1) * CW; e += kThreads) {
+            for (int e = tid; e < (K - 1) * CW; e += NTH) {
                 const int m = e / CW, c = e % CW, x = xb + c;
                 const int64_t pp = s0 + len - (K - 1) + m;
                 const float v = pp >= s0 ? Io<T>::load(x < D ? q : k, (pp * P.h_k + g) * D + (x < D ? x : x - D))
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
             const int cs = m < ck.off[j + 1] - ck.off[j] ? ck.slots[ck.off[j] + m] : -1;
             if (cs >= 0 && cs < P.n_slots) {
                 T* cwin = reinterpret_cast<T*>(P.window) + ((int64_t)cs * P.n_layers + layer) * (int64_t)(K - 1) * C;
-                for (int e = tid; e < (K - 1) * CW; e += kThreads) {
+                for (int e = tid; e < (K - 1) * CW; e += NTH) {
                     const int r = e / CW, c = e % CW;
                     Io<T>::store(cwin, (int64_t)r * C + conv_ch(xb + c), xr[(chunk + r) * LD + c]);
                 }
@@ -547,8 +554,8 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         // K-1 rows past the thread's slice are the next slice's first outputs,
         // so they are read into registers before a barrier.
         {
-            constexpr int TPH = CP / (kThreads / CW);
-            static_assert(kThreads % CW == 0 && TPH >= 1, "token slices of the conv");
+            constexpr int TPH = CP / (NTH / CW);
+            static_assert(NTH % CW == 0 && TPH >= 1, "token slices of the conv");
             const int c = tid % CW, t0c = (tid / CW) * TPH;
             const float* w = cw[pass];
             float line[KM - 1], tail[KM - 1];
@@ -592,16 +599,17 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         // with non-temporal stores: only the scan, a later launch, reads it,
         // and lines left dirty in L2 would lengthen the write-back at the end
         // of this launch.
-        if (wave < NT) {
+        if (lw < NT) {
             bf16x8* gqk = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 if (h * D < xb || h * D >= xb + CW) continue;   // not in this pass
+                if (HP == 2 && h != gi) continue;               // group 0: q, group 1: k
                 float x[NKS][8];
                 float sq = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
-                    const float* row = xr + (wave * 16 + m16) * LD + (h * D - xb) + ks * 32 + q4 * 4;
+                    const float* row = xr + (lw * 16 + m16) * LD + (h * D - xb) + ks * 32 + q4 * 4;
                     ld4x2(x[ks], row, row + 16);
                 }
 #pragma unroll
@@ -616,7 +624,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[ks][e] *= rs;
                     const Frag f = split8(x[ks]);
-                    store_frag_nt(gqk, (h * NT + wave) * NKS + ks, lane, f);
+                    store_frag_nt(gqk, (h * NT + lw) * NKS + ks, lane, f);
                     if (h) fk[ks] = f;
                     else fq[ks] = f;
                 }
@@ -625,21 +633,26 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         __syncthreads();   // the next pass (or the fragments below) overwrite the rows
     }
     bf16x8* const lfr = reinterpret_cast<bf16x8*>(smem);   // [NT*NKS] K^ fragments
-    if (wave < NT) {
+    if (lw < NT && (HP == 1 || gi == 1)) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) store_frag(lfr, wave * NKS + ks, lane, fk[ks]);
+        for (int ks = 0; ks < NKS; ++ks) store_frag(lfr, lw * NKS + ks, lane, fk[ks]);
     }
     __syncthreads();
+    // Per head of a round: A and T (P over A) of group gi's head.
+    const auto sA_of = [&](int gg) { return smem + gg * 2 * CP * LT; };
+    f32x4* const xch = reinterpret_cast<f32x4*>(smem + HP * 2 * CP * LT);   // [2][NT][NT][64]
 
     // ---- KK^T and QK^T lower-triangular tiles: wave w takes tile row w.  A
-    // and B are the same split fragments (one d_k order on both sides).
+    // and B are the same split fragments (one d_k order on both sides).  With
+    // two groups, group 1 (which holds K^) computes KK^T and group 0 (Q^)
+    // QK^T; each passes its tiles to the other through LDS.
     f32x4 kk[NT], qk[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
         kk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
         qk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int ti = wave;  // tile row
+    const int ti = lw;  // tile row
     // Cumulative log-decay of value head hl of the group by wave hl (the
     // first waves have the fewest tile rows below).
     if (wave < G) {
@@ -658,24 +671,52 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
             for (int jt = 0; jt < NT; ++jt) {
                 if (jt <= ti) {
                     const Frag bk = load_frag(lfr, jt * NKS + ks, lane);
-                    kk[jt] = mma3(kk[jt], fk[ks], bk);
-                    qk[jt] = mma3(qk[jt], fq[ks], bk);
+                    if (HP == 1) {
+                        kk[jt] = mma3(kk[jt], fk[ks], bk);
+                        qk[jt] = mma3(qk[jt], fq[ks], bk);
+                    } else if (gi == 1) {
+                        kk[jt] = mma3(kk[jt], fk[ks], bk);
+                    } else {
+                        qk[jt] = mma3(qk[jt], fq[ks], bk);
+                    }
                 }
             }
         }
+        if (HP == 2) {
+#pragma unroll
+            for (int jt = 0; jt < NT; ++jt)
+                if (jt <= ti) xch[((gi * NT + ti) * NT + jt) * 64 + lane] = gi ? kk[jt] : qk[jt];
+        }
     }
     __syncthreads();   // the fragment region is reused below
+    if (HP == 2 && ti < NT) {
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) {
+            if (jt <= ti) {
+                const f32x4 x = xch[(((1 - gi) * NT + ti) * NT + jt) * 64 + lane];
+                if (gi) qk[jt] = x;
+                else kk[jt] = x;
+            }
+        }
+    }
 
-    // ---- per value head of the group: decay, A, T = (I+A)^-1, T', P.
-    for (int hl = 0; hl < G; ++hl) {
+    // ---- per value head of the group (HP at a time, group gi takes head
+    // hl0 + gi): decay, A, T = (I+A)^-1, T', P.  Every wave runs every
+    // barrier; a group without a head in the last round (odd G) idles.
+    for (int hl0 = 0; hl0 < G; hl0 += HP) {
+        const int hl = min(hl0 + gi, G - 1);
+        const bool act = hl0 + gi < G;   // uniform per wave
         const int hv = g * G + hl;
         const double* s_g = s_gg[hl];   // cumulative log-decay (zero past L)
         const float* s_b = s_bb[hl];    // b (zero past L)
+        float* const sA = sA_of(gi);
+        float* const sT = sA + CP * LT;
+        float* const sP = sA;
         // A (strictly lower) into LDS, P (lower incl. diagonal) into
         // registers until T is done.  The lane's four rows share their g and b
         // (one vector read each); blocks above the diagonal are plain zeros.
         float pvr[NT][4];
-        if (ti < NT) {
+        if (act && ti < NT) {
             const double2 ga = *reinterpret_cast<const double2*>(s_g + ti * 16 + q4 * 4);
             const double2 gb = *reinterpret_cast<const double2*>(s_g + ti * 16 + q4 * 4 + 2);
             const float4 bt4 = *reinterpret_cast<const float4*>(s_b + ti * 16 + q4 * 4);
@@ -701,7 +742,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         }
         // T's upper blocks (2b, 2b+1) share a 32-wide k-step with a diagonal
         // block in the T' fragments: zero them, so the fragments need no mask.
-        for (int e = tid; e < (NT / 2) * 256; e += kThreads) {
+        for (int e = gt; act && e < (NT / 2) * 256; e += 256) {
             const int pb = e / 256, r = (e % 256) / 16, c = e % 16;
             sT[(2 * pb * 16 + r) * LT + (2 * pb + 1) * 16 + c] = 0.f;
         }
@@ -712,8 +753,8 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         // 4p..4p+3 of the block's A rows (in registers) and the matching rows
         // of T's column c.  Entries of T not yet computed are still zero, so
         // row r of T is -sum over the whole row of A times T, no predicates.
-        if (wave < NT) {
-            const int blk = wave * 16;
+        if (act && lw < NT) {
+            const int blk = lw * 16;
             const int c = lane >> 2, pp = lane & 3;
             float ar[16][4];
 #pragma unroll
@@ -745,8 +786,8 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
             const auto blkA = [&](int bi, int bj) { return sA + bi * 16 * LT + bj * 16; };
             const auto blkT = [&](int bi, int bj) { return sT + bi * 16 * LT + bj * 16; };
             const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int wu = __builtin_amdgcn_readfirstlane(wave);   // wave index, known uniform
-            if (wu < NT / 2) {   // s = 1: block (2w+1, 2w)
+            const int wu = __builtin_amdgcn_readfirstlane(lw);   // wave in its group, known uniform
+            if (act && wu < NT / 2) {   // s = 1: block (2w+1, 2w)
                 const int bi = 2 * wu + 1, bj = 2 * wu;
                 float* xs = blkA(0, 1 + wu);
                 const f32x4 x = blk_mac<LT>(zero, blkA(bi, bj), blkT(bj, bj), lane);
@@ -755,7 +796,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
                 *reinterpret_cast<f32x4*>(blkT(bi, bj) + r * LT + c4) = -blk_mac<LT>(zero, blkT(bi, bi), xs, lane);
             }
             __syncthreads();
-            if (NT == 4) {
+            if (act && NT == 4) {
                 // s = 2: block (bi, bj) = (2 + w/2, w%2) of T is
                 // -(T_{bi,2} X_{2,bj} + T_{bi,3} X_{3,bj}) with
                 // X_{m,bj} = A_{m,0} T_{0,bj} + A_{m,1} T_{1,bj}.  T_{0,1} and
@@ -780,7 +821,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
             __syncthreads();
         }
         // P over A (A and the block products kept in its upper part are done).
-        if (ti < NT) {
+        if (act && ti < NT) {
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
@@ -792,7 +833,7 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
         // kc > tile/2 are all zero and are not written (the scan never fetches
         // them); inside the others T's upper part is zero (see above).
         bf16x8* gtp = W.tpf + ((int64_t)ci * P.h_v + hv) * NTP * kFragVecs;
-        for (int f = wave; f < NTP; f += kThreads / 64) {
+        for (int f = lw; act && f < NTP; f += 4) {
             const int tp = f / (NT * NKC), tile = (f / NKC) % NT, kc = f % NKC;
             if (kc > tile / 2) continue;
             float x[8];
@@ -805,10 +846,10 @@ __global__ __launch_bounds__(kThreads, NPASS == 2 ? 3 : 2) void prefill_factor_k
             }
             store_frag_nt(gtp, f, lane, split8(x));
         }
-        if (tid < 2 * CP) {   // gamma_t, then eta_t = exp(g_last - g_t), from fp64 g
-            const int t = tid % CP;
-            const float e = tid < CP ? (float)s_g[t] : (float)(s_g[CP - 1] - s_g[t]);
-            __builtin_nontemporal_store(__expf(e), W.gl + ((int64_t)ci * P.h_v + hv) * 2 * CP + tid);
+        if (act && gt < 2 * CP) {   // gamma_t, then eta_t = exp(g_last - g_t), from fp64 g
+            const int t = gt % CP;
+            const float e = gt < CP ? (float)s_g[t] : (float)(s_g[CP - 1] - s_g[t]);
+            __builtin_nontemporal_store(__expf(e), W.gl + ((int64_t)ci * P.h_v + hv) * 2 * CP + gt);
         }
         __syncthreads();
     }
@@ -1318,17 +1359,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     }
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // Factor grids up to this many workgroups run in one round at two per CU.
 constexpr int64_t kFactorOneRoundWgs = 512;
 
 // Dynamic LDS of the factor kernel: the largest of its phases (staged rows
 // of a pass, the K^ fragments, A and T).
-template <int D, int CP, int KC, int NPASS>
+template <int D, int CP, int KC, int NPASS, int NW>
 size_t factor_lds_bytes() {
     constexpr int KM = KC > 0 ? KC : kMaxConvK;
     const size_t a = (size_t)(KM - 1 + CP) * (2 * D / NPASS + 4) * sizeof(float);
     const size_t f = (size_t)(CP / 16) * (D / 32) * kFragVecs * 16;
-    const size_t b = (size_t)2 * CP * (CP + 4) * sizeof(float);
+    // A and T per head of a round, then (two groups) the exchanged tiles
+    const size_t b = (size_t)(NW / 4) * 2 * CP * (CP + 4) * sizeof(float) +
+                     (NW == 8 ? (size_t)2 * (CP / 16) * (CP / 16) * 64 * 16 : 0);
     return std::max(a, std::max(f, b));
 }
 
@@ -1338,19 +1394,23 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
                       const void* q, const void* k, const void* v, const float* a, const float* b,
                       const float* conv_w, void* out, Ckpt ck, hipStream_t stream) {
     const PoolView& P = pool->view;
-    static std::atomic<uint64_t> factor1_lds{0}, factor2_lds{0}, scan_lds{0};
-    // Factor grids that run in one round (two workgroups per CU on the 256
-    // CUs) stage q|k in one pass (the shorter chain per workgroup); larger
-    // grids in two, for three workgroups per CU.  Measured at chunk 64 on a
-    // Qwen3-Next layer: 16 calls of 512 tokens 866 -> (one pass) us, one
-    // 8192-token call 430 -> 416 us and the 16-sequence varlen batch
-    // 1537 -> 1442 us with two passes.
-    const bool one_pass = (int64_t)mc * P.h_k <= kFactorOneRoundWgs;
-    const size_t lf = one_pass ? factor_lds_bytes<D, CP, KC, 1>() : factor_lds_bytes<D, CP, KC, 2>();
+    static std::atomic<uint64_t> factor8_lds{0}, factor1_lds{0}, factor2_lds{0}, scan_lds{0};
+    // Factor grids of at most one workgroup per CU run eight waves per
+    // workgroup (two value heads side by side); grids that run in one round
+    // at two workgroups per CU stage q|k in one pass (the shorter chain per
+    // workgroup); larger grids in two, for three workgroups per CU.  Measured
+    // at chunk 64 on a Qwen3-Next layer: 16 calls of 512 tokens 866 -> (one
+    // pass) us, one 8192-token call 430 -> 416 us and the 16-sequence
+    // varlen batch 1537 -> 1442 us with two passes.
+    const int64_t nwg = (int64_t)mc * P.h_k;
+    const int variant = nwg <= device_cus() ? 8 : nwg <= kFactorOneRoundWgs ? 1 : 2;
+    const size_t lf = variant == 8   ? factor_lds_bytes<D, CP, KC, 1, 8>()
+                      : variant == 1 ? factor_lds_bytes<D, CP, KC, 1, 4>()
+                                     : factor_lds_bytes<D, CP, KC, 2, 4>();
     const size_t ls = ScanLds<D, CP>::bytes;
-    hipError_t e = one_pass
-        ? allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, 1, T>, lf, &factor1_lds)
-        : allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, 2, T>, lf, &factor2_lds);
+    hipError_t e = variant == 8   ? allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, 1, 8, T>, lf, &factor8_lds)
+                   : variant == 1 ? allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, 1, 4, T>, lf, &factor1_lds)
+                                  : allow_dynamic_lds(&prefill_factor_kernel<D, CP, KC, 2, 4, T>, lf, &factor2_lds);
     if (e != hipSuccess) return e;
     e = allow_dynamic_lds(&prefill_scan_kernel<D, CP, KC, T>, ls, &scan_lds);
     if (e != hipSuccess) return e;
@@ -1362,14 +1422,20 @@ hipError_t launch_all(const gdn_pool* pool, Ws W, int32_t layer, int32_t n_seq,
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (one_pass)
-        hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, 1, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
-                           stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
-                           static_cast<const T*>(k), a, b, conv_w, ck, fused, total, mc);
+    const T* qt = static_cast<const T*>(q);
+    const T* kt = static_cast<const T*>(k);
+    if (variant == 8)
+        hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, 1, 8, T>), dim3(mc, P.h_k), dim3(512), lf,
+                           stream, P, W, layer, cu, slot_ids, chunk, qt, kt, a, b, conv_w, ck, fused,
+                           total, mc);
+    else if (variant == 1)
+        hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, 1, 4, T>), dim3(mc, P.h_k), dim3(256), lf,
+                           stream, P, W, layer, cu, slot_ids, chunk, qt, kt, a, b, conv_w, ck, fused,
+                           total, mc);
     else
-        hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, 2, T>), dim3(mc, P.h_k), dim3(kThreads), lf,
-                           stream, P, W, layer, cu, slot_ids, chunk, static_cast<const T*>(q),
-                           static_cast<const T*>(k), a, b, conv_w, ck, fused, total, mc);
+        hipLaunchKernelGGL((prefill_factor_kernel<D, CP, KC, 2, 4, T>), dim3(mc, P.h_k), dim3(256), lf,
+                           stream, P, W, layer, cu, slot_ids, chunk, qt, kt, a, b, conv_w, ck, fused,
+                           total, mc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_scan_kernel<D, CP, KC, T>), dim3((D / kRows) * P.h_v * n_seq),

@@ -148,6 +148,32 @@ def test_prefill_8192_tokens_all_groups(oracle_pool_workers):
     assert torch.equal(pool.state[keep], st0[keep]) and torch.equal(pool.window[keep], wn0[keep])
 
 
+@pytest.mark.parametrize("T", [300, 1000])
+def test_prefill_factor_grid_sizes_all_groups(oracle_pool_workers, T):
+    """The first T tokens of the 8192-token sequence in one call, against the
+    oracle on every group: 300 tokens give 6 x 16 (chunk, q/k head) work items
+    (at most one factor workgroup per CU: eight waves, two value heads side
+    by side), 1000 tokens 17 x 16 (one round of four-wave workgroups, q|k
+    staged in one pass)."""
+    case = syn.prefill_case()
+    s, io = case["shapes"], case["io"]
+    tok = {n: x[:T] for n, x in case["tokens"].items()}
+    say(f"prefill T={T} chunk 64, all groups")
+    pool = make_pool(s, 4, io)
+    scramble_pool(pool, 23)
+    pool.reset(dev(np.array([1], np.int32), torch.int32))
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    out = run_prefill(pool, 0, np.array([0, T], np.int32), np.array([1], np.int32), tok,
+                      dev(case["conv_w"]), 64, io)
+    torch.cuda.synchronize()
+    assert pool.error() == 0
+    ref = oracle_pool_workers.prefill_all_groups(s, tok, case["conv_w"], np.array([0, T]),
+                                                 np.array([0]))
+    _check_layer(pool, out, np.array([1], np.int32), ref, io)
+    keep = [0, 2, 3]
+    assert torch.equal(pool.state[keep], st0[keep]) and torch.equal(pool.window[keep], wn0[keep])
+
+
 def test_prefill_scheduler_split_matches_unsplit(oracle_pool_workers):
     """The same 8192 tokens as 16 calls of 512 tokens carrying state and
     window: equal to the single call (within tolerance) and to the oracle on
