@@ -66,48 +66,23 @@ __device__ __forceinline__ void store_frag4(bf16x8* base, int f, int dl, int e0,
 // ----------------------------------------------- 16x16 fp32 blocks in LDS
 
 // acc + X Z for 16x16 fp32 blocks in LDS (row stride LT floats), on one
-// wave's VALU: the lane holds row lane/4, columns 4*(lane%4)..+3.  Two
-// halves of the inner index, each loaded as a whole before its FMAs; the
-// scheduling barriers keep the next half's loads from being hoisted (about
-// 40 registers at a time).
+// wave's matrix cores in fp32 (four 16x16x4 steps): lane (m, q) reads
+// X[m][k0+q] and Z[k0+q][m] and holds rows 4q..4q+3 of column m of the
+// result.
 template <int LT>
-__device__ __forceinline__ f32x4 blk_mac(f32x4 acc, const float* X, const float* Z, int lane) {
-    const int r = lane >> 2, c4 = (lane & 3) * 4;
+__device__ __forceinline__ f32x4 blk_mfma(f32x4 acc, const float* X, const float* Z, int lane) {
+    const int m = lane & 15, q = lane >> 4;
 #pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 8) {
-        const float4 xa = *reinterpret_cast<const float4*>(X + r * LT + k0);
-        const float4 xb = *reinterpret_cast<const float4*>(X + r * LT + k0 + 4);
-        const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-        f32x4 z[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) z[k] = *reinterpret_cast<const f32x4*>(Z + (k0 + k) * LT + c4);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc += x[k] * z[k];
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int k0 = 0; k0 < 16; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[m * LT + k0 + q], Z[(k0 + q) * LT + m], acc, 0, 0, 0);
     return acc;
 }
-
-// The same for two left operands sharing Z: acc0 + X0 Z and acc1 + X1 Z.
+// Stores a result of blk_mfma (times s) into a 16x16 block.
 template <int LT>
-__device__ __forceinline__ void blk_mac2(f32x4& acc0, f32x4& acc1, const float* X0, const float* X1,
-                                         const float* Z, int lane) {
-    const int r = lane >> 2, c4 = (lane & 3) * 4;
+__device__ __forceinline__ void blk_store(float* Y, f32x4 v, float s, int lane) {
+    const int m = lane & 15, q = lane >> 4;
 #pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 8) {
-        float x0[8], x1[8];
-        ld8(x0, X0 + r * LT + k0);
-        ld8(x1, X1 + r * LT + k0);
-        f32x4 z[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) z[k] = *reinterpret_cast<const f32x4*>(Z + (k0 + k) * LT + c4);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            acc0 += x0[k] * z[k];
-            acc1 += x1[k] * z[k];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int i = 0; i < 4; ++i) Y[(4 * q + i) * LT + m] = s * v[i];
 }
 
 // Orders one wave's LDS writes before its later LDS reads of other lanes'
@@ -778,11 +753,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
         // Off-diagonal blocks by block doubling: for each pair of adjacent
         // runs of s blocks (s = 1, then 2 for four blocks), the lower-left
         // part of T is -T_BB L_BA T_AA (L = I + A; runs A above B).  One wave
-        // per output block; the products X = L_BA T_AA that it needs go
-        // through A's upper blocks (zero, unused), each private to one wave,
-        // within the wave (no workgroup barrier between the two products).
+        // per output block, its 16x16 products on the matrix cores in fp32;
+        // the products X = L_BA T_AA that it needs go through A's upper
+        // blocks (zero, unused), each private to one wave, within the wave
+        // (no workgroup barrier between the two products).
         {
-            const int r = lane >> 2, c4 = (lane & 3) * 4;
             const auto blkA = [&](int bi, int bj) { return sA + bi * 16 * LT + bj * 16; };
             const auto blkT = [&](int bi, int bj) { return sT + bi * 16 * LT + bj * 16; };
             const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -790,10 +765,9 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
             if (act && wu < NT / 2) {   // s = 1: block (2w+1, 2w)
                 const int bi = 2 * wu + 1, bj = 2 * wu;
                 float* xs = blkA(0, 1 + wu);
-                const f32x4 x = blk_mac<LT>(zero, blkA(bi, bj), blkT(bj, bj), lane);
-                *reinterpret_cast<f32x4*>(xs + r * LT + c4) = x;
+                blk_store<LT>(xs, blk_mfma<LT>(zero, blkA(bi, bj), blkT(bj, bj), lane), 1.f, lane);
                 wave_lds_sync();
-                *reinterpret_cast<f32x4*>(blkT(bi, bj) + r * LT + c4) = -blk_mac<LT>(zero, blkT(bi, bi), xs, lane);
+                blk_store<LT>(blkT(bi, bj), blk_mfma<LT>(zero, blkT(bi, bi), xs, lane), -1.f, lane);
             }
             __syncthreads();
             if (act && NT == 4) {
@@ -808,15 +782,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
                 float* const xb = wu == 3 ? sT : sA;
                 float* xs2 = xb + (wu == 2 ? 16 * LT : 0) + (wu == 0 ? 1 : wu == 3 ? 2 : 3) * 16;
                 float* xs3 = xb + wu % 3 * 16 * LT + (wu == 2 || wu == 3 ? 3 : 2) * 16;
-                f32x4 x2 = zero, x3 = zero;
-                blk_mac2<LT>(x2, x3, blkA(2, 0), blkA(3, 0), blkT(0, bj), lane);
-                blk_mac2<LT>(x2, x3, blkA(2, 1), blkA(3, 1), blkT(1, bj), lane);
-                *reinterpret_cast<f32x4*>(xs2 + r * LT + c4) = x2;
-                *reinterpret_cast<f32x4*>(xs3 + r * LT + c4) = x3;
+                f32x4 x2 = blk_mfma<LT>(zero, blkA(2, 0), blkT(0, bj), lane);
+                f32x4 x3 = blk_mfma<LT>(zero, blkA(3, 0), blkT(0, bj), lane);
+                x2 = blk_mfma<LT>(x2, blkA(2, 1), blkT(1, bj), lane);
+                x3 = blk_mfma<LT>(x3, blkA(3, 1), blkT(1, bj), lane);
+                blk_store<LT>(xs2, x2, 1.f, lane);
+                blk_store<LT>(xs3, x3, 1.f, lane);
                 wave_lds_sync();
-                f32x4 t = blk_mac<LT>(zero, blkT(bi, 2), xs2, lane);
-                t = blk_mac<LT>(t, blkT(bi, 3), xs3, lane);
-                *reinterpret_cast<f32x4*>(blkT(bi, bj) + r * LT + c4) = -t;
+                f32x4 t = blk_mfma<LT>(zero, blkT(bi, 2), xs2, lane);
+                t = blk_mfma<LT>(t, blkT(bi, 3), xs3, lane);
+                blk_store<LT>(blkT(bi, bj), t, -1.f, lane);
             }
             __syncthreads();
         }
