@@ -333,7 +333,9 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
     __shared__ __align__(16) float s_bb[kMaxGroup][CP];
     __shared__ float s_la[kMaxGroup][CP];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index through readfirstlane: known uniform, so conditions on
+    // it compile to scalar branches)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m16 = lane & 15, q4 = lane >> 4;
     const int gi = HP == 2 ? wave >> 2 : 0;   // wave group
     const int lw = wave & 3;                  // wave in its group
