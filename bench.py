@@ -52,7 +52,7 @@ DECODE_SRC_SHA256 = "e5a23a53c65d1cf4245f064aad40c171f2ead96029a3935eab7040e4be2
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
 # (profiles/prefill_mfma_counters.txt; profiles/prefill_hbm_traffic.txt has the bytes)
-PREFILL_SRC_SHA256 = "1258da1b382e608c537f88cf25f239efbb96be36a977377f06ce698e49878d32"
+PREFILL_SRC_SHA256 = "21bdfa052d18c49dd6439fb9941dab49a041cca49cdb8676d7039c496eb20471"
 
 
 def prefill_exec_flop_per_token(case):
