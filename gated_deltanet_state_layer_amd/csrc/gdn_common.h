@@ -129,6 +129,20 @@ hipError_t allow_dynamic_lds(KFn* kernel, size_t bytes, std::atomic<uint64_t>* d
     return e;
 }
 
+// Compute units of the current device (queried once per device; 0 if the
+// query fails).
+inline int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // Prefill checkpoints: after every `every_chunks` chunks of sequence j,
 // checkpoint m goes to slot slots[off[j] + m] (if m < off[j+1] - off[j]).
 struct Ckpt {

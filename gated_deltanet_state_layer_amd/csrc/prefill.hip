@@ -1336,19 +1336,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     }
 }
 
-// Compute units of the current device (queried once per device).
-int device_cus() {
-    static std::atomic<int> cus[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int n = cus[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cus[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // Factor grids up to this many workgroups run in one round at two per CU.
 constexpr int64_t kFactorOneRoundWgs = 512;
 

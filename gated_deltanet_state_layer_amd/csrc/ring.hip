@@ -95,11 +95,11 @@ __device__ __forceinline__ void mma3_idx(f32x4* acc, const Frag* const* a, const
 // tiles of the solve (ring_len + n_tok <= 16 NT).  KC > 0: conv taps fixed at
 // compile time (= conv_k); NTM: most new tokens per call (n_tok <= NTM).
 template <int D, int NT, int MODE, int KC, int NTM, typename T>
-__global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
+__device__ __forceinline__ void ring_item(
     PoolView P, int layer, const int32_t* __restrict__ slot_ids, int n_tok,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ conv_w,
-    const int32_t* __restrict__ accept_len, T* __restrict__ out) {
+    const int32_t* __restrict__ accept_len, T* __restrict__ out, const int e, const int h) {
     constexpr int NTOK = 16 * NT;          // tokens of the solve (padded)
     constexpr int KP = D + 4;              // row of kn / qn (floats)
     constexpr int MP = NTOK + 4;           // row of vt and of the token matrices
@@ -142,9 +142,13 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
     bf16x8* const fr = VERIFY ? reinterpret_cast<bf16x8*>(kq) : fr_sep;
     __shared__ int s_last;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The thread index through an empty asm: a persistent caller runs this
+    // body in a loop, and values derived from it would otherwise be hoisted
+    // out of the loop and held in registers across the whole body.
+    int tid_opaque = threadIdx.x;
+    asm volatile("" : "+v"(tid_opaque));
+    const int tid = tid_opaque, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m16 = lane & 15, q4 = lane >> 4;
-    const int e = blockIdx.x, h = blockIdx.y;
     const int slot = slot_ids[e];
     if (slot < 0) return;
     if (slot >= P.n_slots) {
@@ -694,15 +698,106 @@ __global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
     }
 }
 
+// Most entries a persistent commit orders (fold-first) in LDS.
+constexpr int kRingPersistMax = 1024;
+
+// One workgroup per (entry, value head), or, for a commit with persist != 0,
+// a persistent grid of one round of workgroups walking the (entry, head)
+// items with a stride of the grid: folding entries first (a fold solves and
+// writes the state, ~3x an append's time), so that the long items start
+// early and the appends fill in behind them, with no workgroup dispatched
+// per short append.  The order is a stable partition of the entries by the
+// fold test the item itself makes (ring count + accepted tokens > L).
+template <int D, int NT, int MODE, int KC, int NTM, typename T>
+__global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
+    PoolView P, int layer, const int32_t* __restrict__ slot_ids, int n_tok,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ conv_w,
+    const int32_t* __restrict__ accept_len, T* __restrict__ out) {
+    ring_item<D, NT, MODE, KC, NTM, T>(P, layer, slot_ids, n_tok, q, k, v, a, b, conv_w, accept_len,
+                                       out, blockIdx.x, blockIdx.y);
+}
+
+template <int D, int NT, int KC, int NTM, typename T>
+__global__ __launch_bounds__(ring_threads(D), 3) void ring_commit_persistent_kernel(
+    PoolView P, int layer, const int32_t* __restrict__ slot_ids, int n_tok,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ conv_w,
+    const int32_t* __restrict__ accept_len, int n) {
+    constexpr int MODE = kModeCommit;
+    {
+        {
+            __shared__ int s_ord[kRingPersistMax];
+            const int tid = threadIdx.x, lane = tid & 63;
+            if (tid < 64) {   // wave 0: lane l takes entries [l*per, (l+1)*per)
+                const int per = (n + 63) / 64, e0 = min(lane * per, n), e1 = min(e0 + per, n);
+                const auto folds = [&](int e) {
+                    const int slot = slot_ids[e];
+                    if (slot < 0 || slot >= P.n_slots) return false;
+                    const int c = min(max(P.ring_cnt[(int64_t)slot * P.n_layers + layer], 0), P.ring_len);
+                    return c + min(max(accept_len[e], 0), n_tok) > P.ring_len;
+                };
+                int nf = 0;
+                for (int e = e0; e < e1; ++e) nf += folds(e);
+                int incl = nf;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(incl, o);
+                    if (lane >= o) incl += y;
+                }
+                const int total_f = __shfl(incl, 63);
+                int pf = incl - nf, pa = total_f + (e0 - (incl - nf));   // first fold / append slot
+                for (int e = e0; e < e1; ++e) {
+                    if (folds(e)) s_ord[pf++] = e;
+                    else s_ord[pa++] = e;
+                }
+            }
+            __syncthreads();
+#pragma unroll 1
+            for (int i = blockIdx.x; i < n * P.h_v; i += gridDim.x) {
+                // (the entry through readfirstlane: known uniform, so its addresses stay scalar)
+                ring_item<D, NT, MODE, KC, NTM, T>(P, layer, slot_ids, n_tok, q, k, v, a, b, conv_w,
+                                                   accept_len, nullptr,
+                                                   __builtin_amdgcn_readfirstlane(s_ord[i / P.h_v]),
+                                                   i % P.h_v);
+                __syncthreads();
+            }
+        }
+    }
+}
+
 template <int D, int NT, int MODE, int KC, int NTM, typename T>
 void launch_one(const gdn_pool* pool, int32_t layer, int32_t n, const int32_t* slot_ids,
                 int32_t n_tok, const void* q, const void* k, const void* v, const float* a,
                 const float* b, const float* conv_w, const int32_t* accept_len, void* out,
                 hipStream_t stream) {
-    hipLaunchKernelGGL((ring_kernel<D, NT, MODE, KC, NTM, T>), dim3(n, pool->view.h_v),
-                       dim3(ring_threads(D)), 0, stream, pool->view, layer, slot_ids, n_tok,
-                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                       a, b, conv_w, accept_len, static_cast<T*>(out));
+    auto kern = ring_kernel<D, NT, MODE, KC, NTM, T>;
+    auto pkern = ring_commit_persistent_kernel<D, NT, KC, NTM, T>;
+    // A commit runs persistent (one round of workgroups, fold-first order)
+    // when its entries fit the order buffer.
+    int grid = 0;
+    if (MODE == kModeCommit && n <= kRingPersistMax) {
+        static std::atomic<int> per_cu{-1};
+        int pc = per_cu.load(std::memory_order_relaxed);
+        if (pc < 0) {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, reinterpret_cast<const void*>(pkern),
+                                                             ring_threads(D), 0) != hipSuccess)
+                pc = 0;
+            per_cu.store(pc, std::memory_order_relaxed);
+        }
+        const int64_t items = (int64_t)n * pool->view.h_v;
+        if (pc > 0 && device_cus() > 0 && items > (int64_t)pc * device_cus())
+            grid = pc * device_cus();
+    }
+    if (grid > 0)
+        hipLaunchKernelGGL(pkern, dim3(grid), dim3(ring_threads(D)), 0, stream, pool->view, layer,
+                           slot_ids, n_tok, static_cast<const T*>(q), static_cast<const T*>(k),
+                           static_cast<const T*>(v), a, b, conv_w, accept_len, n);
+    else
+        hipLaunchKernelGGL(kern, dim3(n, pool->view.h_v), dim3(ring_threads(D)), 0, stream,
+                           pool->view, layer, slot_ids, n_tok, static_cast<const T*>(q),
+                           static_cast<const T*>(k), static_cast<const T*>(v), a, b, conv_w,
+                           accept_len, static_cast<T*>(out));
 }
 
 // Compile-time shapes: conv_k = 4 with at most 4 new tokens (the common

@@ -154,6 +154,21 @@ def test_ring_cycles_qwen3_next_shapes():
     assert folds > 0
 
 
+@pytest.mark.parametrize("h_k,h_v,d,n,n_slots", [(8, 16, 64, 96, 128), (16, 32, 128, 32, 40)])
+def test_ring_cycles_many_entries_vs_oracle(h_k, h_v, d, n, n_slots):
+    """More (entry, value head) commit items than one round of workgroups
+    (1536 and 1024), so the commit walks them persistently, folding entries
+    first; a padding entry among them; ring of 8, accepted lengths uniform on
+    1..4, against the oracle."""
+    s, io = syn.Shapes(h_k, h_v, d, d, 4), "bf16"
+    say(f"ring cycles, {n} entries: {s}")
+    ids_np = np.random.default_rng(97 + n).permutation(n_slots)[:n].astype(np.int32)
+    ids_np[5] = -1
+    folds = _run_cycles(s, io, 8, 4, 6, n_slots, ids_np, 520 + n,
+                        acc_fn=lambda rng, c, m: rng.integers(1, 5, size=m))
+    assert folds > 0
+
+
 def test_ring_conv_k_2_and_8():
     for K in (2, 8):
         s = syn.Shapes(2, 4, 64, 64, K)
