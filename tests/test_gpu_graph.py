@@ -128,15 +128,16 @@ def test_graph_replayed_verify_and_prefill_equal_eager():
     assert pa.error() == 0
 
 
-def test_graph_replayed_ring_cycle_equals_eager():
+@pytest.mark.parametrize("n,n_slots", [(16, 24), (40, 48)])
+def test_graph_replayed_ring_cycle_equals_eager(n, n_slots):
     """A verify-ring cycle (ring_verify then ring_commit with acceptance
     read from device memory) recorded once and replayed through appends and
     folds; ring counts, records, states, windows and outputs equal the eager
-    twin at every replay."""
+    twin at every replay.  With 40 entries (1280 commit items) the commit
+    runs persistent."""
     s, io, n_tok = syn.QWEN3_NEXT, "bf16", 4
-    say("graph ring cycle")
-    rng = np.random.default_rng(970)
-    n, n_slots = 16, 24
+    say(f"graph ring cycle, {n} entries")
+    rng = np.random.default_rng(970 + n)
     ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
     contents = syn.draw_pool_contents(63, ids_np, s, io)
     pa, pb = make_pool(s, n_slots, io, ring_len=8), make_pool(s, n_slots, io, ring_len=8)
