@@ -452,7 +452,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
     // Raw rows with 16-byte loads, every pass's issued here, before the
     // first is used (source pointer selected, position clamped into the
     // chunk), so the staging costs one round trip: window rows before the
-    // sequence start, zeros past the chunk's valid tokens.
+    // sequence start, token L-1 again past the chunk's valid tokens.
     const int nrow = K - 1 + CP;
     constexpr int vpr = CW / VN;
     constexpr int NST = ((KM - 1 + CP) * vpr + NTH - 1) / NTH;
@@ -490,11 +490,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
         for (int it = 0; it < NST; ++it) {
             const int e = tid + it * NTH;
             if (e < nrow * vpr) {
+                // rows past the chunk's valid tokens hold token L-1 (the load
+                // was clamped): only the conv outputs of padding tokens read
+                // them, and those never reach a valid output or the state
+                // (their b is zero, so their rows of A and of T' are zero)
                 const int r = e / vpr, cv = (e % vpr) * VN;
-                const bool valid = t0 - (K - 1) + r < t0 + L;
                 float x[VN];
 #pragma unroll
-                for (int i = 0; i < VN; ++i) x[i] = valid ? Vec<T>::at(raw[pass][it], i) : 0.f;
+                for (int i = 0; i < VN; ++i) x[i] = Vec<T>::at(raw[pass][it], i);
 #pragma unroll
                 for (int i = 0; i < VN; i += 4)
                     *reinterpret_cast<float4*>(xr + r * LD + cv + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
                 for (int m = 0; m < KM - 1; ++m)
                     if (m < K - 1) z = fmaf(w[m], line[m], z);
                 z = fmaf(w[K - 1], x, z);
-                xr[(t0c + i) * LD + c] = t0c + i < L ? silu(z) : 0.f;
+                xr[(t0c + i) * LD + c] = silu(z);   // padding tokens too (see the staging)
 #pragma unroll
                 for (int m = 0; m < KM - 1; ++m)
                     line[m] = (m == K - 2) ? x : (m < K - 2 ? line[m + 1] : line[m]);
