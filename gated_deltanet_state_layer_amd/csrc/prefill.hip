@@ -1034,11 +1034,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         }
         rg = W.gl[((int64_t)(ci0 + cc) * P.h_v + h) * 2 * CP + (tid % (2 * CP))];
     };
-    // Store chunk cc's raw rows: zero past its valid tokens, window rows
-    // before the sequence start (only the first chunk reaches back there).
+    // Store chunk cc's raw rows, with window rows before the sequence start
+    // (only the first chunk reaches back there).  Rows past its valid tokens
+    // repeat the last one (the load is clamped): only padding tokens' v reads
+    // them, and a padding token's v cannot reach an output or the state (its
+    // b is zero, so its column of T' is zero).
     auto store_raw = [&](int cc, int buf, bool first) {
         const int64_t t0 = s0 + (int64_t)cc * chunk;
-        const int L = min(chunk, len - cc * chunk);
         float* dst = s_raw + buf * NRAW * kRows;
 #pragma unroll
         for (int it = 0; it < kRawIt; ++it) {
@@ -1046,10 +1048,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             const int r = e / kRawVec, cv = (e % kRawVec) * VN;
             if (r < K - 1 + CP) {
                 const int64_t p = t0 - (K - 1) + r;
-                const bool valid = p < t0 + L;
                 float x[VN];
 #pragma unroll
-                for (int i = 0; i < VN; ++i) x[i] = valid ? Vec<T>::at(rv[it], i) : 0.f;
+                for (int i = 0; i < VN; ++i) x[i] = Vec<T>::at(rv[it], i);
                 if (first && p < s0) {   // window rows before the sequence start
 #pragma unroll
                     for (int i = 0; i < VN; ++i) x[i] = s_win[(K - 1 + (int)(p - s0)) * kRows + cv + i];
@@ -1062,8 +1063,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         if (tid < 2 * CP) s_g[buf * 2 * CP + tid] = rg;
     };
     // conv+SiLU of the block's v channels for chunk cc from s_raw[buf].  All
-    // KM taps are applied (weights past conv_k are zero, and raw rows past the
-    // chunk are zero), so there is no branch between the LDS reads.
+    // KM taps are applied (weights past conv_k are zero, and the raw rows they
+    // meet are finite), so there is no branch between the LDS reads; padding
+    // tokens are not masked (see store_raw).
     const int cch = tid % kRows;
     float wv[KM];
 #pragma unroll
@@ -1073,8 +1075,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     // tokens as one vector.
     constexpr int TPT = CP / (kThreads / kRows);
     static_assert(TPT == 2 || TPT == 4, "tokens per thread in the v conv");
-    auto conv_v = [&](int cc, int buf) {
-        const int L = min(chunk, len - cc * chunk);
+    auto conv_v = [&](int buf) {
         const float* src = s_raw + buf * NRAW * kRows;
         float* dst = s_v + buf * CP * kRows;
         const int tt = (tid / kRows) * TPT;
@@ -1087,7 +1088,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             float z = 0.f;
 #pragma unroll
             for (int m = 0; m < KM; ++m) z = fmaf(wv[m], xr[i + m], z);
-            y[i] = tt + i < L ? silu(z) : 0.f;
+            y[i] = silu(z);
         }
         if constexpr (TPT == 4)
             *reinterpret_cast<float4*>(dst + cch * CP + tt) = make_float4(y[0], y[1], y[2], y[3]);
@@ -1145,7 +1146,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     }
     store_raw(0, 0, true);
     __syncthreads();
-    conv_v(0, 0);
+    conv_v(0);
     // Raw rows are fetched one chunk ahead of their LDS store, which is one
     // phase ahead of their conv.
     fetch_raw(min(1, n_ch - 1));
@@ -1322,7 +1323,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                 }
             }
         }
-        if (nxt) conv_v(cc + 1, buf ^ 1);
+        if (nxt) conv_v(buf ^ 1);
         fetch_raw(min(cc + 2, n_ch - 1));
         prefetch(ci0 + min(cc + 2, n_ch - 1));
         __syncthreads();
