@@ -47,12 +47,12 @@ DECODE_SRC_SHA256 = "e5a23a53c65d1cf4245f064aad40c171f2ead96029a3935eab7040e4be2
 # Executed bf16 MFMA flops of the prefill kernels per token, from rocprofv3
 # counter runs (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, factor + scan, median
 # dispatch; profiles/prefill_mfma_counters.txt): the hi/lo bf16 split and the
-# padded tiles make them ~3.4x the algorithmic flops.  Valid for the prefill
+# padded tiles make them ~3.2x the algorithmic flops.  Valid for the prefill
 # source they were taken on (PREFILL_SRC_SHA256), else reported as null.
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
 # (profiles/prefill_mfma_counters.txt; profiles/prefill_hbm_traffic.txt has the bytes)
-PREFILL_SRC_SHA256 = "21bdfa052d18c49dd6439fb9941dab49a041cca49cdb8676d7039c496eb20471"
+PREFILL_SRC_SHA256 = "38b856965f946594e607d2f590ab5f04aecc9cc89665929f20ea2d2f70ed134b"
 
 
 def prefill_exec_flop_per_token(case):
