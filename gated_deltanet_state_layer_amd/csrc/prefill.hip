@@ -696,6 +696,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
         // registers until T is done.  The lane's four rows share their g and b
         // (one vector read each); blocks above the diagonal are plain zeros.
         float pvr[NT][4];
+        // The column index goes through an empty asm: the s < t and s <= t
+        // lane masks below are then recomputed per head (one compare each)
+        // instead of being hoisted out of the loop and spilled (two lane
+        // reads each).
+        int m16h = m16;
+        asm volatile("" : "+v"(m16h));
         if (act && ti < NT) {
             const double2 ga = *reinterpret_cast<const double2*>(s_g + ti * 16 + q4 * 4);
             const double2 gb = *reinterpret_cast<const double2*>(s_g + ti * 16 + q4 * 4 + 2);
@@ -704,7 +710,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
             const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
 #pragma unroll
             for (int jt = 0; jt < NT; ++jt) {
-                const int s = jt * 16 + m16;          // column
+                const int s = jt * 16 + m16h;         // column
                 const double gs = s_g[s];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -735,7 +741,9 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
         // row r of T is -sum over the whole row of A times T, no predicates.
         if (act && lw < NT) {
             const int blk = lw * 16;
-            const int c = lane >> 2, pp = lane & 3;
+            int c = lane >> 2;   // opaque, like m16h above: its masks stay in the loop
+            asm volatile("" : "+v"(c));
+            const int pp = lane & 3;
             float ar[16][4];
 #pragma unroll
             for (int r = 0; r < 16; ++r)
