@@ -1189,26 +1189,34 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
             mma3_n<NKS>(acc, fqk[1], fb);
             // K^ rows of this token tile into LDS in natural [token][d_k]
             // order (fragment elements 0-3 are d_k 32ks+4q.., 4-7 are +16).
-            if (wave < NT) {
-                const int kr = tw * 16 + m16, sz = kswz<D>(kr);
-                __bf16* kh = s_kh + kr * KRS;
-                __bf16* kl = s_kl + kr * KRS;
+            // Half of them go out while the MFMAs run and half after R: with
+            // all 16 writes between the v read and R, the LDS counter (at
+            // most 15 outstanding) could only wait for the v read by waiting
+            // for every write.
+            const auto stage_k = [&](int ks0, int ks1) {
+                if (NT * 64 >= kThreads || wave < NT) {   // no branch when every wave has a tile
+                    const int kr = tw * 16 + m16, sz = kswz<D>(kr);
+                    __bf16* kh = s_kh + kr * KRS;
+                    __bf16* kl = s_kl + kr * KRS;
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const Frag& f = fqk[1][ks];
-                    const int c0 = (ks * 32 + q4 * 4) ^ sz, c1 = (ks * 32 + 16 + q4 * 4) ^ sz;
-                    *reinterpret_cast<bf16x4*>(kh + c0) = __builtin_shufflevector(f.hi, f.hi, 0, 1, 2, 3);
-                    *reinterpret_cast<bf16x4*>(kh + c1) = __builtin_shufflevector(f.hi, f.hi, 4, 5, 6, 7);
-                    *reinterpret_cast<bf16x4*>(kl + c0) = __builtin_shufflevector(f.lo, f.lo, 0, 1, 2, 3);
-                    *reinterpret_cast<bf16x4*>(kl + c1) = __builtin_shufflevector(f.lo, f.lo, 4, 5, 6, 7);
+                    for (int ks = ks0; ks < ks1; ++ks) {
+                        const Frag& f = fqk[1][ks];
+                        const int c0 = (ks * 32 + q4 * 4) ^ sz, c1 = (ks * 32 + 16 + q4 * 4) ^ sz;
+                        *reinterpret_cast<bf16x4*>(kh + c0) = __builtin_shufflevector(f.hi, f.hi, 0, 1, 2, 3);
+                        *reinterpret_cast<bf16x4*>(kh + c1) = __builtin_shufflevector(f.hi, f.hi, 4, 5, 6, 7);
+                        *reinterpret_cast<bf16x4*>(kl + c0) = __builtin_shufflevector(f.lo, f.lo, 0, 1, 2, 3);
+                        *reinterpret_cast<bf16x4*>(kl + c1) = __builtin_shufflevector(f.lo, f.lo, 4, 5, 6, 7);
+                    }
                 }
-            }
+            };
+            stage_k(0, NKS / 2);
             f32x4 ak = acc[0];
 #pragma unroll
             for (int ks = 1; ks < NKS; ++ks) ak += acc[ks];
             const float r4[4] = {v4.x - g4.x * ak[0], v4.y - g4.y * ak[1],
                                  v4.z - g4.z * ak[2], v4.w - g4.w * ak[3]};
             store_frag4(s_rf, tw >> 1, dst_lane, dst_e0, r4);
+            stage_k(NKS / 2, NKS);
             load_qk(cn, 1);
         }
         __syncthreads();
