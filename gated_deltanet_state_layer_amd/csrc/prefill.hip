@@ -847,12 +847,12 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
 
 // One workgroup per (sequence, value head, block of 16 state rows), 256
 // threads, serial over the sequence's chunks.  Per chunk (three phases):
-//   1. wave w < CP/16 takes token tile w: X_K = K S0^T for its 16 tokens
-//      (B operand: the state block, published split in LDS), and
-//      R = V - diag(gamma) X_K goes to LDS as B fragments;
+//   1. wave w < CP/16 takes token tile w: X_K = K S0^T and X_Q = Q S0^T for
+//      its 16 tokens (B operand: the state block, published split in LDS,
+//      read once for both); R = V - diag(gamma) X_K goes to LDS as B
+//      fragments and XQ = diag(gamma) X_Q stays in registers;
 //   2. U = T' R for the tile, published as B fragments with its decayed copy
-//      diag(exp(g_last - g)) U; interleaved with it, X_Q = Q S0^T, and
-//      XQ = diag(gamma) X_Q stays in registers;
+//      diag(exp(g_last - g)) U;
 //   3. O = XQ + P U for the tile is written out; wave w < D/32 updates state
 //      tiles 2w, 2w+1 of S^T (d_k x rows), S^T <- exp(g_last) S^T + K^T (decayed
 //      U), and republishes them.  K^T comes from the chunk's K^ rows, staged
@@ -981,7 +981,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
     Frag fqk[2][NKS];      // Q and K fragments of token tile tw
     Frag ftt[NKC];         // T' fragments of token tile tw
     Frag fpp[NKC];         // P fragments of token tile tw
-    // qk = 0: Q^ (used in phase 2), 1: K^ (phase 1); each is refetched for
+    // qk = 0: Q^, 1: K^ (both used in phase 1); each is refetched for
     // the next chunk right after its last use.
     auto load_qk = [&](int ci, int qk) {
         const bf16x8* base = W.qkf + ((int64_t)ci * P.h_k + g) * NQK * kFragVecs;
@@ -1170,23 +1170,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
         const float4 g4 = *reinterpret_cast<const float4*>(gb + tw * 16 + q4 * 4);
         const float4 e4 = *reinterpret_cast<const float4*>(gb + CP + tw * 16 + q4 * 4);
 
-        // (1) X_K for token tile tw; R = V - diag(gamma) X_K to LDS.  (X_Q
-        // only feeds the output: it is computed in phase 2, where it fills
-        // the gaps of the short U chain.)
+        // (1) X_K and X_Q for token tile tw, from one read of the state
+        // fragments; R = V - diag(gamma) X_K to LDS, XQ = diag(gamma) X_Q in
+        // registers until the output.
         f32x4 xq;
         {
             Frag fb[NKS];
-            f32x4 acc[NKS];
+            f32x4 acc[NKS], accq[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 fb[ks] = load_frag(s_stf, ks, lane);
                 acc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accq[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             // the v rows of the tile, requested with the state fragments so
             // that R waits for the MFMAs only (not another LDS round trip)
             const float4 v4 = *reinterpret_cast<const float4*>(s_v + buf * CP * kRows + m16 * CP + tw * 16 + q4 * 4);
             __builtin_amdgcn_sched_barrier(0);
             mma3_n<NKS>(acc, fqk[1], fb);
+            mma3_n<NKS>(accq, fqk[0], fb);
             // K^ rows of this token tile into LDS in natural [token][d_k]
             // order (fragment elements 0-3 are d_k 32ks+4q.., 4-7 are +16).
             // Half of them go out while the MFMAs run and half after R: with
@@ -1217,14 +1219,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                                  v4.z - g4.z * ak[2], v4.w - g4.w * ak[3]};
             store_frag4(s_rf, tw >> 1, dst_lane, dst_e0, r4);
             stage_k(NKS / 2, NKS);
+            f32x4 aq = accq[0];
+#pragma unroll
+            for (int ks = 1; ks < NKS; ++ks) aq += accq[ks];
+            xq = f32x4{g4.x * aq[0], g4.y * aq[1], g4.z * aq[2], g4.w * aq[3]};
             load_qk(cn, 1);
+            load_qk(cn, 0);
         }
         __syncthreads();
 
-        // (2) U = T' R for token tile tw (U and the decayed U to LDS),
-        //     interleaved with X_Q = Q S0^T (S0 is still the published state).
+        // (2) U = T' R for token tile tw (U and the decayed U to LDS).
         {
-            constexpr int NJ = NKC + NKS;
+            constexpr int NJ = NKC;
             Frag fa[NJ], fb[NJ];
             f32x4 acc[NJ];
 #pragma unroll
@@ -1233,30 +1239,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_scan_kernel(
                 fb[kc] = load_frag(s_rf, kc, lane);
             }
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                fa[NKC + ks] = fqk[0][ks];
-                fb[NKC + ks] = load_frag(s_stf, ks, lane);
-            }
-#pragma unroll
             for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             mma3_n<NJ>(acc, fa, fb);
-            f32x4 uv = acc[0], aq = acc[NKC];
+            f32x4 uv = acc[0];
 #pragma unroll
             for (int kc = 1; kc < NKC; ++kc) uv += acc[kc];
-#pragma unroll
-            for (int ks = 1; ks < NKS; ++ks) aq += acc[NKC + ks];
             float u4[4], uu4[4];
-            const float gl4[4] = {g4.x, g4.y, g4.z, g4.w}, el4[4] = {e4.x, e4.y, e4.z, e4.w};
+            const float el4[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 u4[i] = uv[i];
                 uu4[i] = uv[i] * el4[i];
-                xq[i] = gl4[i] * aq[i];
             }
             store_frag4(s_uf, tw >> 1, dst_lane, dst_e0, u4);
             store_frag4(s_uuf, tw >> 1, dst_lane, dst_e0, uu4);
             load_t(cn);
-            load_qk(cn, 0);
         }
         if (nxt) store_raw(cc + 1, buf ^ 1, false);
         __syncthreads();
