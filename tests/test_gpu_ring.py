@@ -314,3 +314,31 @@ def test_ring_layers_are_independent_and_accept_len_is_clamped():
     assert torch.equal(pool.state[:, 0], l0[0]) and torch.equal(pool.window[:, 0], l0[1]), \
         "layer 0 changed"
     assert pool.error() == 0
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_ring_cycles_random_configuration_vs_oracle(i):
+    """Verify -> commit cycles then a flush on 30 seeded random
+    configurations (q/k heads 1-2, 1-4 value heads per group, d 32/64/128,
+    conv widths 2-8, bf16 and fp32 io, rings of 1-24 tokens, 1-8 drafts,
+    accepted lengths 0..n_tok, up to 40 entries with padding), against the
+    oracle: every cycle's draft outputs, ring counts and windows, the states
+    after the flush, and every slot the calls do not name."""
+    rng = np.random.default_rng(4242 + 65537 * i)
+    h_k = int(rng.integers(1, 3))
+    h_v = h_k * int(rng.choice([1, 2, 3, 4]))
+    d = int(rng.choice([32, 64, 128]))
+    s = syn.Shapes(h_k, h_v, d, d, int(rng.choice([2, 3, 4, 4, 6, 8])))
+    io = str(rng.choice(["bf16", "f32"]))
+    n_tok = int(rng.integers(1, 9))
+    ring_len = int(rng.integers(1, 25))
+    n = int(rng.choice([1, 3, 8, 17, 40]))
+    n_slots = n + int(rng.integers(1, 9))
+    ids_np = rng.permutation(n_slots)[:n].astype(np.int32)
+    if n > 1:
+        ids_np[rng.random(n) < 0.1] = -1
+    if (ids_np < 0).all():
+        ids_np[0] = n_slots - 1 if n_slots - 1 not in ids_np else 0
+    say(f"ring sweep {i}: {s} io={io} L={ring_len} n_tok={n_tok} entries={n} of {n_slots}")
+    _run_cycles(s, io, ring_len, n_tok, int(rng.integers(4, 9)), n_slots, ids_np,
+                int(rng.integers(1 << 20)))
