@@ -181,3 +181,30 @@ def test_in_proj_rejects_unsupported_hidden():
     with pytest.raises(G.GdnError) as ei:
         pool.in_proj_workspace_bytes(4, 100)
     assert ei.value.status == -2
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_in_proj_random_configuration_vs_oracle(i):
+    """24 seeded random configurations: q/k heads 1-4, 1-4 value heads per
+    group, d 32/64/128, hidden sizes 32-4096 (multiples of 32), 1 to 3000
+    tokens (the skinny, split-hidden, 128-tile and 256-tile paths, ragged
+    rows and channels), bf16 and fp32 io, against the oracle."""
+    rng = np.random.default_rng(777 + 8191 * i)
+    h_k = int(rng.integers(1, 5))
+    d = int(rng.choice([32, 64, 128]))
+    s = syn.Shapes(h_k, h_k * int(rng.choice([1, 2, 3, 4])), d, d, 4)
+    hidden = 32 * int(rng.integers(1, 129))
+    n_tok = int(rng.choice([1, 5, 64, 65, 200, 511, 512, 700, 1500, 3000]))
+    io = str(rng.choice(["bf16", "f32"]))
+    x = syn.draw_hidden(rng, (n_tok,), hidden)
+    w = syn.draw_in_proj_weight(rng, s, hidden)
+    pool = make_pool(s, 1, io)
+    q, k, v, a, b, nb = _project(pool, s, x, w, io)
+    say(f"in_proj sweep {i}: {s} hidden {hidden} tokens {n_tok} io {io} workspace {nb}")
+    rq, rk, rv, ra, rb = O.in_projection(x, w, s)
+    check_out("q", host(q), rq, io)
+    check_out("k", host(k), rk, io)
+    check_out("v", host(v), rv, io)
+    check_f32("a", host(a), ra)
+    check_f32("b", host(b), rb)
+    assert pool.error() == 0
