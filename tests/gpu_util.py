@@ -91,6 +91,34 @@ def check_f32(name, x, ref, tol=TOL_F32):
     assert e <= tol, f"{name}: {e:.3e} > {tol:g}"
 
 
+# Near-rank-1 prefill states (a fresh slot that took one or two tokens holds
+# about b v k^T, whose largest entries can be up to d times its RMS): the
+# hi + lo bf16 operand split keeps a product to ~2e-5 of its own size, which
+# relative to such a state's RMS can exceed TOL_F32.  A state that misses the
+# RMS bound passes only if its largest entry is over PEAKED RMS and its error
+# is within TOL_PEAKED of that entry.
+PEAKED = 30.0
+TOL_PEAKED = 4e-5
+
+
+def check_state(name, x, ref):
+    """TOL_F32 relative to the RMS; a near-rank-1 state that misses it is held
+    to TOL_PEAKED relative to its largest entry instead."""
+    ref = np.asarray(ref, np.float64)
+    assert np.isfinite(np.asarray(x)).all(), f"{name}: non-finite values"
+    e = rel_err(x, ref)
+    if e <= TOL_F32:
+        say(f"  {name}: max|err|/rms = {e:.3e} (tol {TOL_F32:g})")
+        return
+    rms = np.sqrt(np.mean(ref * ref))
+    peak = np.abs(ref).max() / rms
+    em = float(np.abs(np.asarray(x, np.float64) - ref).max() / np.abs(ref).max())
+    say(f"  {name}: max|err|/rms = {e:.3e} over {TOL_F32:g}; near rank 1 (largest entry {peak:.0f} "
+        f"RMS): max|err|/max|ref| = {em:.2e} (tol {TOL_PEAKED:g})")
+    assert peak > PEAKED, f"{name}: {e:.3e} > {TOL_F32:g}"
+    assert em <= TOL_PEAKED, f"{name}: {em:.3e} > {TOL_PEAKED:g} of the largest entry"
+
+
 def check_bf16(name, x, ref, tol=TOL_BF16):
     """bf16 outputs: every element within half a bf16 ulp of its reference
     value (the rounding of the output itself) plus tol * RMS(ref)."""

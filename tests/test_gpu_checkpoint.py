@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 
 import gdn_synth as syn
-from gpu_util import (check_f32, check_out, dev, host, load_slots, make_pool, oracle_pool, say,
-                      scramble_pool, tokens_to_dev)
+from gpu_util import (check_f32, check_out, check_state, dev, host, load_slots, make_pool, oracle_pool,
+                      say, scramble_pool, tokens_to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -175,3 +175,74 @@ def test_validate_mode_rejects_overlapping_checkpoint_slots():
     assert e.value.status == -3
     torch.cuda.synchronize()
     assert torch.equal(pool.state, st0)
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_prefill_checkpoints_random_configuration_vs_oracle(i):
+    """20 seeded random configurations of prefill with checkpoints (q/k heads
+    1-2, 1-4 value heads per group, d 32/64/128, chunk 16/32/64, interval of
+    1-4 chunks, conv widths 2-8, bf16 and fp32 io, 1-5 sequences, fresh and
+    continuing slots, checkpoint rows past a sequence's end and negative
+    checkpoint slots), against the oracle: outputs, final states and
+    windows, every stored checkpoint, and every slot nothing was written to."""
+    rng = np.random.default_rng(9001 + 6007 * i)
+    h_k = int(rng.integers(1, 3))
+    d = int(rng.choice([32, 64, 128]))
+    s = syn.Shapes(h_k, h_k * int(rng.choice([1, 2, 3, 4])), d, d, int(rng.choice([2, 3, 4, 4, 6, 8])))
+    chunk = int(rng.choice([16, 32, 64]))
+    every = chunk * int(rng.integers(1, 5))
+    io = str(rng.choice(["bf16", "f32"]))
+    n_seq = int(rng.integers(1, 6))
+    lens = rng.integers(1, 5 * every + 1, n_seq)
+    rows = [int(lens[j] // every + rng.integers(0, 2)) for j in range(n_seq)]   # maybe one past the end
+    n_rows = sum(rows)
+    n_slots = n_seq + n_rows + 2
+    perm = rng.permutation(n_slots).astype(np.int32)
+    ids_np = perm[:n_seq]
+    ck_np = perm[n_seq:n_seq + n_rows].copy()
+    ck_np[rng.random(n_rows) < 0.15] = -1
+    off_np = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    say(f"checkpoint sweep {i}: {s} chunk={chunk} every={every} io={io} lens={lens.tolist()} "
+        f"rows={rows}")
+    tok = syn.draw_tokens(rng, s, (T,), io)
+    w = syn.draw_conv_weights(rng, s)
+    pool = make_pool(s, n_slots, io)
+    scramble_pool(pool, int(rng.integers(1 << 30)))
+    cont = [int(x) for x in ids_np if rng.random() < 0.4]
+    contents = syn.draw_pool_contents(int(rng.integers(1 << 30)), np.array(cont, np.int64), s, io) \
+        if cont else {}
+    if contents:
+        load_slots(pool, contents)
+    fresh = [int(x) for x in ids_np if int(x) not in cont]
+    if fresh:
+        pool.reset(_i32(fresh))
+    st0, wn0 = pool.state.clone(), pool.window.clone()
+    td = tokens_to_dev(tok, io)
+    out = torch.full((T, s.h_v, s.d_v), float("nan"), dtype=td["v"].dtype, device="cuda")
+    ws = torch.empty(max(pool.prefill_workspace_bytes(n_seq, T, chunk), 256), dtype=torch.uint8,
+                     device="cuda")
+    pool.prefill_ckpt(0, _i32(cu), _i32(ids_np), T, chunk, td["q"], td["k"], td["v"], td["a"],
+                      td["b"], dev(w), out, every, _i32(off_np), _i32(ck_np), ws)
+    torch.cuda.synchronize()
+    assert pool.error() == 0
+    ref, snaps, op = _oracle_checkpoints(s, {k: contents[k] for k in cont}, ids_np, cu, tok, w, every)
+    check_out("outputs", host(out), ref, io)
+    written = set()
+    for j, sl in enumerate(ids_np):
+        check_state(f"final state of slot {sl}", host(pool.state[int(sl)]), op.S[j])
+        assert np.array_equal(host(pool.window[int(sl)]), op.X[j]), f"final window of slot {sl}"
+        written.add(int(sl))
+        for m in range(rows[j]):
+            ck = int(ck_np[off_np[j] + m])
+            if ck < 0 or (j, m) not in snaps:   # a negative slot, or a row past the end
+                continue
+            st, wn = snaps[(j, m)]
+            check_state(f"checkpoint {m} of sequence {j} (slot {ck})", host(pool.state[ck]), st)
+            assert np.array_equal(host(pool.window[ck]), wn), f"checkpoint window {(j, m)}"
+            written.add(ck)
+    for sl in range(n_slots):
+        if sl not in written:
+            assert torch.equal(pool.state[sl], st0[sl]) and torch.equal(pool.window[sl], wn0[sl]), \
+                f"slot {sl} changed"
