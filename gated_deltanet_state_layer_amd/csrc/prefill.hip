@@ -744,17 +744,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
             int c = lane >> 2;   // opaque, like m16h above: its masks stay in the loop
             asm volatile("" : "+v"(c));
             const int pp = lane & 3;
-            float ar[16][4];
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ar[r][i] = sA[(blk + r) * LT + blk + 4 * pp + i];
             float tq[4] = {0.f, 0.f, 0.f, 0.f};   // T[blk + 4pp + i][blk + c]
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                // row r of the block's A (this part's four columns), read at
+                // its step rather than all up front: 4 registers, not 64
+                const float4 a4 = *reinterpret_cast<const float4*>(sA + (blk + r) * LT + blk + 4 * pp);
+                const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
                 float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = fmaf(ar[r][i], tq[i], acc);
+                for (int i = 0; i < 4; ++i) acc = fmaf(ar[i], tq[i], acc);
                 acc = group_sum<4>(acc);
                 const float trc = (r == c) ? 1.f : (r > c ? -acc : 0.f);
 #pragma unroll
