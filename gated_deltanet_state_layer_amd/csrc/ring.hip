@@ -445,17 +445,16 @@ __device__ __forceinline__ void ring_item(
         // of the column), then T10 = -T11 (A10 T00)
         if (wave < NT) {
             const int blk = wave * 16, col = lane >> 2, part = lane & 3;
-            float ar[16][4];
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ar[r][i] = mA[(blk + r) * MP + blk + 4 * part + i];
             float tq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                // row r of the block's A (this part's four columns), read at its
+                // step: 4 registers instead of 64 beside the state tile
+                const float4 a4 = *reinterpret_cast<const float4*>(mA + (blk + r) * MP + blk + 4 * part);
+                const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
                 float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = fmaf(ar[r][i], tq[i], acc);
+                for (int i = 0; i < 4; ++i) acc = fmaf(ar[i], tq[i], acc);
                 acc = group_sum<4>(acc);
                 const float trc = r == col ? 1.f : (r > col ? -acc : 0.f);
 #pragma unroll
@@ -709,7 +708,10 @@ constexpr int kRingPersistMax = 1024;
 // per short append.  The order is a stable partition of the entries by the
 // fold test the item itself makes (ring count + accepted tokens > L).
 template <int D, int NT, int MODE, int KC, int NTM, typename T>
-__global__ __launch_bounds__(ring_threads(D)) void ring_kernel(
+// A verify with one token tile and a fixed conv width (the common shape)
+// runs four workgroups per CU: 120 VGPRs without spills, and four state tiles
+// streaming per CU instead of three.
+__global__ __launch_bounds__(ring_threads(D), MODE == kModeVerify && NT == 1 && KC > 0 ? 4 : 1) void ring_kernel(
     PoolView P, int layer, const int32_t* __restrict__ slot_ids, int n_tok,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, const float* __restrict__ conv_w,
