@@ -52,7 +52,7 @@ DECODE_SRC_SHA256 = "e5a23a53c65d1cf4245f064aad40c171f2ead96029a3935eab7040e4be2
 PREFILL_MFMA_FLOP_PER_TOKEN = {"single": (1.573e7 + 2.013e8) * 512 / 8192,
                                "varlen": (7.016e7 + 8.981e8) * 512 / 36080}
 # (profiles/prefill_mfma_counters.txt; profiles/prefill_hbm_traffic.txt has the bytes)
-PREFILL_SRC_SHA256 = "3521b027ef6d0351b23bb3de763149b8ba74e575361526c4485f00e013a58863"
+PREFILL_SRC_SHA256 = "84b624e214c3583cb0e7844ac956ad3cd8863a806430b2bcce5e5a9c7cb0c167"
 
 
 def prefill_exec_flop_per_token(case):

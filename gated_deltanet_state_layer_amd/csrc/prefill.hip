@@ -736,8 +736,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (NPASS == 2 ? 3 : 2)) void p
 
         // (I+A)^-1, blocked by 16.  Diagonal blocks by forward substitution,
         // one wave per block: lane = 4 * column c + part p; part p owns columns
-        // 4p..4p+3 of the block's A rows (in registers) and the matching rows
-        // of T's column c.  Entries of T not yet computed are still zero, so
+        // 4p..4p+3 of the block's A rows (read row by row) and the matching
+        // rows of T's column c (in registers).  Entries of T not yet computed are still zero, so
         // row r of T is -sum over the whole row of A times T, no predicates.
         if (act && lw < NT) {
             const int blk = lw * 16;
