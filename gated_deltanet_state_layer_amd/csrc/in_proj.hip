@@ -179,8 +179,11 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
 // Many tokens: a 256 x 128 output tile per workgroup, wave (wm, wn) owning a
 // 128 x 64 block (8 x 4 MFMA tiles), so each wave reads 384 bytes of LDS
 // operands per MFMA instead of the 512 of a 64 x 64 block, and each k-block
-// of 32 runs 32 MFMAs per wave between barriers.  k-blocks go through LDS,
-// double buffered as above.  It covers the full 128-channel
+// of 32 runs 32 MFMAs per wave between barriers.  k-blocks go through a
+// ring of three LDS stages, written by buffer loads that store straight into
+// LDS (no staging registers), issued two blocks ahead; one barrier per block.
+// Against the double-buffered register staging of the kernel above this took
+// the 8192-token call from 369-381 to 336-343 us.  It covers the full 128-channel
 // columns only: the channels past the last of them (the gate logits when
 // the q|k|v channels are a multiple of 128) go to the skinny kernel below,
 // 64 tokens per workgroup, in a second short launch.  A partial column
@@ -192,8 +195,13 @@ template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
     int n_tn) {
-    __shared__ __align__(16) uint16_t sa[2][BM2 * LDK];
-    __shared__ __align__(16) uint16_t sb[2][BN * LDK];
+    // Three stages of (256 x rows + 128 W rows) x 32 k, 64 bytes per row,
+    // filled by loads that write LDS directly (no registers in between).
+    // Those loads count on vmcnt until their data is in LDS; the waits in the
+    // loop below are explicit, since nothing else orders the LDS reads after
+    // them.
+    constexpr int kStage = (BM2 + BN) * BK;          // bf16 per stage
+    __shared__ __align__(16) uint16_t sa[3 * kStage];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
@@ -208,69 +216,72 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
     const int m0 = tm * BM2, n0 = tn * BN;
     const int nblk = H / BK;
     const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
-    // staging: vector e = tid + 256 i of a tile is row e / 4, k 8 (e % 4);
-    // x: 4 vectors per thread (256 rows), W: 2 (128 rows).  Rows past M or N
-    // read zeros (offset past the descriptor).
-    int ga[4], gb[2], la[4], lb[2];
-    bool va_ok[4], vb_ok[2];
+    // One load instruction fills 16 rows (1 KiB): lane l writes bytes
+    // 16 l .. 16 l + 15 after the wave-uniform base, i.e. row l / 4, slot
+    // l % 4.  Slot s of row r holds the k-chunk s ^ ((r / 4) % 4), so that the
+    // 16 rows of an MFMA fragment read hit 16 different bank groups.  Rows
+    // past M or N read zeros (offset past the descriptor).
+    const int lrow = lane >> 2, kchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    int gx[4], gw[2];
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) {
-        const int e = tid + i2 * kThreads, r = e >> 2, kv = (e & 3) * 8;
-        va_ok[i2] = m0 + r < M;
-        ga[i2] = va_ok[i2] ? ((m0 + r) * H + kv) * 2 : 0;
-        la[i2] = r * LDK + kv;
+        const int r = wave * 64 + i2 * 16 + lrow;
+        gx[i2] = m0 + r < M ? ((m0 + r) * H + kchunk * 8) * 2 : kOffOOB;
     }
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2) {
-        const int e = tid + i2 * kThreads, r = e >> 2, kv = (e & 3) * 8;
-        vb_ok[i2] = n0 + r < N;
-        gb[i2] = vb_ok[i2] ? ((n0 + r) * H + kv) * 2 : 0;
-        lb[i2] = r * LDK + kv;
+        const int r = wave * 32 + i2 * 16 + lrow;
+        gw[i2] = n0 + r < N ? ((n0 + r) * H + kchunk * 8) * 2 : kOffOOB;
     }
-    uint4 va[4], vb[2];
-    auto fetch = [&](int kb) {
-        const bool ok = kb < nblk;
+    using lds_ptr = __attribute__((address_space(3))) void*;
+    auto issue = [&](int kb, int st) {
+        uint16_t* base = sa + st * kStage;
+        const int kofs = kb * BK * 2;
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2)
-            va[i2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                x_rs, ok && va_ok[i2] ? ga[i2] + kb * BK * 2 : kOffOOB, 0, 0));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                x_rs, (lds_ptr)(base + (wave * 64 + i2 * 16) * BK), 16,
+                gx[i2] == kOffOOB ? kOffOOB : gx[i2] + kofs, 0, 0, 0);
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2)
-            vb[i2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                w_rs, ok && vb_ok[i2] ? gb[i2] + kb * BK * 2 : kOffOOB, 0, 0));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                w_rs, (lds_ptr)(base + (BM2 + wave * 32 + i2 * 16) * BK), 16,
+                gw[i2] == kOffOOB ? kOffOOB : gw[i2] + kofs, 0, 0, 0);
     };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) *reinterpret_cast<uint4*>(&sa[buf][la[i2]]) = va[i2];
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) *reinterpret_cast<uint4*>(&sb[buf][lb[i2]]) = vb[i2];
-    };
+    const int rsw = 8 * (q4 ^ ((m16 >> 2) & 3));     // this lane's k-chunk, swizzled (bf16)
     f32x4 acc[8][4];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    fetch(0);
-    stage(0);
-    __syncthreads();
+    issue(0, 0);
+    if (nblk > 1) issue(1, 1);
+    int st = 0;
     for (int kb = 0; kb < nblk; ++kb) {
-        const int buf = kb & 1;
-        fetch(kb + 1);
+        // this thread's loads of block kb are done (block kb + 1's may still
+        // be in flight), then every thread's are, and every wave has finished
+        // reading the stage that block kb + 2 goes to
+        if (kb + 1 < nblk) __builtin_amdgcn_s_waitcnt(0x0f76);   // vmcnt(6)
+        else __builtin_amdgcn_s_waitcnt(0x0f70);                 // vmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + 2 < nblk) issue(kb + 2, st == 0 ? 2 : st - 1);
+        const uint16_t* sx = sa + st * kStage;
+        const uint16_t* sw = sx + BM2 * BK;
         bf16x8 fa[8], fb[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
-            fb[nt] = *reinterpret_cast<const bf16x8*>(&sb[buf][(wn * 64 + nt * 16 + m16) * LDK + q4 * 8]);
+            fb[nt] = *reinterpret_cast<const bf16x8*>(&sw[(wn * 64 + nt * 16 + m16) * BK + rsw]);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
-            fa[mt] = *reinterpret_cast<const bf16x8*>(&sa[buf][(wm * 128 + mt * 16 + m16) * LDK + q4 * 8]);
+            fa[mt] = *reinterpret_cast<const bf16x8*>(&sx[(wm * 128 + mt * 16 + m16) * BK + rsw]);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
-        stage(buf ^ 1);
-        __syncthreads();
+        st = st == 2 ? 0 : st + 1;
     }
+    __syncthreads();   // every wave is done with the operand stages
     // Epilogue through LDS: lane (m16, q4) holds rows 16 mt + 4 q4 + j of
     // column 16 nt + m16 of the wave's 128 x 64 block, so stores straight from
     // the accumulators write 2- or 4-byte pieces.  Each wave instead writes 32
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
     // lane holds y[m0 + 128 wm + 16 mt + 4 q + j][n0 + 64 wn + 16 nt + m16]
     constexpr int ER = 32, ELD = 64 + 4;   // rows per pass; padded row (floats)
     static_assert(4 * ER * ELD * sizeof(float) <= sizeof(sa), "epilogue buffer fits in sa");
-    float* eb = reinterpret_cast<float*>(&sa[0][0]) + wave * ER * ELD;
+    float* eb = reinterpret_cast<float*>(&sa[0]) + wave * ER * ELD;
 #pragma unroll
     for (int pass = 0; pass < 128 / ER; ++pass) {
 #pragma unroll
