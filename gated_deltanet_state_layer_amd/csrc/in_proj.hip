@@ -11,8 +11,9 @@
 // dimension is not split): the 256 x 128 tile kernel, plus the skinny kernel
 // for the channels past its last full 128-channel column.  Otherwise the
 // gemm kernel: grid (N/128, M/128, ksplit), 4 waves, a 128 x 128 output tile
-// per workgroup; k-blocks of 32 go through LDS, double buffered, loaded with
-// 16-byte buffer loads whose descriptors return zeros past the ragged ends.
+// per workgroup; k-blocks of 32 go through a ring of three LDS stages,
+// filled two blocks ahead by 16-byte buffer loads that write LDS directly and
+// whose descriptors return zeros past the ragged ends.
 // With few tokens the hidden dimension is split over ksplit workgroups so
 // that enough weight bytes are in flight; a second kernel adds the partial
 // sums.  Otherwise the gemm kernel writes the outputs itself.
@@ -87,18 +88,19 @@ __device__ __forceinline__ void put8(const ProjOut& o, int64_t m, int n, const f
 }
 
 // 128 x 128 output tile per workgroup (wave (wm, wn) owns a 64 x 64
-// quadrant: 4 x 4 MFMA tiles), k-blocks of 32 staged in LDS, double
-// buffered: each thread loads its share of block kb+1 (two 16-byte vectors
-// of x, two of W) while the waves multiply block kb, then stores it.
+// quadrant: 4 x 4 MFMA tiles), k-blocks of 32 in a ring of three LDS stages:
+// the loads of block kb+2 go out while the waves multiply block kb, straight
+// into LDS, with no staging registers and one barrier per block.
 constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LDK = BK + 8;          // LDS row in bf16 (16-byte aligned, skewed banks)
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
     float* __restrict__ part, int blocks_per_split) {
-    __shared__ __align__(16) uint16_t sa[2][BM * LDK];
-    __shared__ __align__(16) uint16_t sb[2][BN * LDK];
+    // Three stages of (128 x rows + 128 W rows) x 32 k, 64 bytes per row,
+    // filled by loads that write LDS directly, as in the wide kernel below.
+    constexpr int kStage = (BM + BN) * BK;           // bf16 per stage
+    __shared__ __align__(16) uint16_t sa[3 * kStage];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
@@ -108,56 +110,64 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
     const int kb_begin = blockIdx.z * blocks_per_split;
     const int kb_end = min(nblk, kb_begin + blocks_per_split);
     const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
-    // staging: vector e = tid + 256 i (i < 2) of a tile is row e / 4, k 8 (e % 4)
-    int ga[2], gb[2], ls[2];
+    // Each wave fills 32 x rows and 32 W rows per stage, 16 rows per load:
+    // lane l writes row l / 4, slot l % 4, and slot s of row r holds the
+    // k-chunk s ^ ((r / 4) % 4).  Rows past M or N read zeros (offsets past
+    // the descriptors).
+    const int lrow = lane >> 2, kchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    int gx[2], gw[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int e = tid + i * kThreads, r = e >> 2, kv = (e & 3) * 8;
-        ga[i] = ((m0 + r) * H + kv) * 2;     // rows past M / N read zeros
-        gb[i] = ((n0 + r) * H + kv) * 2;
-        ls[i] = r * LDK + kv;
+    for (int i2 = 0; i2 < 2; ++i2) {
+        const int r = wave * 32 + i2 * 16 + lrow;
+        gx[i2] = m0 + r < M ? ((m0 + r) * H + kchunk * 8) * 2 : kOffOOB;
+        gw[i2] = n0 + r < N ? ((n0 + r) * H + kchunk * 8) * 2 : kOffOOB;
     }
-    uint4 va[2], vb[2];
-    auto fetch = [&](int kb) {
-        const bool ok = kb < kb_end;
+    using lds_ptr = __attribute__((address_space(3))) void*;
+    auto issue = [&](int kb, int st) {
+        uint16_t* base = sa + st * kStage;
+        const int kofs = kb * BK * 2;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            va[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, ok ? ga[i] + kb * BK * 2 : kOffOOB, 0, 0));
-            vb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(w_rs, ok ? gb[i] + kb * BK * 2 : kOffOOB, 0, 0));
+        for (int i2 = 0; i2 < 2; ++i2) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                x_rs, (lds_ptr)(base + (wave * 32 + i2 * 16) * BK), 16,
+                gx[i2] == kOffOOB ? kOffOOB : gx[i2] + kofs, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                w_rs, (lds_ptr)(base + (BM + wave * 32 + i2 * 16) * BK), 16,
+                gw[i2] == kOffOOB ? kOffOOB : gw[i2] + kofs, 0, 0, 0);
         }
     };
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<uint4*>(&sa[buf][ls[i]]) = va[i];
-            *reinterpret_cast<uint4*>(&sb[buf][ls[i]]) = vb[i];
-        }
-    };
+    const int rsw = 8 * (q4 ^ ((m16 >> 2) & 3));     // this lane's k-chunk, swizzled (bf16)
     f32x4 acc[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    fetch(kb_begin);
-    stage(0);
-    __syncthreads();
+    if (kb_begin < kb_end) issue(kb_begin, 0);
+    if (kb_begin + 1 < kb_end) issue(kb_begin + 1, 1);
+    int st = 0;
     for (int kb = kb_begin; kb < kb_end; ++kb) {
-        const int buf = (kb - kb_begin) & 1;
-        fetch(kb + 1);
+        // this thread's loads of block kb are done (block kb + 1's, four
+        // loads, may still be in flight), then every thread's are, and every
+        // wave has finished reading the stage that block kb + 2 goes to
+        if (kb + 1 < kb_end) __builtin_amdgcn_s_waitcnt(0x0f74);   // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0f70);                   // vmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + 2 < kb_end) issue(kb + 2, st == 0 ? 2 : st - 1);
+        const uint16_t* sx = sa + st * kStage;
+        const uint16_t* sw = sx + BM * BK;
         bf16x8 fa[4], fb[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-            fa[mt] = *reinterpret_cast<const bf16x8*>(&sa[buf][(wm * 64 + mt * 16 + m16) * LDK + q4 * 8]);
+            fa[mt] = *reinterpret_cast<const bf16x8*>(&sx[(wm * 64 + mt * 16 + m16) * BK + rsw]);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
-            fb[nt] = *reinterpret_cast<const bf16x8*>(&sb[buf][(wn * 64 + nt * 16 + m16) * LDK + q4 * 8]);
+            fb[nt] = *reinterpret_cast<const bf16x8*>(&sw[(wn * 64 + nt * 16 + m16) * BK + rsw]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
-        stage(buf ^ 1);
-        __syncthreads();
+        st = st == 2 ? 0 : st + 1;
     }
     // lane holds y[m0 + 64 wm + 16 mt + 4 q + j][n0 + 64 wn + 16 nt + m16]
 #pragma unroll
@@ -182,8 +192,9 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
 // of 32 runs 32 MFMAs per wave between barriers.  k-blocks go through a
 // ring of three LDS stages, written by buffer loads that store straight into
 // LDS (no staging registers), issued two blocks ahead; one barrier per block.
-// Against the double-buffered register staging of the kernel above this took
-// the 8192-token call from 369-381 to 336-343 us.  It covers the full 128-channel
+// Against double-buffered register staging (each thread loading its share of
+// block kb+1 into registers while the waves multiply block kb, then writing
+// it to LDS) this took the 8192-token call from 369-381 to 336-343 us.  It covers the full 128-channel
 // columns only: the channels past the last of them (the gate logits when
 // the q|k|v channels are a multiple of 128) go to the skinny kernel below,
 // 64 tokens per workgroup, in a second short launch.  A partial column
