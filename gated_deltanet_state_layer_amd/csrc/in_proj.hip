@@ -8,8 +8,8 @@
 // and accumulate in fp32 on the bf16 matrix cores.
 //
 // Up to 64 tokens: the skinny kernel below.  From 512 tokens (when the hidden
-// dimension is not split): the 256 x 128 tile kernel, plus the skinny kernel
-// for the channels past its last full 128-channel column.  Otherwise the
+// dimension is not split): the 256 x 256 tile kernel, plus the skinny kernel
+// for the channels past its last full 256-channel column.  Otherwise the
 // gemm kernel: grid (N/128, M/128, ksplit), 4 waves, a 128 x 128 output tile
 // per workgroup; k-blocks of 32 go through a ring of three LDS stages,
 // filled two blocks ahead by 16-byte buffer loads that write LDS directly and
@@ -186,45 +186,50 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
     }
 }
 
-// Many tokens: a 256 x 128 output tile per workgroup, wave (wm, wn) owning a
-// 128 x 64 block (8 x 4 MFMA tiles), so each wave reads 384 bytes of LDS
-// operands per MFMA instead of the 512 of a 64 x 64 block, and each k-block
-// of 32 runs 32 MFMAs per wave between barriers.  k-blocks go through a
-// ring of three LDS stages, written by buffer loads that store straight into
-// LDS (no staging registers), issued two blocks ahead; one barrier per block.
-// Against double-buffered register staging (each thread loading its share of
+// Many tokens: a 256 x 256 output tile per workgroup of 8 waves, wave (wm, wn)
+// owning a 128 x 64 block (8 x 4 MFMA tiles), so each wave reads 384 bytes of
+// LDS operands per MFMA instead of the 512 of a 64 x 64 block, and each
+// k-block of 32 runs 32 MFMAs per wave between barriers.  k-blocks go through
+// a ring of three LDS stages (32 KiB each), written by buffer loads that
+// store straight into LDS (no staging registers), issued two blocks ahead;
+// one barrier per block.  One workgroup per CU (96 KiB of LDS), two waves per
+// SIMD.  Measured at 8192 tokens (hidden 2048): against double-buffered
+// register staging of a 256 x 128 tile (each thread loading its share of
 // block kb+1 into registers while the waves multiply block kb, then writing
-// it to LDS) this took the 8192-token call from 369-381 to 336-343 us.  It covers the full 128-channel
-// columns only: the channels past the last of them (the gate logits when
-// the q|k|v channels are a multiple of 128) go to the skinny kernel below,
-// 64 tokens per workgroup, in a second short launch.  A partial column
-// would add a fifth round of tiles at 8192 tokens (2080 tiles over 512
-// workgroup slots) for 1/128 of the work.
-constexpr int BM2 = 256;
+// it to LDS), the direct loads took the call from 369-381 to 336-343 us, and
+// the 256 x 256 tile (a quarter fewer operand bytes per MFMA from L2) from
+// 341-362 to 324-341 us; a fourth stage was no faster.  It covers the full
+// 256-channel columns only: the channels past the last of them (the 64 gate
+// logits when the q|k|v channels are a multiple of 256) go to the skinny
+// kernel below, 64 tokens per workgroup, in a second short launch.  A partial
+// column would add a fifth round of tiles at 8192 tokens for 1/128 of the
+// work.
+constexpr int BM2 = 256, BN2 = 256;
+constexpr int kWideThreads = 512;
 
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
+__global__ __launch_bounds__(kWideThreads, 1) void in_proj_wide_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
     int n_tn) {
-    // Three stages of (256 x rows + 128 W rows) x 32 k, 64 bytes per row,
+    // Three stages of (256 x rows + 256 W rows) x 32 k, 64 bytes per row,
     // filled by loads that write LDS directly (no registers in between).
     // Those loads count on vmcnt until their data is in LDS; the waits in the
     // loop below are explicit, since nothing else orders the LDS reads after
     // them.
-    constexpr int kStage = (BM2 + BN) * BK;          // bf16 per stage
+    constexpr int kStage = (BM2 + BN2) * BK;          // bf16 per stage
     __shared__ __align__(16) uint16_t sa[3 * kStage];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int N = o.n_out;
     const int n_tm = (M + BM2 - 1) / BM2;
     // Tile order: column-major (consecutive ids share their W rows).  A
     // banded order that gives each XCD a compact 8 x 8 group of tiles was
-    // measured no faster (385 vs 379 us at 8192 tokens).
+    // measured no faster with a 256 x 128 tile (385 vs 379 us at 8192 tokens).
     const int t = blockIdx.x;
     if (t >= n_tm * n_tn) return;
     const int tm = t % n_tm, tn = t / n_tm;
-    const int m0 = tm * BM2, n0 = tn * BN;
+    const int m0 = tm * BM2, n0 = tn * BN2;
     const int nblk = H / BK;
     const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
     // One load instruction fills 16 rows (1 KiB): lane l writes bytes
@@ -233,15 +238,11 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
     // 16 rows of an MFMA fragment read hit 16 different bank groups.  Rows
     // past M or N read zeros (offset past the descriptor).
     const int lrow = lane >> 2, kchunk = (lane & 3) ^ ((lane >> 4) & 3);
-    int gx[4], gw[2];
-#pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-        const int r = wave * 64 + i2 * 16 + lrow;
-        gx[i2] = m0 + r < M ? ((m0 + r) * H + kchunk * 8) * 2 : kOffOOB;
-    }
+    int gx[2], gw[2];
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2) {
         const int r = wave * 32 + i2 * 16 + lrow;
+        gx[i2] = m0 + r < M ? ((m0 + r) * H + kchunk * 8) * 2 : kOffOOB;
         gw[i2] = n0 + r < N ? ((n0 + r) * H + kchunk * 8) * 2 : kOffOOB;
     }
     using lds_ptr = __attribute__((address_space(3))) void*;
@@ -249,15 +250,14 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
         uint16_t* base = sa + st * kStage;
         const int kofs = kb * BK * 2;
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2)
+        for (int i2 = 0; i2 < 2; ++i2) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                x_rs, (lds_ptr)(base + (wave * 64 + i2 * 16) * BK), 16,
+                x_rs, (lds_ptr)(base + (wave * 32 + i2 * 16) * BK), 16,
                 gx[i2] == kOffOOB ? kOffOOB : gx[i2] + kofs, 0, 0, 0);
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 w_rs, (lds_ptr)(base + (BM2 + wave * 32 + i2 * 16) * BK), 16,
                 gw[i2] == kOffOOB ? kOffOOB : gw[i2] + kofs, 0, 0, 0);
+        }
     };
     const int rsw = 8 * (q4 ^ ((m16 >> 2) & 3));     // this lane's k-chunk, swizzled (bf16)
     f32x4 acc[8][4];
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
         // this thread's loads of block kb are done (block kb + 1's may still
         // be in flight), then every thread's are, and every wave has finished
         // reading the stage that block kb + 2 goes to
-        if (kb + 1 < nblk) __builtin_amdgcn_s_waitcnt(0x0f76);   // vmcnt(6)
+        if (kb + 1 < nblk) __builtin_amdgcn_s_waitcnt(0x0f74);   // vmcnt(4)
         else __builtin_amdgcn_s_waitcnt(0x0f70);                 // vmcnt(0)
         asm volatile("s_barrier" ::: "memory");
         if (kb + 2 < nblk) issue(kb + 2, st == 0 ? 2 : st - 1);
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_wide_kernel(
     // sa/sb; each wave touches only its own buffer, so no barrier is needed.
     // lane holds y[m0 + 128 wm + 16 mt + 4 q + j][n0 + 64 wn + 16 nt + m16]
     constexpr int ER = 32, ELD = 64 + 4;   // rows per pass; padded row (floats)
-    static_assert(4 * ER * ELD * sizeof(float) <= sizeof(sa), "epilogue buffer fits in sa");
+    static_assert(8 * ER * ELD * sizeof(float) <= sizeof(sa), "epilogue buffer fits in sa");
     float* eb = reinterpret_cast<float*>(&sa[0]) + wave * ER * ELD;
 #pragma unroll
     for (int pass = 0; pass < 128 / ER; ++pass) {
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void in_proj_epilogue_kernel(const float*
 
 }  // namespace
 
-// From this many tokens (and no split of the hidden dimension) the 256 x 128
+// From this many tokens (and no split of the hidden dimension) the 256 x 256
 // tile kernel runs.
 constexpr int64_t kWideMinTokens = 512;
 
@@ -501,19 +501,19 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
     };
     if (M <= 64) return skinny(0);
     const int ks = in_proj_ksplit(pool, M, H);
-    const int n_full = o.n_out / BN;   // full 128-channel columns
+    const int n_full = o.n_out / BN2;   // full 256-channel columns
     if (ks == 1 && M >= kWideMinTokens && n_full > 0) {
         const int tiles = (int)((M + BM2 - 1) / BM2) * n_full;
         const dim3 grid((unsigned)tiles);
         if (bf)
-            hipLaunchKernelGGL(in_proj_wide_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, xs, ws,
+            hipLaunchKernelGGL(in_proj_wide_kernel<uint16_t>, grid, dim3(kWideThreads), 0, stream, xs, ws,
                                (int)M, H, o, n_full);
         else
-            hipLaunchKernelGGL(in_proj_wide_kernel<float>, grid, dim3(kThreads), 0, stream, xs, ws,
+            hipLaunchKernelGGL(in_proj_wide_kernel<float>, grid, dim3(kWideThreads), 0, stream, xs, ws,
                                (int)M, H, o, n_full);
         const hipError_t e = hipGetLastError();
-        if (e != hipSuccess || n_full * BN == o.n_out) return e;
-        return skinny(n_full * BN);
+        if (e != hipSuccess || n_full * BN2 == o.n_out) return e;
+        return skinny(n_full * BN2);
     }
     const int nblk = H / BK, per = (nblk + ks - 1) / ks;
     float* part = ks > 1 ? static_cast<float*>(workspace) : nullptr;
