@@ -65,6 +65,9 @@ def test_in_proj_qwen3_next_vs_oracle(n_tok):
     (1, 3, 64, 160, 70, "bf16"),     # 3 gates each: gate rows straddle a tile
     (2, 4, 128, 4096, 5, "bf16"),    # long hidden, split 16 ways
     (2, 4, 64, 96, 700, "f32"),      # 256-token tiles: ragged rows, an 8-channel last tile
+    (1, 2, 128, 32, 600, "bf16"),    # 256-token tiles over a single k-block
+    (1, 2, 128, 64, 530, "f32"),     # 256-token tiles over two k-blocks
+    (1, 1, 32, 96, 600, "bf16"),     # many tokens, fewer than 256 channels: the 128-tile path
 ])
 def test_in_proj_other_shapes(h_k, h_v, d, hidden, n_tok, io):
     s = syn.Shapes(h_k, h_v, d, d, 4)
