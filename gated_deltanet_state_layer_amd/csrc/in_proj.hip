@@ -27,7 +27,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kOffOOB = 0x7fff0000;   // an offset past every descriptor used here
+// An offset past every descriptor used here: the calls accept x and W only
+// below INT32_MAX - 256 * hidden bytes (hidden >= 32), so below 0x7fffe000.
+constexpr int kOffOOB = 0x7ffffff0;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
