@@ -342,35 +342,39 @@ constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
 constexpr size_t kSkinnyLds = (size_t)kSkinnyWaves * 64 * 64 * sizeof(float);
 
 // NS > 0: each wave's k-step count fixed at compile time (the loop below is
-// then straight-line code with exact waits); 0: any count.
-template <typename T, int NS>
-__global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
+// then straight-line code with exact waits); 0: any count.  TMT: 16-token
+// tiles per workgroup, 4 (64 tokens) or 2 (32 tokens: half the registers and
+// LDS, so two workgroups fit per CU; three k-steps in flight to stay within
+// 128 registers).
+template <typename T, int NS, int TMT = 4>
+__global__ __launch_bounds__(kSkinnyThreads, TMT < 4 ? 4 : 1) void in_proj_skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
     int c0) {
-    extern __shared__ __align__(16) float red[];     // [8 waves][64 tokens][64 channels]
+    constexpr int kStg = TMT < 4 ? 3 : kSkinnyStages;
+    extern __shared__ __align__(16) float red[];     // [8 waves][16 TMT tokens][64 channels]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
-    const int N = o.n_out, n0 = c0 + blockIdx.x * 64, m0 = blockIdx.y * 64;
+    const int N = o.n_out, n0 = c0 + blockIdx.x * 64, m0 = blockIdx.y * 16 * TMT;
     const int nsteps = H / 32, per = (nsteps + kSkinnyWaves - 1) / kSkinnyWaves;
     const int s_begin = wave * per, s_end = min(nsteps, s_begin + per);
     const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
-    int xo[4], wo[4];
+    int xo[TMT], wo[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        xo[t] = ((m0 + t * 16 + m16) * H) * 2 + q4 * 16;    // tokens past M read zeros
-        wo[t] = ((n0 + t * 16 + m16) * H) * 2 + q4 * 16;    // channels past N read zeros
-    }
+    for (int t = 0; t < TMT; ++t) xo[t] = ((m0 + t * 16 + m16) * H) * 2 + q4 * 16;    // tokens past M read zeros
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wo[t] = ((n0 + t * 16 + m16) * H) * 2 + q4 * 16;    // channels past N read zeros
     auto fetch = [&](int st, bf16x8* xf, bf16x8* wf) {
         const bool ok = st < s_end;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            xf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(x_rs, ok ? xo[t] + st * 64 : kOffOOB, 0, 0));
+            if (t < TMT)
+                xf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(x_rs, ok ? xo[t] + st * 64 : kOffOOB, 0, 0));
             wf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(w_rs, ok ? wo[t] + st * 64 : kOffOOB, 0, 0));
         }
     };
-    f32x4 acc[4][4];
+    f32x4 acc[TMT][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < TMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Up to kSkinnyStages k-steps of loads in flight per wave: a step's MFMAs
@@ -378,10 +382,10 @@ __global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
     // every step waiting a whole memory latency.  Each stage's registers are
     // refilled right after its MFMAs.  Steps past the wave's range load zeros
     // (no memory access).
-    bf16x8 xs[kSkinnyStages][4], ws[kSkinnyStages][4];
+    bf16x8 xs[kStg][4], ws[kStg][4];
     auto mma_stage = [&](int i) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < TMT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xs[i][mt], ws[i][nt], acc[mt][nt], 0, 0, 0);
@@ -391,12 +395,12 @@ __global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
         // loads where they are written: left alone, the scheduler sinks them
         // next to their MFMAs to save registers, and every step waits again.
 #pragma unroll
-        for (int i = 0; i < kSkinnyStages && i < NS; ++i) fetch(s_begin + i, xs[i], ws[i]);
+        for (int i = 0; i < kStg && i < NS; ++i) fetch(s_begin + i, xs[i], ws[i]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            mma_stage(j % kSkinnyStages);
-            if (j + kSkinnyStages < NS) fetch(s_begin + j + kSkinnyStages, xs[j % kSkinnyStages], ws[j % kSkinnyStages]);
+            mma_stage(j % kStg);
+            if (j + kStg < NS) fetch(s_begin + j + kStg, xs[j % kStg], ws[j % kStg]);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
@@ -410,20 +414,20 @@ __global__ __launch_bounds__(kSkinnyThreads) void in_proj_skinny_kernel(
         }
     }
     // lane holds y[m0 + 16 mt + 4 q + j][n0 + 16 nt + m16]
-    float* mine = red + wave * 64 * 64;
+    float* mine = red + wave * TMT * 16 * 64;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < TMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) mine[(mt * 16 + q4 * 4 + j) * 64 + nt * 16 + m16] = acc[mt][nt][j];
     __syncthreads();
-    for (int idx = tid; idx < 64 * 64; idx += kSkinnyThreads) {
+    for (int idx = tid; idx < TMT * 16 * 64; idx += kSkinnyThreads) {
         const int m = m0 + (idx >> 6), n = n0 + (idx & 63);
         if (m >= M || n >= N) continue;
         float y = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kSkinnyWaves; ++ww) y += red[ww * 64 * 64 + idx];
+        for (int ww = 0; ww < kSkinnyWaves; ++ww) y += red[ww * TMT * 16 * 64 + idx];
         put<T>(o, m, n, y);
     }
 }
@@ -515,6 +519,22 @@ hipError_t launch_in_proj(const gdn_pool* pool, int64_t M, int32_t H, const void
                                (int)M, H, o, n_full);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || n_full * BN2 == o.n_out) return e;
+        if ((H / 32 + kSkinnyWaves - 1) / kSkinnyWaves == 8) {
+            // The strip past the last full column with 32 tokens per
+            // workgroup: at 8192 tokens 256 workgroups instead of 128, each
+            // streaming half as much of x (21.6 -> ~14 us for the 64 gate
+            // channels at hidden 2048).
+            const int c0 = n_full * BN2;
+            const dim3 g2((o.n_out - c0 + 63) / 64, (unsigned)((M + 31) / 32));
+            const size_t lds = (size_t)kSkinnyWaves * 32 * 64 * sizeof(float);
+            if (bf)
+                hipLaunchKernelGGL((in_proj_skinny_kernel<uint16_t, 8, 2>), g2, dim3(kSkinnyThreads), lds,
+                                   stream, xs, ws, (int)M, H, o, c0);
+            else
+                hipLaunchKernelGGL((in_proj_skinny_kernel<float, 8, 2>), g2, dim3(kSkinnyThreads), lds,
+                                   stream, xs, ws, (int)M, H, o, c0);
+            return hipGetLastError();
+        }
         return skinny(n_full * BN2);
     }
     const int nblk = H / BK, per = (nblk + ks - 1) / ks;

@@ -68,6 +68,7 @@ def test_in_proj_qwen3_next_vs_oracle(n_tok):
     (1, 2, 128, 32, 600, "bf16"),    # 256-token tiles over a single k-block
     (1, 2, 128, 64, 530, "f32"),     # 256-token tiles over two k-blocks
     (1, 1, 32, 96, 600, "bf16"),     # many tokens, fewer than 256 channels: the 128-tile path
+    (1, 2, 128, 2048, 600, "f32"),   # 256-token tiles, then the 4 gate channels 32 tokens per workgroup
 ])
 def test_in_proj_other_shapes(h_k, h_v, d, hidden, n_tok, io):
     s = syn.Shapes(h_k, h_v, d, d, 4)
