@@ -329,10 +329,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void in_proj_wide_kernel(
 }
 
 // Few tokens (M <= 64): the weight stream is the whole cost.  One workgroup
-// of 8 waves per 64 output channels and 64 tokens (grid y; also used for the
-// channels past the last full column of the 256-token-tile kernel); wave w
-// multiplies the full 64 x 64 tile
-// over its eighth of the hidden dimension, operands straight from memory into
+// of 8 waves per 64 output channels and 64 tokens (grid y; also used, with 32
+// tokens per workgroup when each wave has 8 k-steps, for the channels past
+// the last full column of the 256-token-tile kernel); wave w multiplies the
+// full 64 x 64 tile over its eighth of the hidden dimension, operands straight from memory into
 // MFMA registers (16 bytes per lane, one step ahead), and the eight partial
 // tiles are added in LDS before the fused epilogue.  No partial sums leave
 // the chip and there is no second launch.
