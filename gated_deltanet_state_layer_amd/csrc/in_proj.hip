@@ -190,22 +190,22 @@ __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
 
 // Many tokens: a 256 x 256 output tile per workgroup of 8 waves, wave (wm, wn)
 // owning a 128 x 64 block (8 x 4 MFMA tiles), so each wave reads 384 bytes of
-// LDS operands per MFMA instead of the 512 of a 64 x 64 block, and each
-// k-block of 32 runs 32 MFMAs per wave between barriers.  k-blocks go through
-// a ring of three LDS stages (32 KiB each), written by buffer loads that
-// store straight into LDS (no staging registers), issued two blocks ahead;
-// one barrier per block.  One workgroup per CU (96 KiB of LDS), two waves per
-// SIMD.  Measured at 8192 tokens (hidden 2048): against double-buffered
-// register staging of a 256 x 128 tile (each thread loading its share of
-// block kb+1 into registers while the waves multiply block kb, then writing
-// it to LDS), the direct loads took the call from 369-381 to 336-343 us, and
-// the 256 x 256 tile (a quarter fewer operand bytes per MFMA from L2) from
-// 341-362 to 324-341 us; a fourth stage was no faster.  It covers the full
-// 256-channel columns only: the channels past the last of them (the 64 gate
-// logits when the q|k|v channels are a multiple of 256) go to the skinny
-// kernel below, 64 tokens per workgroup, in a second short launch.  A partial
-// column would add a fifth round of tiles at 8192 tokens for 1/128 of the
-// work.
+// LDS operands per MFMA instead of the 512 of a 64 x 64 block.  k-blocks of
+// 64 (64 MFMAs per wave between barriers) go through two LDS stages of
+// 64 KiB, written by buffer loads that store straight into LDS (no staging
+// registers), issued one block ahead; one barrier per block.  One workgroup
+// per CU (128 KiB of LDS), two waves per SIMD.  Measured at 8192 tokens
+// (hidden 2048), same-box A/Bs: against double-buffered register staging of
+// a 256 x 128 tile (each thread loading its share of block kb+1 into
+// registers while the waves multiply block kb, then writing it to LDS), the
+// direct loads (three stages of k 32) took the call from 369-381 to
+// 336-343 us; the 256 x 256 tile (a quarter fewer operand bytes per MFMA
+// from L2) from 341-362 to 324-341 us (a fourth stage: no faster); k-blocks
+// of 64 in two stages (half the barriers) from 323-332 to 298-303 us.  It
+// covers the full 256-channel columns only: the channels past the last of
+// them (the 64 gate logits when the q|k|v channels are a multiple of 256) go
+// to the skinny kernel below in a second short launch.  A partial column
+// would add a fifth round of tiles at 8192 tokens for 1/128 of the work.
 constexpr int BM2 = 256, BN2 = 256;
 constexpr int kWideThreads = 512;
 
@@ -213,13 +213,14 @@ template <typename T>
 __global__ __launch_bounds__(kWideThreads, 1) void in_proj_wide_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
     int n_tn) {
-    // Three stages of (256 x rows + 256 W rows) x 32 k, 64 bytes per row,
+    // Two stages of (256 x rows + 256 W rows) x 64 k, 128 bytes per row,
     // filled by loads that write LDS directly (no registers in between).
     // Those loads count on vmcnt until their data is in LDS; the waits in the
     // loop below are explicit, since nothing else orders the LDS reads after
     // them.
-    constexpr int kStage = (BM2 + BN2) * BK;          // bf16 per stage
-    __shared__ __align__(16) uint16_t sa[3 * kStage];
+    constexpr int KB = 64;                           // k per stage
+    constexpr int kStage = (BM2 + BN2) * KB;          // bf16 per stage
+    __shared__ __align__(16) uint16_t sa[2 * kStage];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
     const int wm = wave >> 2, wn = wave & 3;
@@ -232,67 +233,68 @@ __global__ __launch_bounds__(kWideThreads, 1) void in_proj_wide_kernel(
     if (t >= n_tm * n_tn) return;
     const int tm = t % n_tm, tn = t / n_tm;
     const int m0 = tm * BM2, n0 = tn * BN2;
-    const int nblk = H / BK;
+    const int nblk = (H + KB - 1) / KB;
     const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
-    // One load instruction fills 16 rows (1 KiB): lane l writes bytes
-    // 16 l .. 16 l + 15 after the wave-uniform base, i.e. row l / 4, slot
-    // l % 4.  Slot s of row r holds the k-chunk s ^ ((r / 4) % 4), so that the
-    // 16 rows of an MFMA fragment read hit 16 different bank groups.  Rows
-    // past M or N read zeros (offset past the descriptor).
-    const int lrow = lane >> 2, kchunk = (lane & 3) ^ ((lane >> 4) & 3);
-    int gx[2], gw[2];
+    // One load instruction fills 8 rows of 128 bytes (1 KiB): lane l writes
+    // bytes 16 l .. 16 l + 15 after the wave-uniform base, i.e. row l / 8,
+    // slot l % 8.  Slot s of row r holds the k-chunk s ^ ((r / 2) % 8), so
+    // that the 16 rows of an MFMA fragment read hit 16 different bank
+    // groups.  Rows past M or N, and chunks past H (hidden sizes that are odd
+    // multiples of 32), read zeros (offset past the descriptor).
+    const int lrow = lane >> 3, lslot = lane & 7;
+    int gx[4], gw[4], kc[4];
 #pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2) {
-        const int r = wave * 32 + i2 * 16 + lrow;
-        gx[i2] = m0 + r < M ? ((m0 + r) * H + kchunk * 8) * 2 : kOffOOB;
-        gw[i2] = n0 + r < N ? ((n0 + r) * H + kchunk * 8) * 2 : kOffOOB;
+    for (int i2 = 0; i2 < 4; ++i2) {
+        const int r = wave * 32 + i2 * 8 + lrow;
+        kc[i2] = lslot ^ ((4 * i2 + (lrow >> 1)) & 7);
+        gx[i2] = m0 + r < M ? ((m0 + r) * H + kc[i2] * 8) * 2 : kOffOOB;
+        gw[i2] = n0 + r < N ? ((n0 + r) * H + kc[i2] * 8) * 2 : kOffOOB;
     }
     using lds_ptr = __attribute__((address_space(3))) void*;
     auto issue = [&](int kb, int st) {
         uint16_t* base = sa + st * kStage;
-        const int kofs = kb * BK * 2;
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
+        for (int i2 = 0; i2 < 4; ++i2) {
+            const bool in_k = kb * KB + kc[i2] * 8 < H;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                x_rs, (lds_ptr)(base + (wave * 32 + i2 * 16) * BK), 16,
-                gx[i2] == kOffOOB ? kOffOOB : gx[i2] + kofs, 0, 0, 0);
+                x_rs, (lds_ptr)(base + (wave * 32 + i2 * 8) * KB), 16,
+                gx[i2] == kOffOOB || !in_k ? kOffOOB : gx[i2] + kb * KB * 2, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                w_rs, (lds_ptr)(base + (BM2 + wave * 32 + i2 * 16) * BK), 16,
-                gw[i2] == kOffOOB ? kOffOOB : gw[i2] + kofs, 0, 0, 0);
+                w_rs, (lds_ptr)(base + (BM2 + wave * 32 + i2 * 8) * KB), 16,
+                gw[i2] == kOffOOB || !in_k ? kOffOOB : gw[i2] + kb * KB * 2, 0, 0, 0);
         }
     };
-    const int rsw = 8 * (q4 ^ ((m16 >> 2) & 3));     // this lane's k-chunk, swizzled (bf16)
+    const int rkey = (m16 >> 1) & 7;
     f32x4 acc[8][4];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     issue(0, 0);
-    if (nblk > 1) issue(1, 1);
-    int st = 0;
     for (int kb = 0; kb < nblk; ++kb) {
-        // this thread's loads of block kb are done (block kb + 1's may still
-        // be in flight), then every thread's are, and every wave has finished
-        // reading the stage that block kb + 2 goes to
-        if (kb + 1 < nblk) __builtin_amdgcn_s_waitcnt(0x0f74);   // vmcnt(4)
-        else __builtin_amdgcn_s_waitcnt(0x0f70);                 // vmcnt(0)
+        // this thread's loads of block kb are done, then every thread's are,
+        // and every wave has finished reading the stage block kb + 1 goes to
+        __builtin_amdgcn_s_waitcnt(0x0f70);                      // vmcnt(0)
         asm volatile("s_barrier" ::: "memory");
-        if (kb + 2 < nblk) issue(kb + 2, st == 0 ? 2 : st - 1);
-        const uint16_t* sx = sa + st * kStage;
-        const uint16_t* sw = sx + BM2 * BK;
-        bf16x8 fa[8], fb[4];
+        if (kb + 1 < nblk) issue(kb + 1, (kb + 1) & 1);
+        const uint16_t* sx = sa + (kb & 1) * kStage;
+        const uint16_t* sw = sx + BM2 * KB;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-            fb[nt] = *reinterpret_cast<const bf16x8*>(&sw[(wn * 64 + nt * 16 + m16) * BK + rsw]);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            fa[mt] = *reinterpret_cast<const bf16x8*>(&sx[(wm * 128 + mt * 16 + m16) * BK + rsw]);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int kh = 0; kh < 2; ++kh) {
+            const int so = 8 * ((kh * 4 + q4) ^ rkey);
+            bf16x8 fa[8], fb[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
-        st = st == 2 ? 0 : st + 1;
+                fb[nt] = *reinterpret_cast<const bf16x8*>(&sw[(wn * 64 + nt * 16 + m16) * KB + so]);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                fa[mt] = *reinterpret_cast<const bf16x8*>(&sx[(wm * 128 + mt * 16 + m16) * KB + so]);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
+        }
     }
     __syncthreads();   // every wave is done with the operand stages
     // Epilogue through LDS: lane (m16, q4) holds rows 16 mt + 4 q4 + j of
