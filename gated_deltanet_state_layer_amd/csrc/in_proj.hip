@@ -11,9 +11,9 @@
 // dimension is not split): the 256 x 256 tile kernel, plus the skinny kernel
 // for the channels past its last full 256-channel column.  Otherwise the
 // gemm kernel: grid (N/128, M/128, ksplit), 4 waves, a 128 x 128 output tile
-// per workgroup; k-blocks of 32 go through a ring of three LDS stages,
-// filled two blocks ahead by 16-byte buffer loads that write LDS directly and
-// whose descriptors return zeros past the ragged ends.
+// per workgroup; k-blocks of 64 go through two LDS stages, filled one block
+// ahead by 16-byte buffer loads that write LDS directly and whose descriptors
+// return zeros past the ragged ends.
 // With few tokens the hidden dimension is split over ksplit workgroups so
 // that enough weight bytes are in flight; a second kernel adds the partial
 // sums.  Otherwise the gemm kernel writes the outputs itself.
@@ -90,86 +90,91 @@ __device__ __forceinline__ void put8(const ProjOut& o, int64_t m, int n, const f
 }
 
 // 128 x 128 output tile per workgroup (wave (wm, wn) owns a 64 x 64
-// quadrant: 4 x 4 MFMA tiles), k-blocks of 32 in a ring of three LDS stages:
-// the loads of block kb+2 go out while the waves multiply block kb, straight
-// into LDS, with no staging registers and one barrier per block.
+// quadrant: 4 x 4 MFMA tiles), k-blocks of 64 in two LDS stages of 32 KiB:
+// the loads of block kb+1 go out while the waves multiply block kb, straight
+// into LDS, with no staging registers and one barrier per block.  Against a
+// ring of three stages of k 32 this took 96 / 256 / 511 tokens (hidden 2048)
+// from 23.0 / 30.8 / 45.3 to 21.9 / 27.9 / 38.9 us, same box.
 constexpr int BM = 128, BN = 128, BK = 32;
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void in_proj_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int M, int H, ProjOut o,
     float* __restrict__ part, int blocks_per_split) {
-    // Three stages of (128 x rows + 128 W rows) x 32 k, 64 bytes per row,
+    // Two stages of (128 x rows + 128 W rows) x 64 k, 128 bytes per row,
     // filled by loads that write LDS directly, as in the wide kernel below.
-    constexpr int kStage = (BM + BN) * BK;           // bf16 per stage
-    __shared__ __align__(16) uint16_t sa[3 * kStage];
+    constexpr int KB = 64;                           // k per stage
+    constexpr int kStage = (BM + BN) * KB;           // bf16 per stage
+    __shared__ __align__(16) uint16_t sa[2 * kStage];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
     const int N = o.n_out;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int nblk = H / BK;
-    const int kb_begin = blockIdx.z * blocks_per_split;
-    const int kb_end = min(nblk, kb_begin + blocks_per_split);
+    // this split's k range, [k_begin, k_end), in steps of KB
+    const int k_begin = blockIdx.z * blocks_per_split * BK;
+    const int k_end = min(H, k_begin + blocks_per_split * BK);
+    const int nkb = k_end > k_begin ? (k_end - k_begin + KB - 1) / KB : 0;
     const auto x_rs = buf_rsrc(x, M * H * 2), w_rs = buf_rsrc(w, N * H * 2);
-    // Each wave fills 32 x rows and 32 W rows per stage, 16 rows per load:
-    // lane l writes row l / 4, slot l % 4, and slot s of row r holds the
-    // k-chunk s ^ ((r / 4) % 4).  Rows past M or N read zeros (offsets past
-    // the descriptors).
-    const int lrow = lane >> 2, kchunk = (lane & 3) ^ ((lane >> 4) & 3);
-    int gx[2], gw[2];
+    // Each wave fills 32 x rows and 32 W rows per stage, 8 rows of 128 bytes
+    // per load: lane l writes row l / 8, slot l % 8, and slot s of row r
+    // holds the k-chunk s ^ ((r / 2) % 8).  Rows past M or N, and chunks past
+    // the split's end, read zeros (offsets past the descriptors).
+    const int lrow = lane >> 3, lslot = lane & 7;
+    int gx[4], gw[4], kc[4];
 #pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2) {
-        const int r = wave * 32 + i2 * 16 + lrow;
-        gx[i2] = m0 + r < M ? ((m0 + r) * H + kchunk * 8) * 2 : kOffOOB;
-        gw[i2] = n0 + r < N ? ((n0 + r) * H + kchunk * 8) * 2 : kOffOOB;
+    for (int i2 = 0; i2 < 4; ++i2) {
+        const int r = wave * 32 + i2 * 8 + lrow;
+        kc[i2] = lslot ^ ((4 * i2 + (lrow >> 1)) & 7);
+        gx[i2] = m0 + r < M ? ((m0 + r) * H + kc[i2] * 8) * 2 : kOffOOB;
+        gw[i2] = n0 + r < N ? ((n0 + r) * H + kc[i2] * 8) * 2 : kOffOOB;
     }
     using lds_ptr = __attribute__((address_space(3))) void*;
     auto issue = [&](int kb, int st) {
         uint16_t* base = sa + st * kStage;
-        const int kofs = kb * BK * 2;
+        const int k0 = k_begin + kb * KB;
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
+        for (int i2 = 0; i2 < 4; ++i2) {
+            const bool in_k = k0 + kc[i2] * 8 < k_end;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                x_rs, (lds_ptr)(base + (wave * 32 + i2 * 16) * BK), 16,
-                gx[i2] == kOffOOB ? kOffOOB : gx[i2] + kofs, 0, 0, 0);
+                x_rs, (lds_ptr)(base + (wave * 32 + i2 * 8) * KB), 16,
+                gx[i2] == kOffOOB || !in_k ? kOffOOB : gx[i2] + k0 * 2, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                w_rs, (lds_ptr)(base + (BM + wave * 32 + i2 * 16) * BK), 16,
-                gw[i2] == kOffOOB ? kOffOOB : gw[i2] + kofs, 0, 0, 0);
+                w_rs, (lds_ptr)(base + (BM + wave * 32 + i2 * 8) * KB), 16,
+                gw[i2] == kOffOOB || !in_k ? kOffOOB : gw[i2] + k0 * 2, 0, 0, 0);
         }
     };
-    const int rsw = 8 * (q4 ^ ((m16 >> 2) & 3));     // this lane's k-chunk, swizzled (bf16)
+    const int rkey = (m16 >> 1) & 7;
     f32x4 acc[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (kb_begin < kb_end) issue(kb_begin, 0);
-    if (kb_begin + 1 < kb_end) issue(kb_begin + 1, 1);
-    int st = 0;
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-        // this thread's loads of block kb are done (block kb + 1's, four
-        // loads, may still be in flight), then every thread's are, and every
-        // wave has finished reading the stage that block kb + 2 goes to
-        if (kb + 1 < kb_end) __builtin_amdgcn_s_waitcnt(0x0f74);   // vmcnt(4)
-        else __builtin_amdgcn_s_waitcnt(0x0f70);                   // vmcnt(0)
+    if (nkb > 0) issue(0, 0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        // this thread's loads of block kb are done, then every thread's are,
+        // and every wave has finished reading the stage block kb + 1 goes to
+        __builtin_amdgcn_s_waitcnt(0x0f70);                      // vmcnt(0)
         asm volatile("s_barrier" ::: "memory");
-        if (kb + 2 < kb_end) issue(kb + 2, st == 0 ? 2 : st - 1);
-        const uint16_t* sx = sa + st * kStage;
-        const uint16_t* sw = sx + BM * BK;
-        bf16x8 fa[4], fb[4];
+        if (kb + 1 < nkb) issue(kb + 1, (kb + 1) & 1);
+        const uint16_t* sx = sa + (kb & 1) * kStage;
+        const uint16_t* sw = sx + BM * KB;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            fa[mt] = *reinterpret_cast<const bf16x8*>(&sx[(wm * 64 + mt * 16 + m16) * BK + rsw]);
+        for (int kh = 0; kh < 2; ++kh) {
+            const int so = 8 * ((kh * 4 + q4) ^ rkey);
+            bf16x8 fa[4], fb[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-            fb[nt] = *reinterpret_cast<const bf16x8*>(&sw[(wn * 64 + nt * 16 + m16) * BK + rsw]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
+                fa[mt] = *reinterpret_cast<const bf16x8*>(&sx[(wm * 64 + mt * 16 + m16) * KB + so]);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
-        st = st == 2 ? 0 : st + 1;
+                fb[nt] = *reinterpret_cast<const bf16x8*>(&sw[(wn * 64 + nt * 16 + m16) * KB + so]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
+        }
     }
     // lane holds y[m0 + 64 wm + 16 mt + 4 q + j][n0 + 64 wn + 16 nt + m16]
 #pragma unroll
